@@ -1,0 +1,254 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the dropless MoE expert MLP on one MI355X
+ * (gfx950), run as a sync-free ragged grouped GEMM with a fused GLU epilogue.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "NVIDIA CuTe DSL 융합 커널은 MoE 학습의 CPU·메모리 병목을 지운다"
+ *   [P2] "SonicMoE로 보는 GPU 커널 최적화"
+ *   [P3] "Dropless MoE 학습과 NVIDIA Transformer Engine 소개"
+ *
+ * Conventions shared by every entry point
+ *   - bf16 tensors are passed as uint16_t* raw bit patterns; all sizes are
+ *     element counts; every matrix is row-major and densely packed.
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     The caller owns every buffer and keeps it alive until the stream work
+ *     that uses it has completed. The library allocates nothing, keeps no
+ *     pointer after a call returns and holds no mutable global state, so
+ *     calls are reentrant and thread-safe.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     legacy default stream). No call synchronises, allocates or copies
+ *     device-to-host, so every call may be recorded into a hipGraph. Shapes
+ *     that depend on the routing (per-expert counts and offsets) are read by
+ *     the kernels from device memory only [P1, core-idea section: per-expert
+ *     counts tracked on the GPU so no host shape query is needed].
+ *   - Host-checkable errors (NULL pointers, bad sizes, misaligned pointers,
+ *     a too-small workspace or capacity) return a negative status before any
+ *     launch. A launch failure returns MOE_ERR_LAUNCH. Data-dependent
+ *     problems never trap: they set bits in a caller-owned device error word.
+ *
+ * Layout of the expert-major ragged buffer [P3, sections on ragged tensors,
+ * dropless MoE, grouped GEMM (128-token alignment) and the dropless
+ * boundary (one slot per (token, expert) pair, expert regions padded)]:
+ *   pair p = t*k + j (token t, slot j) goes to expert e = topk_idx[t, j];
+ *   expert e owns rows [offsets[e], offsets[e+1]), offsets[0] = 0,
+ *   offsets[e+1] - offsets[e] = 128 * ceil(counts[e] / 128) (0 if empty);
+ *   its pairs sit in rows offsets[e] + rank in ascending p, the remaining
+ *   rows of its region are padding and every permuted tensor the library
+ *   writes holds zeros there; rows >= offsets[E] are never read or written.
+ *   M_cap = moe_capacity_rows(T, k, E) rows always suffice, so nothing is
+ *   ever dropped [P3, dropless-boundary section: a worst-case buffer never
+ *   drops].
+ *
+ * FC1 weight layout [P3, grouped-GEMM section: prefused FC1 weight of shape
+ * (experts, embed_dim, 2*mlp_dim); P1, core-idea section: gate and input
+ * columns interleaved so one tile holds both halves]: w1 is [E, d, 2n];
+ * column block b (32 wide) of each row holds gate columns [2*32b, 2*32b+32)
+ * = gate[32b, 32b+32) followed by up columns = up[32b, 32b+32).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ALIGN 128          /* rows per expert-region alignment unit    */
+#define MOE_MX_BLOCK 32        /* elements per MXFP8 scale block           */
+#define MOE_GLU_INTERLEAVE 32  /* gate/up interleave granularity (columns) */
+#define MOE_MAX_EXPERTS 1024
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)  /* NULL/negative/misaligned argument      */
+#define MOE_ERR_UNSUPPORTED (-2)  /* valid but unsupported shape or option  */
+#define MOE_ERR_WORKSPACE (-3)    /* workspace or M_cap too small           */
+#define MOE_ERR_LAUNCH (-4)       /* a kernel launch reported an error      */
+
+/* activation of the gated MLP */
+#define MOE_ACT_SWIGLU 0       /* silu(gate) * up, silu(x) = x / (1 + e^-x) */
+
+/* stage bits of moe_grouped_mlp_fwd / moe_grouped_mlp_bwd */
+#define MOE_STAGE_FC1 0x01     /* H = X_perm W1_e, A = SwiGLU(H)            */
+#define MOE_STAGE_FC2 0x02     /* Y = A W2_e                                */
+#define MOE_STAGE_DGRAD2 0x04  /* dA' = dY_u W2_e^T + dSwiGLU epilogue, dS  */
+#define MOE_STAGE_WGRAD2 0x08  /* dW2_e = A'^T dY_u                          */
+#define MOE_STAGE_DGRAD1 0x10  /* dX_perm = dH W1_e^T                        */
+#define MOE_STAGE_WGRAD1 0x20  /* dW1_e = X_perm^T dH                        */
+#define MOE_STAGES_FWD (MOE_STAGE_FC1 | MOE_STAGE_FC2)
+#define MOE_STAGES_BWD (MOE_STAGE_DGRAD2 | MOE_STAGE_WGRAD2 | MOE_STAGE_DGRAD1 | MOE_STAGE_WGRAD1)
+
+/* bits of the device error word */
+#define MOE_ERRBIT_NONFINITE_LOGIT 0x1
+
+/* moe_quant_mxfp8 mode bits */
+#define MOE_QUANT_ROWWISE 0x1
+#define MOE_QUANT_COLWISE 0x2
+
+typedef void* moe_stream_t; /* hipStream_t */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(int status);
+
+/* Worst-case row count of the expert-major buffer for T tokens, top-k over E
+ * experts: 128*ceil(T*k/128) + 128*E. Returns -1 for invalid arguments.
+ * Host-only; touches no device. */
+int64_t moe_capacity_rows(int T, int k, int E);
+
+/* Device workspace (bytes) that moe_route_counts needs. Host-only. */
+size_t moe_route_workspace_bytes(int T, int k, int E);
+
+/* Device workspace (bytes) that moe_grouped_mlp_bwd needs (per-row router
+ * gradient partials). Host-only. */
+size_t moe_mlp_bwd_workspace_bytes(int n, int64_t M_cap);
+
+/*
+ * moe_route_counts -- softmax top-k routing plus the device-resident ragged
+ * layout: per-expert counts, 128-aligned prefix offsets and both row maps.
+ *   [P3, ragged-tensor section: a learned router sends each token to its
+ *   top-K experts and the per-expert counts vary per batch; P1, core-idea
+ *   section: counts stay in GPU memory; P3, grouped-GEMM section: 128-token
+ *   alignment of expert regions.]
+ * Routing: p = softmax over all E logits of a token (fp32); experts ranked by
+ * raw logit, descending, ties to the lower expert index; slot j holds the
+ * j-th best; topk_w[t, j] = p of that expert, renormalised over the k chosen
+ * ones when renorm != 0.
+ *   logits   [T, E] fp32 (in)
+ *   topk_idx [T, k] int32 (out)    topk_w [T, k] fp32 (out)
+ *   counts   [E] int32 (out)       offsets [E+1] int32 (out)
+ *   row_of   [T*k] int32 (out): row of pair p in the expert-major buffer
+ *   src_of   [M_cap] int32 (out): pair held by each row, -1 for padding and
+ *            for rows >= offsets[E]
+ *   err_word [1] int32 (in/out, device): MOE_ERRBIT_NONFINITE_LOGIT is OR-ed
+ *            in when a logit is NaN or infinite (the routing of such a token
+ *            is then unspecified but every output stays in range)
+ *   workspace: >= moe_route_workspace_bytes(T, k, E) bytes, 16-byte aligned
+ * Requires 1 <= k <= E <= MOE_MAX_EXPERTS, T >= 1, M_cap >= capacity rows.
+ */
+int moe_route_counts(const float* logits, int T, int E, int k, int renorm,
+                     int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                     int32_t* row_of, int32_t* src_of, int64_t M_cap, int32_t* err_word,
+                     void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * moe_permute -- gather token rows into the expert-major buffer
+ *   x_perm[r] = x[src_of[r] / k] for r < offsets[E] with src_of[r] >= 0, and
+ *   x_perm[r] = 0 for the padding rows of every expert region.
+ *   [P2, SonicMoE section: the gather sub-kernel; P3, EP section: dispatch
+ *   permutes tokens expert-major.] Used for activations (forward) and for the
+ *   upstream gradient dO (backward; no weighting).
+ *   x [T, d] bf16 (in), src_of [M_cap], offsets [E+1] (in),
+ *   x_perm [M_cap, d] bf16 (out; rows >= offsets[E] untouched).
+ * Requires d % 8 == 0; x and x_perm 16-byte aligned.
+ */
+int moe_permute(const uint16_t* x, const int32_t* src_of, const int32_t* offsets,
+                int T, int k, int E, int d, int64_t M_cap, uint16_t* x_perm,
+                moe_stream_t stream);
+
+/*
+ * moe_combine -- weighted un-permute: out[t] = sum over j ascending of
+ *   w[t, j] * y[row_of[t*k + j]], accumulated in fp32, rounded once to bf16.
+ *   w == NULL means unit weights (the backward's dX = sum_j dX_perm rows).
+ *   [P2, SonicMoE section: scatter + expert aggregation sub-kernels; P3, EP
+ *   section: combine restores token order and accumulates per token.]
+ *   y [M_cap, d] bf16, row_of [T*k], w [T, k] fp32 or NULL (in),
+ *   out [T, d] bf16 (out). Requires d % 8 == 0, 16-byte aligned y and out.
+ */
+int moe_combine(const uint16_t* y, const int32_t* row_of, const float* w,
+                int T, int k, int d, uint16_t* out, moe_stream_t stream);
+
+/* MXFP8 side of the forward (all device pointers). E4M3 codes (OCP, bias 7,
+ * saturating to +-448), E8M0 block scales (code = exponent + 127) over 32
+ * elements: shared exponent floor(log2 amax) - 8, zero block -> code 0. */
+typedef struct moe_mx_fwd {
+    uint8_t* a_q;          /* [M_cap, n]    row-wise codes of A (out)            */
+    uint8_t* a_s;          /* [M_cap, n/32] row-wise scales of A (out)           */
+    uint8_t* at_q;         /* [n, M_cap]    transposed (column-wise) codes, or NULL */
+    uint8_t* at_s;         /* [n, M_cap/32] transposed scales, or NULL           */
+    const uint8_t* w2t_q;  /* [E, d, n]     W2_e quantized along n, transposed (in) */
+    const uint8_t* w2t_s;  /* [E, d, n/32]  its scales (in)                      */
+} moe_mx_fwd;
+
+/*
+ * moe_grouped_mlp_fwd -- grouped FC1 + SwiGLU epilogue, then grouped FC2,
+ * one launch each over all experts, tiles scheduled from device offsets;
+ * empty experts take no tiles.
+ *   [P1, problem and core-idea sections: the GLU activation fused into the
+ *   FC1 GEMM epilogue over interleaved weights; P3, grouped-GEMM section: one
+ *   call for all experts computing only the real rows.]
+ *   FC1: H = X_perm[R_e] W1_e (fp32 accumulate); A = bf16(silu(g) * u) from
+ *        the fp32 accumulators; H is stored (bf16) when h != NULL.
+ *   FC2: Y = bf16(A[R_e] W2_e); with mx != NULL the FC1 epilogue also writes
+ *        the MXFP8 row-wise (and, if at_q != NULL, transposed) copy of the
+ *        bf16 A [P1, core-idea section: MXFP8 and transposed output fused in
+ *        the GEMM], and FC2 runs on MX-scaled MFMA from a_q/a_s and
+ *        w2t_q/w2t_s instead of w2 [P3, three-components section: MXFP8
+ *        grouped GEMM].
+ *   x_perm [M_cap, d], w1 [E, d, 2n], w2 [E, n, d] (bf16, in);
+ *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out),
+ *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
+ *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a).
+ * Requires d % 64 == 0, n % 64 == 0, act == MOE_ACT_SWIGLU,
+ * M_cap % 128 == 0; 16-byte aligned pointers.
+ */
+int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
+                        const int32_t* offsets, int E, int d, int n, int64_t M_cap,
+                        int act, unsigned stages, uint16_t* h, uint16_t* a, uint16_t* y,
+                        const moe_mx_fwd* mx, moe_stream_t stream);
+
+/*
+ * moe_grouped_mlp_bwd -- backward of the expert MLP for fixed routing.
+ *   [P2, backward-rewrite section: dS_{t,e} = <dO_t, Y> = <dO_t W2^T, A>;
+ *   GEMM-overlapping section: the dH kernel reloads H in its epilogue and
+ *   stores dH, dS and A'; P1, published-evidence section: dSwiGLU fused into
+ *   the dgrad GEMM.]
+ *   DGRAD2: dA' = dY_u[R_e] W2_e^T (fp32); epilogue with a = silu(g) u from
+ *           the stored H and w = topk_w of the row's pair (0 for padding):
+ *           dS partials += dA' . a per row; dA = w dA';
+ *           dg = dA u s (1 + g (1 - s)), s = sigmoid(g); du = dA silu(g);
+ *           dH = bf16 interleaved (dg, du); A' = bf16(w a);
+ *           then ds[t, j] = sum of the row's partials in a fixed order.
+ *   WGRAD2: dW2_e = A'[R_e]^T dY_u[R_e] (fp32; exactly 0 for empty experts).
+ *   DGRAD1: dX_perm[R_e] = bf16(dH[R_e] W1_e^T).
+ *   WGRAD1: dW1_e = X_perm[R_e]^T dH[R_e] (fp32, interleaved like w1).
+ *   dy_u = moe_permute of dO (unweighted). Stages run in the order above.
+ *   x_perm, dy_u [M_cap, d]; w1 [E, d, 2n]; w2 [E, n, d]; h [M_cap, 2n]
+ *   (bf16, in); topk_w [T, k] fp32, src_of [M_cap], row_of [T*k],
+ *   offsets [E+1] (in); dh [M_cap, 2n], a_w [M_cap, n], dx_perm [M_cap, d]
+ *   (bf16, out); ds [T, k] fp32 (out); dw1 [E, d, 2n], dw2 [E, n, d]
+ *   (fp32, out). Outputs of stages not requested may be NULL.
+ *   workspace: >= moe_mlp_bwd_workspace_bytes(n, M_cap) bytes.
+ * Requires the shape constraints of moe_grouped_mlp_fwd.
+ */
+int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
+                        const uint16_t* h, const uint16_t* dy_u, const float* topk_w,
+                        const int32_t* src_of, const int32_t* row_of, const int32_t* offsets,
+                        int T, int k, int E, int d, int n, int64_t M_cap, int act,
+                        unsigned stages, uint16_t* dh, uint16_t* a_w, float* ds,
+                        uint16_t* dx_perm, float* dw1, float* dw2,
+                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * moe_quant_mxfp8 -- standalone MXFP8 quantization of `batch` bf16 matrices
+ * src [batch, R, C] [P3, three-components section: group-aware MXFP8
+ * quantization; P1, problem section: the BF16 -> MXFP8 pass plus its
+ * transposed copy].
+ *   MOE_QUANT_ROWWISE: blocks of 32 consecutive columns;
+ *     q_row [batch, R, C] codes, s_row [batch, R, C/32] scales.
+ *   MOE_QUANT_COLWISE: blocks of 32 consecutive rows, stored transposed;
+ *     q_col [batch, C, R] codes, s_col [batch, C, R/32] scales.
+ *   Row-wise needs C % 32 == 0, column-wise R % 32 == 0. On the expert-major
+ *   buffer every 32-row block lies inside one expert region (regions are
+ *   128-row aligned), which is what makes the quantization group-aware.
+ */
+int moe_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode,
+                    uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                    moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,181 @@
+// extern "C" entry points of libmoe: host-side validation, then kernel launches
+// on the caller's stream. Nothing here allocates, synchronises or reads device
+// memory; every shape that depends on the routing stays on the device.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t S(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int64_t capacity(int T, int k, int E) {
+    if (T <= 0 || k <= 0 || E <= 0 || k > E || E > MOE_MAX_EXPERTS) return -1;
+    return align_up((int64_t)T * k, MOE_ALIGN) + (int64_t)MOE_ALIGN * E;
+}
+
+// Shapes of the grouped MLP that the kernels support.
+int check_mlp_shape(int E, int d, int n, int64_t M_cap, int act) {
+    if (E <= 0 || E > MOE_MAX_EXPERTS || d <= 0 || n <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
+    if (act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+    if (d % 64 || n % 64 || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
+    if (M_cap > (int64_t)1 << 30 || (int64_t)d * 2 * n > ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+int64_t moe_capacity_rows(int T, int k, int E) { return capacity(T, k, E); }
+
+size_t moe_route_workspace_bytes(int T, int k, int E) {
+    if (capacity(T, k, E) < 0) return 0;
+    return moe::route_workspace_bytes(T, k, E);
+}
+
+size_t moe_mlp_bwd_workspace_bytes(int n, int64_t M_cap) {
+    if (n <= 0 || M_cap <= 0) return 0;
+    return (size_t)M_cap * moe::ds_partials_per_row(n) * sizeof(float);
+}
+
+int moe_route_counts(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* src_of, int64_t M_cap, int32_t* err_word, void* workspace,
+                     size_t workspace_bytes, moe_stream_t stream) {
+    const int64_t cap = capacity(T, k, E);
+    if (cap < 0) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_idx || !topk_w || !counts || !offsets || !row_of || !src_of || !workspace)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return MOE_ERR_INVALID_ARG;
+    if (M_cap < cap || M_cap > ((int64_t)1 << 31) - 1) return MOE_ERR_WORKSPACE;
+    if (workspace_bytes < moe::route_workspace_bytes(T, k, E)) return MOE_ERR_WORKSPACE;
+    const int rc = moe::launch_route(logits, T, E, k, renorm, topk_idx, topk_w, counts, offsets,
+                                     row_of, src_of, M_cap, err_word, workspace, S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
+int moe_permute(const uint16_t* x, const int32_t* src_of, const int32_t* offsets, int T, int k,
+                int E, int d, int64_t M_cap, uint16_t* x_perm, moe_stream_t stream) {
+    const int64_t cap = capacity(T, k, E);
+    if (cap < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
+    if (!x || !src_of || !offsets || !x_perm) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+    if (d % 8) return MOE_ERR_UNSUPPORTED;
+    if (M_cap < cap) return MOE_ERR_WORKSPACE;
+    const int rc = moe::launch_permute(x, src_of, offsets, k, E, d, M_cap, x_perm, S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
+int moe_combine(const uint16_t* y, const int32_t* row_of, const float* w, int T, int k, int d,
+                uint16_t* out, moe_stream_t stream) {
+    if (T <= 0 || k <= 0 || d <= 0 || k > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+    if (!y || !row_of || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(out)) return MOE_ERR_INVALID_ARG;
+    if (d % 8) return MOE_ERR_UNSUPPORTED;
+    const int rc = moe::launch_combine(y, row_of, w, T, k, d, out, S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
+int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
+                        const int32_t* offsets, int E, int d, int n, int64_t M_cap, int act,
+                        unsigned stages, uint16_t* h, uint16_t* a, uint16_t* y,
+                        const moe_mx_fwd* mx, moe_stream_t stream) {
+    int rc = check_mlp_shape(E, d, n, M_cap, act);
+    if (rc) return rc;
+    if (!offsets || !a) return MOE_ERR_INVALID_ARG;
+    if ((stages & ~(unsigned)MOE_STAGES_FWD) || stages == 0) return MOE_ERR_INVALID_ARG;
+    if (mx) return MOE_ERR_UNSUPPORTED;
+    if (stages & MOE_STAGE_FC1) {
+        if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
+        if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
+    }
+    if (!aligned16(a)) return MOE_ERR_INVALID_ARG;
+    if (stages & MOE_STAGE_FC2) {
+        if (!w2 || !y || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+    }
+    hipStream_t s = S(stream);
+    if (stages & MOE_STAGE_FC1)
+        if (moe::launch_fc1_swiglu(x_perm, w1, offsets, E, d, n, M_cap, h, a, s)) return MOE_ERR_LAUNCH;
+    if (stages & MOE_STAGE_FC2)
+        if (moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, s)) return MOE_ERR_LAUNCH;
+    return MOE_OK;
+}
+
+int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
+                        const uint16_t* h, const uint16_t* dy_u, const float* topk_w,
+                        const int32_t* src_of, const int32_t* row_of, const int32_t* offsets,
+                        int T, int k, int E, int d, int n, int64_t M_cap, int act, unsigned stages,
+                        uint16_t* dh, uint16_t* a_w, float* ds, uint16_t* dx_perm, float* dw1,
+                        float* dw2, void* workspace, size_t workspace_bytes,
+                        moe_stream_t stream) {
+    int rc = check_mlp_shape(E, d, n, M_cap, act);
+    if (rc) return rc;
+    const int64_t cap = capacity(T, k, E);
+    if (cap < 0) return MOE_ERR_INVALID_ARG;
+    if (M_cap < cap) return MOE_ERR_WORKSPACE;
+    if ((stages & ~(unsigned)MOE_STAGES_BWD) || stages == 0) return MOE_ERR_INVALID_ARG;
+    if (!offsets) return MOE_ERR_INVALID_ARG;
+    if (stages & MOE_STAGE_DGRAD2) {
+        if (!dy_u || !w2 || !h || !topk_w || !src_of || !row_of || !dh || !a_w || !ds || !workspace)
+            return MOE_ERR_INVALID_ARG;
+        if (!aligned16(dy_u) || !aligned16(w2) || !aligned16(h) || !aligned16(dh) ||
+            !aligned16(a_w) || !aligned16(workspace))
+            return MOE_ERR_INVALID_ARG;
+        if (workspace_bytes < moe_mlp_bwd_workspace_bytes(n, M_cap)) return MOE_ERR_WORKSPACE;
+    }
+    if (stages & MOE_STAGE_WGRAD2) {
+        if (!a_w || !dy_u || !dw2 || !aligned16(a_w) || !aligned16(dy_u) || !aligned16(dw2))
+            return MOE_ERR_INVALID_ARG;
+    }
+    if (stages & MOE_STAGE_DGRAD1) {
+        if (!dh || !w1 || !dx_perm || !aligned16(dh) || !aligned16(w1) || !aligned16(dx_perm))
+            return MOE_ERR_INVALID_ARG;
+    }
+    if (stages & MOE_STAGE_WGRAD1) {
+        if (!x_perm || !dh || !dw1 || !aligned16(x_perm) || !aligned16(dh) || !aligned16(dw1))
+            return MOE_ERR_INVALID_ARG;
+    }
+    hipStream_t s = S(stream);
+    float* part = static_cast<float*>(workspace);
+    if (stages & MOE_STAGE_DGRAD2) {
+        if (moe::launch_dgrad2_dswiglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, dh,
+                                       a_w, part, s))
+            return MOE_ERR_LAUNCH;
+        if (moe::launch_ds_reduce(part, row_of, T, k, n, ds, s)) return MOE_ERR_LAUNCH;
+    }
+    if (stages & MOE_STAGE_WGRAD2)
+        if (moe::launch_wgrad(a_w, n, dy_u, d, offsets, E, dw2, s)) return MOE_ERR_LAUNCH;
+    if (stages & MOE_STAGE_DGRAD1)
+        if (moe::launch_dgrad1(dh, w1, offsets, E, d, n, M_cap, dx_perm, s)) return MOE_ERR_LAUNCH;
+    if (stages & MOE_STAGE_WGRAD1)
+        if (moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, dw1, s)) return MOE_ERR_LAUNCH;
+    return MOE_OK;
+}
+
+int moe_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
+                    uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, moe_stream_t stream) {
+    if (!src || batch <= 0 || R <= 0 || C <= 0) return MOE_ERR_INVALID_ARG;
+    if (mode <= 0 || (mode & ~(MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE))) return MOE_ERR_INVALID_ARG;
+    if ((mode & MOE_QUANT_ROWWISE) && (!q_row || !s_row)) return MOE_ERR_INVALID_ARG;
+    if ((mode & MOE_QUANT_COLWISE) && (!q_col || !s_col)) return MOE_ERR_INVALID_ARG;
+    if ((mode & MOE_QUANT_ROWWISE) && C % MOE_MX_BLOCK) return MOE_ERR_UNSUPPORTED;
+    if ((mode & MOE_QUANT_COLWISE) && R % MOE_MX_BLOCK) return MOE_ERR_UNSUPPORTED;
+    return MOE_ERR_UNSUPPORTED;  // not built yet
+}
+
+}  // extern "C"

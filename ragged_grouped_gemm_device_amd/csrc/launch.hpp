@@ -1,0 +1,47 @@
+// Internal launcher declarations of libmoe (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define MOE_MAX_E 1024
+#define MOE_ALIGN_ROWS 128
+#define MOE_ERRBIT_NONFINITE_LOGIT 0x1
+
+namespace moe {
+
+constexpr int kChunkPairs = 1024;  // pairs per wavefront chunk of the layout sort
+
+int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                 float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                 int32_t* src_of, int64_t M_cap, int32_t* err_word, void* ws, hipStream_t s);
+size_t route_workspace_bytes(int T, int k, int E);
+
+int launch_permute(const uint16_t* x, const int32_t* src_of, const int32_t* offsets, int k, int E,
+                   int d, int64_t M_cap, uint16_t* x_perm, hipStream_t s);
+int launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, int T, int k, int d,
+                   uint16_t* out, hipStream_t s);
+
+// Grouped GEMMs. All take the device offsets [E+1] of the ragged layout.
+int launch_fc1_swiglu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
+                      int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, hipStream_t s);
+int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
+               int64_t M_cap, uint16_t* y, hipStream_t s);
+int launch_dgrad2_dswiglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
+                          const float* topk_w, const int32_t* src_of, const int32_t* offsets,
+                          int E, int d, int n, int64_t M_cap, uint16_t* dh, uint16_t* a_w,
+                          float* ds_part, hipStream_t s);
+int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,
+                     float* ds, hipStream_t s);
+int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets, int E, int d,
+                  int n, int64_t M_cap, uint16_t* dx_perm, hipStream_t s);
+int launch_wgrad(const uint16_t* act, int Ma, const uint16_t* grad, int Nb, const int32_t* offsets,
+                 int E, float* dw, hipStream_t s);
+int ds_partials_per_row(int n);
+
+// MXFP8
+int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
+                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,233 @@
+// Routing and ragged layout kernels (gfx950).
+//
+// route_topk_kernel: softmax over E + top-k per token, one wavefront per token.
+//   [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, section on ragged
+//   tensors: a learned router activates each token's top-K experts.]
+// layout kernels: per-expert counts, 128-aligned offsets and the two row maps,
+//   computed on the device with no host readback, deterministically (a stable
+//   counting sort: per-chunk histograms, an exclusive scan over chunks, then
+//   in-order ranks from wavefront ballots; no atomics decide an order).
+//   [NVIDIA CuTe DSL fusion-kernel page, core-idea section: per-expert token
+//   counts live in GPU memory; Transformer Engine page, grouped-GEMM section:
+//   expert regions aligned to 128 tokens; dropless-boundary section: one slot
+//   per (token, expert) pair, regions padded to the alignment unit.]
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kMaxPerLane = MOE_MAX_E / 64;   // logits held per lane (E <= 1024)
+
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int renorm,
+                                                         int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w,
+                                                         int32_t* __restrict__ err_word) {
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + (int64_t)t * E;
+    float v[kMaxPerLane];
+    bool bad = false;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        float x = -INFINITY;
+        if (e < E) {
+            x = row[e];
+            if (!isfinite(x)) {
+                bad = true;
+                x = -INFINITY;  // a non-finite logit is never preferred
+            }
+        }
+        v[i] = x;
+        mx = fmaxf(mx, x);
+    }
+    if (__ballot(bad) != 0ull && lane == 0 && err_word) atomicOr(err_word, MOE_ERRBIT_NONFINITE_LOGIT);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+        if (lane + 64 * i < E && v[i] > -INFINITY) s += expf(v[i] - mx);
+    s = wave_sum(s);
+    if (!(mx > -INFINITY)) s = 1.f;  // every logit non-finite: weights become 0
+
+    uint32_t taken = 0;  // bit i: v[i] already selected
+    float chosen_w[8];
+    float wsum = 0.f;
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        const float p = (bv > -INFINITY) ? expf(bv - mx) / s : 0.f;
+        wsum += p;
+        if (j < 8) chosen_w[j] = p;
+        if (lane == 0) {
+            topk_idx[(int64_t)t * k + j] = bi;
+            if (!renorm) topk_w[(int64_t)t * k + j] = p;
+        }
+    }
+    if (renorm && lane == 0) {
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+        for (int j = 0; j < k; ++j) {
+            float p;
+            if (j < 8) {
+                p = chosen_w[j];
+            } else {
+                const int e = topk_idx[(int64_t)t * k + j];
+                p = expf(row[e] - mx) / s;  // k > 8: recompute from the logit
+            }
+            topk_w[(int64_t)t * k + j] = p * inv;
+        }
+    }
+}
+
+// Lanes of this wavefront whose value of e (0 <= e < 2^nbits) equals ours.
+__device__ __forceinline__ uint64_t match_lanes(int e, bool valid, int nbits) {
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return valid ? m : 0ull;
+}
+
+// Per-chunk histograms (chunk = kChunkPairs consecutive pairs, one wavefront)
+// and the -1 fill of src_of.
+__global__ void __launch_bounds__(256) layout_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                          int64_t P, int E, int nchunks,
+                                                          int32_t* __restrict__ hist,
+                                                          int32_t* __restrict__ src_of,
+                                                          int64_t M_cap) {
+    extern __shared__ int32_t s_cnt[];  // [4][E]
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    int32_t* cnt = s_cnt + wave * E;
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    // fill src_of with -1 (grid-stride)
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < M_cap; r += (int64_t)gridDim.x * 256)
+        src_of[r] = -1;
+    const int chunk = blockIdx.x * 4 + wave;
+    __syncthreads();
+    if (chunk < nchunks) {
+        const int64_t base = (int64_t)chunk * kChunkPairs;
+        for (int s = 0; s < kChunkPairs; s += 64) {
+            const int64_t p = base + s + lane;
+            if (p < P) atomicAdd(&cnt[topk_idx[p]], 1);  // integer sum: order-free
+        }
+    }
+    __syncthreads();
+    if (chunk < nchunks)
+        for (int e = lane; e < E; e += 64) hist[(int64_t)chunk * E + e] = cnt[e];
+}
+
+// Exclusive scan of the histograms over chunks (per expert), counts, and the
+// 128-aligned offsets. One workgroup.
+__global__ void __launch_bounds__(1024) layout_scan_kernel(const int32_t* __restrict__ hist,
+                                                           int nchunks, int E,
+                                                           int32_t* __restrict__ base,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets) {
+    __shared__ int32_t s_pad[MOE_MAX_E];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            base[(int64_t)c * E + e] = run;
+            run += hist[(int64_t)c * E + e];
+        }
+        counts[e] = run;
+        s_pad[e] = (run + MOE_ALIGN_ROWS - 1) / MOE_ALIGN_ROWS * MOE_ALIGN_ROWS;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t o = 0;
+        offsets[0] = 0;
+        for (int e = 0; e < E; ++e) {
+            o += s_pad[e];
+            offsets[e + 1] = o;
+        }
+    }
+}
+
+// In-order ranks: each wavefront walks its chunk 64 pairs at a time.
+__global__ void __launch_bounds__(256) layout_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                             int64_t P, int E, int nbits,
+                                                             int nchunks,
+                                                             const int32_t* __restrict__ base,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ row_of,
+                                                             int32_t* __restrict__ src_of) {
+    extern __shared__ int32_t s_cnt[];  // [4][E]
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    int32_t* cnt = s_cnt + wave * E;
+    const int chunk = blockIdx.x * 4 + wave;
+    if (chunk >= nchunks) return;  // wave-private LDS: no block barrier below
+    for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)chunk * E + e] + offsets[e];
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t b0 = (int64_t)chunk * kChunkPairs;
+    for (int s = 0; s < kChunkPairs; s += 64) {
+        const int64_t p = b0 + s + lane;
+        const bool valid = p < P;
+        const int e = valid ? topk_idx[p] : 0;
+        const uint64_t m = match_lanes(e, valid, nbits);
+        int32_t row = 0;
+        if (valid) row = cnt[e] + __popcll(m & lt);
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (valid && (m & lt) == 0ull) cnt[e] = row + __popcll(m);  // group leader advances
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            row_of[p] = row;
+            src_of[row] = (int32_t)p;
+        }
+    }
+}
+
+int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                 float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                 int32_t* src_of, int64_t M_cap, int32_t* err_word, void* ws, hipStream_t s) {
+    const int64_t P = (int64_t)T * k;
+    const int nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
+    int32_t* hist = (int32_t*)ws;
+    int32_t* base = hist + (int64_t)nchunks * E;
+    route_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w, err_word);
+    const int nblk = (nchunks + 3) / 4;
+    const size_t lds = 4 * (size_t)E * sizeof(int32_t);
+    layout_hist_kernel<<<nblk, 256, lds, s>>>(topk_idx, P, E, nchunks, hist, src_of, M_cap);
+    layout_scan_kernel<<<1, 1024, 0, s>>>(hist, nchunks, E, base, counts, offsets);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    layout_scatter_kernel<<<nblk, 256, lds, s>>>(topk_idx, P, E, nbits, nchunks, base, offsets,
+                                                 row_of, src_of);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+size_t route_workspace_bytes(int T, int k, int E) {
+    const int64_t P = (int64_t)T * k;
+    const int64_t nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+    return (size_t)(2 * nchunks * E) * sizeof(int32_t);
+}
+
+}  // namespace moe

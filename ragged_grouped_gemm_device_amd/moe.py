@@ -1,0 +1,239 @@
+"""ctypes binding of libmoe.so: the C ABI of include/moe.h with the same names.
+
+Argument marshalling only: every step runs in the library's HIP kernels, on
+torch's current HIP stream. torch tensors supply device memory; bf16 tensors
+are passed by address (torch.bfloat16 or int16/uint16 bit patterns).
+Failing to load the library raises immediately -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_LAUNCH = -4
+MOE_ALIGN = 128
+MOE_MX_BLOCK = 32
+MOE_GLU_INTERLEAVE = 32
+MOE_MAX_EXPERTS = 1024
+MOE_ACT_SWIGLU = 0
+MOE_STAGE_FC1 = 0x01
+MOE_STAGE_FC2 = 0x02
+MOE_STAGE_DGRAD2 = 0x04
+MOE_STAGE_WGRAD2 = 0x08
+MOE_STAGE_DGRAD1 = 0x10
+MOE_STAGE_WGRAD1 = 0x20
+MOE_STAGES_FWD = MOE_STAGE_FC1 | MOE_STAGE_FC2
+MOE_STAGES_BWD = MOE_STAGE_DGRAD2 | MOE_STAGE_WGRAD2 | MOE_STAGE_DGRAD1 | MOE_STAGE_WGRAD1
+MOE_ERRBIT_NONFINITE_LOGIT = 0x1
+MOE_QUANT_ROWWISE = 0x1
+MOE_QUANT_COLWISE = 0x2
+
+# (name, restype, argtypes) of every exported symbol
+_P = C.c_void_p
+_I = C.c_int
+_I64 = C.c_int64
+_SZ = C.c_size_t
+SIGNATURES = {
+    "moe_status_str": (C.c_char_p, [_I]),
+    "moe_capacity_rows": (_I64, [_I, _I, _I]),
+    "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_mlp_bwd_workspace_bytes": (_SZ, [_I, _I64]),
+    "moe_route_counts": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_permute": (_I, [_P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
+    "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P, _P, _P]),
+    "moe_grouped_mlp_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I,
+                                 C.c_uint, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_quant_mxfp8": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _P]),
+}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_lib().moe_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+class moe_mx_fwd(C.Structure):
+    _fields_ = [("a_q", _P), ("a_s", _P), ("at_q", _P), ("at_s", _P), ("w2t_q", _P), ("w2t_s", _P)]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run ragged_grouped_gemm_device_amd.build")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def load():
+    """Load libmoe.so (raises if it is missing) and return the CDLL."""
+    return _lib()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoEError(fn, rc)
+
+
+# ------------------------------------------------------------------ host-only
+def moe_status_str(status: int) -> str:
+    return _lib().moe_status_str(status).decode()
+
+
+def moe_capacity_rows(T: int, k: int, E: int) -> int:
+    return int(_lib().moe_capacity_rows(T, k, E))
+
+
+def moe_route_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(_lib().moe_route_workspace_bytes(T, k, E))
+
+
+def moe_mlp_bwd_workspace_bytes(n: int, M_cap: int) -> int:
+    return int(_lib().moe_mlp_bwd_workspace_bytes(n, M_cap))
+
+
+# ------------------------------------------------------------------ device calls
+def moe_route_counts(logits, k, topk_idx, topk_w, counts, offsets, row_of, src_of, M_cap,
+                     err_word, workspace, renorm=False):
+    T, E = logits.shape
+    rc = _lib().moe_route_counts(_ptr(logits), T, E, k, int(bool(renorm)), _ptr(topk_idx),
+                                 _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                 _ptr(src_of), M_cap, _ptr(err_word), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    _check("moe_route_counts", rc)
+
+
+def moe_permute(x, src_of, offsets, k, E, x_perm):
+    T, d = x.shape
+    rc = _lib().moe_permute(_ptr(x), _ptr(src_of), _ptr(offsets), T, k, E, d, x_perm.shape[0],
+                            _ptr(x_perm), _stream())
+    _check("moe_permute", rc)
+
+
+def moe_combine(y, row_of, w, k, out):
+    T, d = out.shape
+    rc = _lib().moe_combine(_ptr(y), _ptr(row_of), _ptr(w), T, k, d, _ptr(out), _stream())
+    _check("moe_combine", rc)
+
+
+def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD, mx=None,
+                        act=MOE_ACT_SWIGLU):
+    E, d, n2 = w1.shape
+    M_cap = a.shape[0]
+    mxp = None
+    if mx is not None:
+        mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s")])
+        mxp = C.byref(mxs)
+    rc = _lib().moe_grouped_mlp_fwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(offsets), E, d, n2 // 2,
+                                    M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y), mxp, _stream())
+    _check("moe_grouped_mlp_fwd", rc)
+
+
+def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets, dh, a_w, ds,
+                        dx_perm, dw1, dw2, workspace, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU):
+    E, d, n2 = w1.shape
+    T, k = topk_w.shape
+    M_cap = src_of.shape[0]
+    rc = _lib().moe_grouped_mlp_bwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(h), _ptr(dy_u),
+                                    _ptr(topk_w), _ptr(src_of), _ptr(row_of), _ptr(offsets), T, k,
+                                    E, d, n2 // 2, M_cap, act, stages, _ptr(dh), _ptr(a_w), _ptr(ds),
+                                    _ptr(dx_perm), _ptr(dw1), _ptr(dw2), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream())
+    _check("moe_grouped_mlp_bwd", rc)
+
+
+def moe_quant_mxfp8(src, mode, q_row=None, s_row=None, q_col=None, s_col=None):
+    if src.dim() == 2:
+        batch, (R, Cc) = 1, src.shape
+    else:
+        batch, R, Cc = src.shape
+    rc = _lib().moe_quant_mxfp8(_ptr(src), batch, R, Cc, mode, _ptr(q_row), _ptr(s_row),
+                                _ptr(q_col), _ptr(s_col), _stream())
+    _check("moe_quant_mxfp8", rc)
+
+
+# ------------------------------------------------------------------ buffers
+class Buffers:
+    """Device buffers of one forward + backward pass (plain torch allocations)."""
+
+    def __init__(self, T: int, k: int, E: int, d: int, n: int, device="cuda", mx: bool = False):
+        dev = torch.device(device)
+        bf, i32, f32, u8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
+        self.T, self.k, self.E, self.d, self.n = T, k, E, d, n
+        self.M_cap = M = moe_capacity_rows(T, k, E)
+        self.topk_idx = torch.empty(T, k, dtype=i32, device=dev)
+        self.topk_w = torch.empty(T, k, dtype=f32, device=dev)
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.row_of = torch.empty(T * k, dtype=i32, device=dev)
+        self.src_of = torch.empty(M, dtype=i32, device=dev)
+        self.err = torch.zeros(1, dtype=i32, device=dev)
+        self.route_ws = torch.empty(max(16, moe_route_workspace_bytes(T, k, E)), dtype=u8, device=dev)
+        self.x_perm = torch.empty(M, d, dtype=bf, device=dev)
+        self.h = torch.empty(M, 2 * n, dtype=bf, device=dev)
+        self.a = torch.empty(M, n, dtype=bf, device=dev)
+        self.y = torch.empty(M, d, dtype=bf, device=dev)
+        self.out = torch.empty(T, d, dtype=bf, device=dev)
+        self.dy_u = torch.empty(M, d, dtype=bf, device=dev)
+        self.dh = torch.empty(M, 2 * n, dtype=bf, device=dev)
+        self.a_w = torch.empty(M, n, dtype=bf, device=dev)
+        self.ds = torch.empty(T, k, dtype=f32, device=dev)
+        self.dx_perm = torch.empty(M, d, dtype=bf, device=dev)
+        self.dx = torch.empty(T, d, dtype=bf, device=dev)
+        self.dw1 = torch.empty(E, d, 2 * n, dtype=f32, device=dev)
+        self.dw2 = torch.empty(E, n, d, dtype=f32, device=dev)
+        self.bwd_ws = torch.empty(max(16, moe_mlp_bwd_workspace_bytes(n, M)), dtype=u8, device=dev)
+        if mx:
+            self.a_q = torch.empty(M, n, dtype=u8, device=dev)
+            self.a_s = torch.empty(M, n // 32, dtype=u8, device=dev)
+            self.at_q = torch.empty(n, M, dtype=u8, device=dev)
+            self.at_s = torch.empty(n, M // 32, dtype=u8, device=dev)
+            self.w2t_q = torch.empty(E, d, n, dtype=u8, device=dev)
+            self.w2t_s = torch.empty(E, d, n // 32, dtype=u8, device=dev)
+
+
+def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True):
+    """route -> permute -> FC1+SwiGLU -> FC2 -> combine (all enqueued, no sync)."""
+    moe_route_counts(logits, buf.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
+                     buf.src_of, buf.M_cap, buf.err, buf.route_ws, renorm)
+    moe_permute(x, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
+    moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
+                        fwd_stages)
+    moe_combine(buf.y, buf.row_of, buf.topk_w, buf.k, buf.out)
+
+
+def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD):
+    """gather dO -> dgrad2+dSwiGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum."""
+    moe_permute(dout, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
+    moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
+                        buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                        buf.bwd_ws, stages)
+    moe_combine(buf.dx_perm, buf.row_of, None, buf.k, buf.dx)

@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every symbol include/moe.h declares, and
+rejects invalid arguments on the host before launching anything (CPU only)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from ragged_grouped_gemm_device_amd import moe as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(M.LIB_PATH), reason="libmoe.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = M.load()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in M.SIGNATURES, n
+
+
+def test_constants_match_header():
+    src = open(HEADER).read()
+    for name in ("MOE_ALIGN", "MOE_MX_BLOCK", "MOE_GLU_INTERLEAVE", "MOE_MAX_EXPERTS",
+                 "MOE_STAGE_FC1", "MOE_STAGE_FC2", "MOE_STAGE_DGRAD2", "MOE_STAGE_WGRAD2",
+                 "MOE_STAGE_DGRAD1", "MOE_STAGE_WGRAD1", "MOE_QUANT_ROWWISE", "MOE_QUANT_COLWISE",
+                 "MOE_ERRBIT_NONFINITE_LOGIT", "MOE_ACT_SWIGLU"):
+        m = re.search(r"#define\s+%s\s+(\(?-?[0-9a-fx]+\)?)" % name, src)
+        assert m, name
+        assert int(m.group(1).strip("()"), 0) == getattr(M, name), name
+    for name in ("MOE_OK", "MOE_ERR_INVALID_ARG", "MOE_ERR_UNSUPPORTED", "MOE_ERR_WORKSPACE",
+                 "MOE_ERR_LAUNCH"):
+        m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, src)
+        assert int(m.group(1)) == getattr(M, name)
+
+
+def test_status_strings_and_capacity():
+    assert M.moe_status_str(0) == "MOE_OK"
+    assert M.moe_status_str(-3) == "MOE_ERR_WORKSPACE"
+    assert M.moe_status_str(12345) == "MOE_ERR_UNKNOWN"
+    assert M.moe_capacity_rows(256, 2, 8) == 512 + 1024
+    assert M.moe_capacity_rows(16384, 8, 32) == 131072 + 4096
+    assert M.moe_capacity_rows(8192, 4, 32) == 32768 + 4096
+    assert M.moe_capacity_rows(1, 1, 1) == 256
+    assert M.moe_capacity_rows(10, 3, 2) == -1          # k > E
+    assert M.moe_capacity_rows(10, 1, 2000) == -1       # E > MOE_MAX_EXPERTS
+    assert M.moe_route_workspace_bytes(0, 1, 1) == 0
+    assert M.moe_mlp_bwd_workspace_bytes(2048, 1024) == 1024 * 16 * 4
+
+
+def _fake(addr=0x1000):
+    return C.c_void_p(addr)
+
+
+def test_host_validation_returns_before_launch():
+    lib = M.load()
+    f = _fake()
+    # NULL logits
+    rc = lib.moe_route_counts(None, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, f, 1 << 20, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    # k > E
+    rc = lib.moe_route_counts(f, 8, 4, 5, 0, f, f, f, f, f, f, 1024, None, f, 1 << 20, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    # capacity too small
+    rc = lib.moe_route_counts(f, 8, 4, 2, 0, f, f, f, f, f, f, 100, None, f, 1 << 20, None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    # workspace too small
+    rc = lib.moe_route_counts(f, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, f, 0, None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    rc = lib.moe_route_counts(f, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, _fake(0x1004), 1 << 20, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    # permute: d not a multiple of 8
+    rc = lib.moe_permute(f, f, f, 8, 2, 4, 12, 1024, f, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_permute(_fake(0x1002), f, f, 8, 2, 4, 16, 1024, f, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    # combine: NULL output
+    rc = lib.moe_combine(f, f, None, 8, 2, 16, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    # mlp fwd: unsupported activation / shapes / stage bits
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 7, 3, None, f, f, None, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 96, 64, 1024, 0, 3, None, f, f, None, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1000, 0, 3, None, f, f, None, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 0, 0x40, None, f, f, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 0, 3, None, f, None, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # FC2 without y
+    # mlp bwd: workspace too small for the dS partials
+    rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x04,
+                                 f, f, f, f, f, f, f, 0, None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 256, 0, 0x04,
+                                 f, f, f, f, f, f, f, 1 << 20, None)
+    assert rc == M.MOE_ERR_WORKSPACE               # M_cap below capacity
+    # quant: bad mode / shape
+    rc = lib.moe_quant_mxfp8(f, 1, 64, 64, 0, f, f, f, f, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_quant_mxfp8(f, 1, 64, 48, 1, f, f, None, None, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED
+    rc = lib.moe_quant_mxfp8(f, 1, 40, 64, 2, None, None, f, f, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED

@@ -1,0 +1,138 @@
+"""GPU parity of the whole hot path (forward and backward) against the oracle.
+
+Sizes run through several 256 x 256 tiles, ragged expert segments, empty
+experts, partial N tiles and the all-tokens-to-one-expert case. Every output
+buffer is poisoned with NaN first, so every defined element must be written.
+Tolerance: max-abs-normalised error <= 2e-2 per floating tensor; integer and
+copied tensors bit-exact; padding rows exactly zero; dW of empty experts 0.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from ragged_grouped_gemm_device_amd import workloads as W
+
+from ._util import bf16_bits, bf16_tensor, bf16_values, f32_tensor, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+CASES = [
+    W.WORKLOADS["tiny"],
+    W.small("ragged", T=700, k=3, E=6, d=192, n=320, seed=21, routing="zipf"),
+    W.small("empty", T=300, k=2, E=16, d=256, n=128, seed=22, routing="zipf"),
+    W.small("wide", T=1200, k=2, E=4, d=512, n=384, seed=23),
+    W.small("balanced", T=1024, k=1, E=4, d=256, n=256, seed=24, routing="balanced"),
+]
+
+
+@pytest.fixture(scope="module")
+def M():
+    from ragged_grouped_gemm_device_amd import moe
+    moe.load()
+    return moe
+
+
+def _poison(buf):
+    for name in ("x_perm", "h", "a", "y", "out", "dy_u", "dh", "a_w", "ds", "dx_perm", "dx",
+                 "dw1", "dw2"):
+        getattr(buf, name).fill_(float("nan"))
+
+
+def _run_gpu(M, wl, inp, constant_logits=False):
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n)
+    _poison(buf)
+    x = bf16_tensor(inp["x"])
+    logits = f32_tensor(inp["logits"])
+    w1 = bf16_tensor(inp["w1"])
+    w2 = bf16_tensor(inp["w2"])
+    dout = bf16_tensor(inp["dout"])
+    M.forward(buf, x, logits, w1, w2)
+    M.backward(buf, dout, w1, w2)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _oracle(wl, inp):
+    x = O.from_bf16(inp["x"])
+    w1 = O.from_bf16(inp["w1"])
+    w2 = O.from_bf16(inp["w2"])
+    f = O.forward(x, inp["logits"], w1, w2, wl.k)
+    b = O.mlp_backward(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"]), f["topk_w"],
+                       f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k)
+    return f, b
+
+
+def _check(name, got, ref, rows=None, tol=TOL):
+    if rows is not None:
+        got, ref = got[:rows], ref[:rows]
+    assert np.isfinite(got).all(), f"{name}: unwritten (NaN) or non-finite elements"
+    err = rel_err(got, ref)
+    print(f"  {name}: max-abs-normalised error {err:.3e}", flush=True)
+    assert err <= tol, f"{name}: {err}"
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_forward_backward_parity(M, wl):
+    print(f"mlp case {wl}", flush=True)
+    inp = W.make_inputs(wl)
+    buf = _run_gpu(M, wl, inp)
+    f, b = _oracle(wl, inp)
+    end = int(f["offsets"][-1])
+
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), f["topk_idx"])
+    assert np.array_equal(buf.counts.cpu().numpy(), f["counts"])
+    assert np.array_equal(buf.offsets.cpu().numpy(), f["offsets"])
+    assert np.array_equal(buf.row_of.cpu().numpy(), f["row_of"])
+    assert np.array_equal(buf.src_of.cpu().numpy(), f["src_of"])
+    assert np.array_equal(bf16_bits(buf.x_perm)[:end], O.bf16_bits(f["x_perm"][:end]))
+    assert np.array_equal(bf16_bits(buf.dy_u)[:end], O.bf16_bits(b["dy_u"][:end]))
+
+    _check("H", bf16_values(buf.h), f["H"], end)
+    _check("A", bf16_values(buf.a), f["A"], end)
+    _check("Y", bf16_values(buf.y), f["Y"], end)
+    _check("out", bf16_values(buf.out), f["out"])
+    _check("dS", buf.ds.cpu().numpy(), b["dS"])
+    _check("dH", bf16_values(buf.dh), b["dH"], end)
+    _check("A'", bf16_values(buf.a_w), b["a_w"], end)
+    _check("dX_perm", bf16_values(buf.dx_perm), b["dx_perm"], end)
+    _check("dX", bf16_values(buf.dx), b["dx"])
+    _check("dW1", buf.dw1.cpu().numpy(), b["dW1"])
+    _check("dW2", buf.dw2.cpu().numpy(), b["dW2"])
+
+    # padding rows of every permuted tensor are exactly zero
+    pad = f["src_of"][:end] < 0
+    for name in ("x_perm", "h", "a", "y", "dy_u", "dh", "a_w", "dx_perm"):
+        v = bf16_bits(getattr(buf, name))[:end][pad]
+        assert np.all((v == 0) | (v == 0x8000)), name
+    # empty experts: exactly zero weight gradients
+    for e in np.nonzero(f["counts"] == 0)[0]:
+        assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
+
+
+def test_all_tokens_to_one_expert(M):
+    wl = W.small("one", T=520, k=1, E=8, d=128, n=128, seed=31)
+    inp = W.make_inputs(wl)
+    inp["logits"][:] = 0.0                     # ties everywhere -> expert 0
+    buf = _run_gpu(M, wl, inp)
+    f, b = _oracle(wl, inp)
+    assert list(buf.counts.cpu().numpy()) == [520, 0, 0, 0, 0, 0, 0, 0]
+    _check("out", bf16_values(buf.out), f["out"])
+    _check("dX", bf16_values(buf.dx), b["dx"])
+    _check("dW1", buf.dw1.cpu().numpy(), b["dW1"])
+    assert torch.all(buf.dw1[1:] == 0) and torch.all(buf.dw2[1:] == 0)
+
+
+def test_determinism(M):
+    wl = CASES[1]
+    inp = W.make_inputs(wl)
+    a = _run_gpu(M, wl, inp)
+    b = _run_gpu(M, wl, inp)
+    end = int(a.offsets[-1])
+    for name in ("topk_w", "out", "ds", "dx", "dw1", "dw2"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    for name in ("h", "a", "y", "dh", "a_w", "dx_perm"):
+        assert torch.equal(getattr(a, name)[:end], getattr(b, name)[:end]), name
