@@ -1,0 +1,229 @@
+"""Benchmark of the dropless MoE expert MLP hot path on one MI355X.
+
+One step = the whole path over one batch: route -> counts/offsets -> permute
+-> FC1+SwiGLU -> FC2 -> combine, then gather dO -> FC2 dgrad+dSwiGLU (+dS)
+-> FC2 wgrad -> FC1 dgrad -> FC1 wgrad -> unpermute-sum. Inputs are seeded
+synthetic tensors already resident in HBM when timing starts.
+
+value = algorithmic GEMM FLOPs of the step (real routed rows only,
+18 * T*k * d * n) / step time, in TFLOP/s. The dominant kernel (FC1 +
+SwiGLU) is also timed with HIP events on the stream it runs on, inside the
+timed steps, for the roofline object. The CPU oracle is timed on a bounded
+sample of the same workload for the cpu_baseline object.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "grouped-MLP TFLOP/s fwd & bwd (% of MFMA peak); permute/quant GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def _t16(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _cpu_baseline(wl, inp, target_s=15.0):
+    """Time the oracle on the first R tokens (routed like the full batch)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    def run(R):
+        x = O.from_bf16(inp["x"][:R])
+        w1 = O.from_bf16(inp["w1"])
+        w2 = O.from_bf16(inp["w2"])
+        t0 = time.perf_counter()
+        f = O.forward(x, inp["logits"][:R], w1, w2, wl.k)
+        O.mlp_backward(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"][:R]),
+                       f["topk_w"], f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k)
+        return time.perf_counter() - t0
+
+    R = 128
+    dt = run(R)
+    R2 = int(min(wl.T, max(R, R * target_s / max(dt, 1e-3))))
+    R2 = max(128, R2 // 128 * 128)
+    dt2 = run(R2)
+    flops = 18.0 * R2 * wl.k * wl.d * wl.n
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": flops / dt2 / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"first {R2} of {wl.T} tokens of the {wl.name} workload (top-{wl.k}), whole "
+                  f"forward+backward in numpy fp64, {dt2:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="balanced")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--detail", action="store_true", help="also time every stage alone (stderr)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
+              "collectives; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from ragged_grouped_gemm_device_amd import moe as M
+    from ragged_grouped_gemm_device_amd import workloads as W
+
+    M.load()
+    wl = W.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(wl)
+    print(f"[bench] inputs for {wl.name} generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    torch.cuda.set_device(0)
+    x, w1, w2, dout = (_t16(inp[key], torch) for key in ("x", "w1", "w2", "dout"))
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n)
+    stream = torch.cuda.current_stream()
+
+    ev = []  # (start, end) of the FC1 launch in each timed step
+
+    def step(record=False):
+        M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
+                           buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
+        M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1)
+        if record:
+            e1.record(stream)
+            ev.append((e0, e1))
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2)
+        M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
+        M.backward(buf, dout, w1, w2)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(record=True)
+        if i % 10 == 9:
+            print(f"[bench] step {i + 1}/{args.steps}", file=sys.stderr, flush=True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+    fc1_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    assert int(buf.err.item()) == 0
+
+    M_rows = wl.T * wl.k
+    flops = 18.0 * M_rows * wl.d * wl.n
+    fc1_flops = 4.0 * M_rows * wl.d * wl.n
+    fc1_tf = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    value = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
+          f"FC1+SwiGLU {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    if args.detail:
+        _detail(M, torch, wl, buf, x, w1, w2, dout, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(wl, inp)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
+                        f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+SwiGLU->FC2->combine"
+                        f" + full backward with dSwiGLU, dS and ragged wgrads",
+            "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
+            "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": {
+            "kernel": "grouped_gemm FC1+SwiGLU",
+            "bound": "mfma",
+            "achieved": round(fc1_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fc1_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, reps=10):
+    """Time each stage alone (stderr only)."""
+    def timeit(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    Mr = wl.T * wl.k
+    d, n = wl.d, wl.n
+    end = int(buf.offsets[-1].item())
+    rows = [
+        ("permute", lambda: M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm),
+         None, 2.0 * wl.T * d + 2.0 * end * d + 4.0 * end),
+        ("FC1+SwiGLU", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a,
+                                                     buf.y, M.MOE_STAGE_FC1), 4.0 * Mr * d * n, None),
+        ("FC2", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, buf.y,
+                                              M.MOE_STAGE_FC2), 2.0 * Mr * d * n, None),
+        ("combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out), None,
+         2.0 * Mr * d + 2.0 * wl.T * d + 8.0 * Mr),
+    ]
+    for st, fl in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n), (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n),
+                   (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n), (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n)):
+        rows.append((f"bwd stage 0x{st:02x}", (lambda s=st: M.moe_grouped_mlp_bwd(
+            buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s)), fl, None))
+    for name, fn, fl, by in rows:
+        ms = timeit(fn)
+        msg = f"[detail] {name:16s} {ms * 1e3:9.1f} us"
+        if fl:
+            msg += f"  {fl / ms / 1e9:8.1f} TFLOP/s ({100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS:.1f}% bf16 peak)"
+        if by:
+            msg += f"  {by / ms / 1e6:8.1f} GB/s ({100 * by / ms / 1e6 / PEAK_HBM_GBS:.1f}% HBM)"
+        print(msg, file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -191,7 +191,9 @@ typedef struct moe_mx_fwd {
  *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
  *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a).
  * Requires d % 64 == 0, n % 64 == 0, act == MOE_ACT_SWIGLU,
- * M_cap % 128 == 0; 16-byte aligned pointers.
+ * M_cap % 128 == 0, M_cap * max(d, 2n) * 2 < 2^31 and d * 2n * 2 < 2^31
+ * (operands are addressed with 32-bit byte offsets); 16-byte aligned
+ * pointers. Otherwise MOE_ERR_UNSUPPORTED.
  */
 int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
                         const int32_t* offsets, int E, int d, int n, int64_t M_cap,

@@ -22,7 +22,10 @@ int check_mlp_shape(int E, int d, int n, int64_t M_cap, int act) {
     if (E <= 0 || E > MOE_MAX_EXPERTS || d <= 0 || n <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
     if (act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
     if (d % 64 || n % 64 || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
-    if (M_cap > (int64_t)1 << 30 || (int64_t)d * 2 * n > ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    // the GEMMs address operands with 32-bit buffer offsets (bytes)
+    const int64_t widest = d > 2 * n ? d : 2 * n;
+    if (M_cap * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * 2 * n * 2 >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

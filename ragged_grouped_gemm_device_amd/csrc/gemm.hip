@@ -14,10 +14,13 @@
 // dH, dS and A'; kernel structure prologue/mainloop/epilogue and software
 // pipelining from its GPU-kernel primer and IO-hiding sections.]
 //
-// Workgroup tile 256 x 256 x 64, 4 wavefronts in a 2 x 2 grid, each owning a
-// 128 x 128 sub-tile as 4 x 4 MFMA 32x32 tiles (fp32 accumulators). Operands
-// are staged global -> registers -> LDS (two LDS buffers: the next K slab is
-// fetched while the current one is multiplied). An operand whose K index is
+// Workgroup tile 256 x 256 x 64, 8 wavefronts (two per SIMD) in a 2 x 4 grid,
+// each owning a 128 x 64 sub-tile as 4 x 2 MFMA 32x32 tiles (fp32
+// accumulators); a wavefront raises its issue priority while it runs MFMAs so
+// its sibling's memory instructions fill the gaps. Operands move global -> LDS
+// with direct buffer loads (two LDS buffers: the next K slab streams in while
+// the current one is multiplied); reads past an expert's rows or past N come
+// back as zeros from the buffer bounds. An operand whose K index is
 // contiguous in memory is kept K-major in LDS and read with ds_read_b128; an
 // operand whose M/N index is contiguous is kept MN-major and read with the
 // gfx950 transpose load ds_read_b64_tr_b16, so no operand is transposed in
@@ -30,7 +33,11 @@
 namespace moe {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                 // 2 x 4 wavefronts, 2 per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int WN = 64;                    // columns per wavefront (2 MFMA tiles)
+constexpr int TNW = WN / 32;
+constexpr int kLoads = BM * BK * 2 / (kThreads * 16);  // 16-byte copies per thread per slab
 
 enum Epi { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_F32 = 3 };
 
@@ -60,10 +67,12 @@ struct GemmArgs {
 };
 
 // LDS layouts (offsets in bf16 elements). 16-byte chunks are XOR-swizzled
-// with the low bits of the row so that the fragment reads of a wavefront
-// spread over the LDS banks.
+// with row bits so that the fragment reads of a wavefront spread over the LDS
+// banks: a 256-byte bank window holds two 128-byte K-major rows, so rows r and
+// r + 2 must differ in chunk, i.e. the swizzle uses bits 1..3 of the row.
+__device__ __forceinline__ int kmaj_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int kmaj_off(int r, int chunk) {  // [256 rows][64 k]
-    return r * BK + ((chunk ^ (r & 7)) << 3);
+    return r * BK + ((chunk ^ kmaj_swz(r)) << 3);
 }
 __device__ __forceinline__ int mnmaj_off(int k, int chunk) {  // [64 k][256 mn]
     return k * 256 + ((chunk ^ ((k & 7) << 2)) << 3);
@@ -78,21 +87,22 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
     return x * q + min(x, r) + i;
 }
 
-template <bool KMAJ>
-struct Stage {
-    // Global -> register staging of one 256 x 64 operand slab (8 x 16 B per thread).
-    uint4 v[8];
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
 
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * BK];
+    // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
+    __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
     __shared__ int s_tiles[MOE_MAX_E + 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
     const int ntn = (p.N + BN - 1) / BN;
 
     // ---------------------------------------------------------- tile decode
@@ -124,7 +134,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         const int total = mtiles * ntn;
         if ((int)blockIdx.x >= total) return;
         const int t = xcd_remap(blockIdx.x, total);
-        // bands of 8 M tiles, N-tiles inner: neighbours share B column slabs
+        // bands of 8 M tiles, N tiles inner: neighbours share B column slabs
         constexpr int G = 8;
         const int band = t / (G * ntn);
         const int within = t - band * G * ntn;
@@ -157,58 +167,77 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         k_end = p.offsets[e + 1];
     }
 
-    const uint16_t* Bp = RAGGED_K ? p.B : p.B + (int64_t)e * p.b_estride;
+    // ---------------------------------------------------------- operand sources
+    // Buffer resources bound the readable bytes: rows past the expert's region
+    // (ragged M) or past N read as zero; masked lanes use an offset past the end.
+    const uint16_t* a_base;
+    uint32_t a_bytes, a_step;
+    if constexpr (!RAGGED_K) {
+        a_base = p.A + (int64_t)row0 * p.lda;
+        a_bytes = (uint32_t)((int64_t)(row_end - row0) * p.lda * 2);
+        a_step = BK * 2;
+    } else {
+        a_base = p.A + (int64_t)k_begin * p.lda;
+        a_bytes = (uint32_t)((int64_t)(k_end - k_begin) * p.lda * 2);
+        a_step = (uint32_t)(BK * p.lda * 2);
+    }
+    const uint16_t* b_base;
+    uint32_t b_bytes, b_step;
+    if constexpr (RAGGED_K) {
+        b_base = p.B + (int64_t)k_begin * p.ldb;
+        b_bytes = (uint32_t)((int64_t)(k_end - k_begin) * p.ldb * 2);
+        b_step = (uint32_t)(BK * p.ldb * 2);
+    } else if constexpr (B_KMAJ) {
+        b_base = p.B + (int64_t)e * p.b_estride + (int64_t)n0 * p.ldb;
+        b_bytes = (uint32_t)((int64_t)(p.N - n0) * p.ldb * 2);
+        b_step = BK * 2;
+    } else {
+        b_base = p.B + (int64_t)e * p.b_estride;
+        b_bytes = (uint32_t)((int64_t)p.K * p.ldb * 2);
+        b_step = (uint32_t)(BK * p.ldb * 2);
+    }
+    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a_base, a_bytes);
+    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(b_base, b_bytes);
 
-    // ---------------------------------------------------------- global loads
-    auto load_a = [&](uint4* v, int k0) {
+    // Lane byte offsets of the 8 x 16 B chunks this thread moves per slab.
+    // Instruction i of wavefront w fills LDS block i*4 + w (1 KiB); lane l
+    // writes chunk l of it, so the lane loads whichever global chunk the
+    // swizzled layout puts there.
+    uint32_t a_off[kLoads], b_off[kLoads];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = i * kThreads + tid;
-            if constexpr (A_KMAJ) {
-                const int r = id >> 3, c = id & 7;
-                const int row = row0 + r;
-                v[i] = (row < row_end) ? *(const uint4*)(p.A + (int64_t)row * p.lda + k0 + c * 8)
-                                       : make_uint4(0, 0, 0, 0);
-            } else {
-                const int kr = id >> 5, c = id & 31;
-                const int col = m0 + c * 8;
-                v[i] = (col < p.M) ? *(const uint4*)(p.A + (int64_t)(k0 + kr) * p.lda + col)
-                                   : make_uint4(0, 0, 0, 0);
-            }
+    for (int i = 0; i < kLoads; ++i) {
+        const int q = (i * kWaves + wave) * 64 + lane;
+        if constexpr (A_KMAJ) {
+            const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
+            a_off[i] = (uint32_t)((r * p.lda + c * 8) * 2);
+        } else {
+            const int kr = q >> 5, c = (q & 31) ^ ((kr & 7) << 2);
+            const int col = m0 + c * 8;
+            a_off[i] = col < p.M ? (uint32_t)((kr * p.lda + col) * 2) : kMasked;
         }
-    };
-    auto load_b = [&](uint4* v, int k0) {
+        if constexpr (B_KMAJ) {
+            const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
+            b_off[i] = (uint32_t)((r * p.ldb + c * 8) * 2);
+        } else {
+            const int kr = q >> 5, c = (q & 31) ^ ((kr & 7) << 2);
+            const int col = n0 + c * 8;
+            b_off[i] = col < p.N ? (uint32_t)((kr * p.ldb + col) * 2) : kMasked;
+        }
+    }
+
+    // Enqueue the direct global -> LDS copies of K slab `ks_idx` into buffer `buf`.
+    auto issue = [&](int ks_idx, int buf) {
+        const uint32_t da = (uint32_t)ks_idx * a_step, db = (uint32_t)ks_idx * b_step;
+        LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = i * kThreads + tid;
-            if constexpr (B_KMAJ) {
-                const int r = id >> 3, c = id & 7;
-                const int n = n0 + r;
-                v[i] = (n < p.N) ? *(const uint4*)(Bp + (int64_t)n * p.ldb + k0 + c * 8)
-                                 : make_uint4(0, 0, 0, 0);
-            } else {
-                const int kr = id >> 5, c = id & 31;
-                const int col = n0 + c * 8;
-                v[i] = (col < p.N) ? *(const uint4*)(Bp + (int64_t)(k0 + kr) * p.ldb + col)
-                                   : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_a = [&](const uint4* v, uint16_t* s) {
+        for (int i = 0; i < kLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024),
+                                                     16, a_off[i] + da, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = i * kThreads + tid;
-            const int off = A_KMAJ ? kmaj_off(id >> 3, id & 7) : mnmaj_off(id >> 5, id & 31);
-            *(uint4*)(s + off) = v[i];
-        }
-    };
-    auto store_b = [&](const uint4* v, uint16_t* s) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = i * kThreads + tid;
-            const int off = B_KMAJ ? kmaj_off(id >> 3, id & 7) : mnmaj_off(id >> 5, id & 31);
-            *(uint4*)(s + off) = v[i];
-        }
+        for (int i = 0; i < kLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (LDS_AS void*)(lds + BM * BK * 2 + (i * kWaves + wave) * 1024), 16,
+                b_off[i] + db, 0, 0, 0);
     };
 
     // ---------------------------------------------------------- fragments
@@ -231,48 +260,61 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][TNW];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16_t){};
+        for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
 
     // ---------------------------------------------------------- main loop
+    // Slab kt+1 streams into the other LDS buffer while slab kt is multiplied;
+    // the fragments of K step ks+1 are read while the MFMAs of ks run.
     const int nk = (k_end - k_begin) / BK;
     if (nk > 0) {
-        uint4 ra[8], rb[8];
-        load_a(ra, k_begin);
-        load_b(rb, k_begin);
-        store_a(ra, s_a[0]);
-        store_b(rb, s_b[0]);
+        bf16x8_t fa[2][4], fb[2][TNW];
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        {
+            const uint16_t* sa = s_ab[0];
+            const uint16_t* sb = s_ab[0] + BM * BK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[0][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, 0);
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) fb[0][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, 0);
+        }
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) {
-                load_a(ra, k_begin + (kt + 1) * BK);
-                load_b(rb, k_begin + (kt + 1) * BK);
-            }
-            const uint16_t* sa = s_a[cur];
-            const uint16_t* sb = s_b[cur];
+            if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
+            const uint16_t* sa = s_ab[cur];
+            const uint16_t* sb = s_ab[cur] + BM * BK;
+            static_for<BK / 16>([&](auto KS) {
+                constexpr int ks = KS;
+                constexpr int c = ks & 1;
+                if constexpr (ks + 1 < BK / 16) {
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8_t fa[4], fb[4];
+                    for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fa[i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) fb[j] = frag(sb, B_KMAJ, wn * 128 + 32 * j, ks);
+                    for (int j = 0; j < TNW; ++j) fb[c ^ 1][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks + 1);
+                }
+                __builtin_amdgcn_s_setprio(1);  // the MFMA phase wins issue over the sibling wavefront
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-            }
-            if (more) {
-                store_a(ra, s_a[cur ^ 1]);
-                store_b(rb, s_b[cur ^ 1]);
-            }
+                    for (int j = 0; j < TNW; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
+            });
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            if (kt + 1 < nk) {
+                const uint16_t* na = s_ab[cur ^ 1];
+                const uint16_t* nb = s_ab[cur ^ 1] + BM * BK;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fa[0][i] = frag(na, A_KMAJ, wm * 128 + 32 * i, 0);
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) fb[0][j] = frag(nb, B_KMAJ, wn * WN + 32 * j, 0);
+            }
         }
     }
 
@@ -281,86 +323,83 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // column 8q + 4h + s with h = l >> 5.
     const int h = lane >> 5;
     const int rbase = (RAGGED_K ? m0 : row0) + wm * 128 + (lane & 31);
-    const int cbase = n0 + wn * 128 + 4 * h;
+    const int cbase = n0 + wn * WN + 4 * h;
 
     if constexpr (EPI == EPI_F32) {
         float* out = p.outf + (int64_t)e * p.f_estride;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = rbase + 32 * i;
-            if (m >= p.M) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (n0 + wn * 128 + 32 * j >= p.N) continue;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = cbase + 32 * j + 8 * q;
-                    float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    *(float4*)(out + (int64_t)m * p.ldf + c) = v;
-                }
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            if (m < p.M) {
+                static_for<TNW>([&](auto J) {
+                    if (n0 + wn * WN + 32 * J < p.N) {
+                        static_for<4>([&](auto Q) {
+                            const int c = cbase + 32 * J + 8 * Q;
+                            const float4 v = make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1],
+                                                         acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                            *(float4*)(out + (int64_t)m * p.ldf + c) = v;
+                        });
+                    }
+                });
             }
-        }
+        });
     } else if constexpr (EPI == EPI_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = rbase + 32 * i;
-            if (m >= row_end) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (n0 + wn * 128 + 32 * j >= p.N) continue;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = cbase + 32 * j + 8 * q;
-                    uint2 v;
-                    v.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-                    v.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                    *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) = v;
-                }
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            if (m < row_end) {
+                static_for<TNW>([&](auto J) {
+                    if (n0 + wn * WN + 32 * J < p.N) {
+                        static_for<4>([&](auto Q) {
+                            const int c = cbase + 32 * J + 8 * Q;
+                            uint2 v;
+                            v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                            v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                            *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) = v;
+                        });
+                    }
+                });
             }
-        }
+        });
     } else if constexpr (EPI == EPI_SWIGLU) {
         // columns come in (gate 32, up 32) pairs: tiles j = 2u (gate), 2u+1 (up)
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            if (m < row_end) {
+                static_for<TNW / 2>([&](auto U) {
+                    const int hc = n0 + wn * WN + 64 * U;  // first gate column of the pair
+                    if (hc < p.N) {
+                        const int ac = hc / 2 + 4 * h;      // output column base
+                        static_for<4>([&](auto Q) {
+                            const f32x16_t& G = acc[I][2 * U];
+                            const f32x16_t& Up = acc[I][2 * U + 1];
+                            float av[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = rbase + 32 * i;
-            if (m >= row_end) continue;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int hc = n0 + wn * 128 + 64 * u;  // first gate column of the pair
-                if (hc >= p.N) continue;
-                const int ac = hc / 2 + 4 * h;          // output column base
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float av[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float g = acc[i][2 * u][4 * q + s];
-                        const float up = acc[i][2 * u + 1][4 * q + s];
-                        av[s] = g / (1.f + __expf(-g)) * up;
+                            for (int s = 0; s < 4; ++s) {
+                                const float g = G[4 * Q + s];
+                                av[s] = g / (1.f + __expf(-g)) * Up[4 * Q + s];
+                            }
+                            uint2 v;
+                            v.x = pack_bf16x2(av[0], av[1]);
+                            v.y = pack_bf16x2(av[2], av[3]);
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 8 * Q) = v;
+                            if (p.out0) {
+                                uint2 g2, u2;
+                                g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
+                                g2.y = pack_bf16x2(G[4 * Q + 2], G[4 * Q + 3]);
+                                u2.x = pack_bf16x2(Up[4 * Q], Up[4 * Q + 1]);
+                                u2.y = pack_bf16x2(Up[4 * Q + 2], Up[4 * Q + 3]);
+                                const int64_t rowp = (int64_t)m * p.ld0;
+                                *(uint2*)(p.out0 + rowp + hc + 4 * h + 8 * Q) = g2;
+                                *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * Q) = u2;
+                            }
+                        });
                     }
-                    uint2 v;
-                    v.x = pack_bf16x2(av[0], av[1]);
-                    v.y = pack_bf16x2(av[2], av[3]);
-                    *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 8 * q) = v;
-                    if (p.out0) {
-                        uint2 g2, u2;
-                        g2.x = pack_bf16x2(acc[i][2 * u][4 * q], acc[i][2 * u][4 * q + 1]);
-                        g2.y = pack_bf16x2(acc[i][2 * u][4 * q + 2], acc[i][2 * u][4 * q + 3]);
-                        u2.x = pack_bf16x2(acc[i][2 * u + 1][4 * q], acc[i][2 * u + 1][4 * q + 1]);
-                        u2.y = pack_bf16x2(acc[i][2 * u + 1][4 * q + 2], acc[i][2 * u + 1][4 * q + 3]);
-                        const int64_t rowp = (int64_t)m * p.ld0;
-                        *(uint2*)(p.out0 + rowp + hc + 4 * h + 8 * q) = g2;
-                        *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * q) = u2;
-                    }
-                }
+                });
             }
-        }
+        });
     } else if constexpr (EPI == EPI_DSWIGLU) {
         // acc = dA' over activation columns c; H holds (gate, up) interleaved.
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = rbase + 32 * i;
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
             const bool row_ok = m < row_end;
             float w = 0.f;
             if (row_ok) {
@@ -369,48 +408,47 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             }
             float dsum = 0.f;
             if (row_ok) {
+                const int64_t hrow = (int64_t)m * p.ld_aux;
+                const int64_t drow = (int64_t)m * p.ld0;
+                static_for<TNW>([&](auto J) {
+                    const int ct = n0 + wn * WN + 32 * J;  // first column of the tile
+                    if (ct < p.N) {
+                        const int gcol = 2 * ct;             // gate block of this 32-column tile
+                        static_for<4>([&](auto Q) {
+                            const int cc = 8 * Q + 4 * h;    // column within the tile
+                            float g[4], uu[4];
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
+                            float dg[4], du[4], aw[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int ct = n0 + wn * 128 + 32 * j;  // first column of the tile
-                    if (ct >= p.N) continue;
-                    const int gcol = 2 * ct;                 // gate block of this 32-column tile
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int cc = 8 * q + 4 * h;        // column within the tile
-                        const int64_t hrow = (int64_t)m * p.ld_aux;
-                        float g[4], uu[4];
-                        unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
-                        unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
-                        float dg[4], du[4], aw[4];
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            const float sg = 1.f / (1.f + __expf(-g[s]));
-                            const float sl = g[s] * sg;
-                            const float a = sl * uu[s];
-                            const float dap = acc[i][j][4 * q + s];
-                            dsum = fmaf(dap, a, dsum);
-                            const float da = w * dap;
-                            dg[s] = da * uu[s] * sg * (1.f + g[s] * (1.f - sg));
-                            du[s] = da * sl;
-                            aw[s] = w * a;
-                        }
-                        const int64_t drow = (int64_t)m * p.ld0;
-                        uint2 v;
-                        v.x = pack_bf16x2(dg[0], dg[1]);
-                        v.y = pack_bf16x2(dg[2], dg[3]);
-                        *(uint2*)(p.out0 + drow + gcol + cc) = v;
-                        v.x = pack_bf16x2(du[0], du[1]);
-                        v.y = pack_bf16x2(du[2], du[3]);
-                        *(uint2*)(p.out0 + drow + gcol + 32 + cc) = v;
-                        v.x = pack_bf16x2(aw[0], aw[1]);
-                        v.y = pack_bf16x2(aw[2], aw[3]);
-                        *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = v;
+                            for (int s = 0; s < 4; ++s) {
+                                const float sg = 1.f / (1.f + __expf(-g[s]));
+                                const float sl = g[s] * sg;
+                                const float a = sl * uu[s];
+                                const float dap = acc[I][J][4 * Q + s];
+                                dsum = fmaf(dap, a, dsum);
+                                const float da = w * dap;
+                                dg[s] = da * uu[s] * sg * (1.f + g[s] * (1.f - sg));
+                                du[s] = da * sl;
+                                aw[s] = w * a;
+                            }
+                            uint2 v;
+                            v.x = pack_bf16x2(dg[0], dg[1]);
+                            v.y = pack_bf16x2(dg[2], dg[3]);
+                            *(uint2*)(p.out0 + drow + gcol + cc) = v;
+                            v.x = pack_bf16x2(du[0], du[1]);
+                            v.y = pack_bf16x2(du[2], du[3]);
+                            *(uint2*)(p.out0 + drow + gcol + 32 + cc) = v;
+                            v.x = pack_bf16x2(aw[0], aw[1]);
+                            v.y = pack_bf16x2(aw[2], aw[3]);
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = v;
+                        });
                     }
-                }
+                });
             }
             dsum += __shfl_xor(dsum, 32, 64);  // the partner lane holds the other half
-            if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * 2 + wn] = dsum;
-        }
+            if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
+        });
     }
 }
 
@@ -449,7 +487,7 @@ static GemmArgs zero_args() {
     return a;
 }
 
-int ds_partials_per_row(int n) { return 2 * ((n + BN - 1) / BN); }
+int ds_partials_per_row(int n) { return (BN / WN) * ((n + BN - 1) / BN); }
 
 int launch_fc1_swiglu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
                       int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, hipStream_t s) {

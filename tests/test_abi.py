@@ -55,7 +55,7 @@ def test_status_strings_and_capacity():
     assert M.moe_capacity_rows(10, 3, 2) == -1          # k > E
     assert M.moe_capacity_rows(10, 1, 2000) == -1       # E > MOE_MAX_EXPERTS
     assert M.moe_route_workspace_bytes(0, 1, 1) == 0
-    assert M.moe_mlp_bwd_workspace_bytes(2048, 1024) == 1024 * 16 * 4
+    assert M.moe_mlp_bwd_workspace_bytes(2048, 1024) == 1024 * 32 * 4
 
 
 def _fake(addr=0x1000):
