@@ -160,8 +160,9 @@ int moe_combine(const uint16_t* y, const int32_t* row_of, const float* w,
                 int T, int k, int d, uint16_t* out, moe_stream_t stream);
 
 /* MXFP8 side of the forward (all device pointers). E4M3 codes (OCP, bias 7,
- * saturating to +-448), E8M0 block scales (code = exponent + 127) over 32
- * elements: shared exponent floor(log2 amax) - 8, zero block -> code 0. */
+ * round to nearest-even), E8M0 block scales (code = exponent + 127) over 32
+ * elements: the shared exponent is the smallest e with amax <= 448 * 2^e, so
+ * no element saturates; a zero block takes code 0. */
 typedef struct moe_mx_fwd {
     uint8_t* a_q;          /* [M_cap, n]    row-wise codes of A (out)            */
     uint8_t* a_s;          /* [M_cap, n/32] row-wise scales of A (out)           */

@@ -30,8 +30,10 @@ Readings where the pages are silent (each listed in the design notes):
     dH, A', dX_perm, dX) are rounded to the nearest bf16 (ties to even);
     every other value is fp64;
   * A' = w * A (routing-weighted activation) and dW in fp64/fp32;
-  * MXFP8 per OCP MX v1.0: shared exponent floor(log2 amax) - 8, E4M3 codes
-    rounded to nearest-even and saturated to +-448, zero block -> scale 0.
+  * MXFP8 blocks of 32 elements (OCP MX v1.0 element and scale formats) with
+    the shared exponent rounded up so that no element saturates: the smallest
+    e with amax <= 448 * 2^e (the Transformer Engine MXFP8 recipe rounds the
+    scale up); E4M3 codes rounded to nearest-even, zero block -> scale 0.
 
 Parity pins live in tests/test_oracle_*.py.
 """
@@ -364,11 +366,16 @@ def e4m3_decode(code) -> np.ndarray:
 
 
 def mx_block_exponent(amax) -> np.ndarray:
-    """Shared exponent of a block: floor(log2 amax) - 8 clamped to [-127, 127];
-    a zero block takes -127 (scale code 0)."""
+    """Shared exponent of a block: the smallest integer e with amax <= 448 * 2^e
+    (so no element of the block saturates), clamped to [-127, 127]; a zero
+    block takes -127 (scale code 0).
+
+    Equivalently floor(log2 amax) - 8, plus one when amax's significand
+    exceeds 1.75 (448 = 1.75 * 2^8)."""
     amax = np.asarray(amax, dtype=np.float64)
-    _, q = np.frexp(amax)
-    e = np.clip(q - 1 - 8, -127, 127)
+    m, q = np.frexp(amax)                  # amax = m * 2^q, 0.5 <= m < 1
+    e = (q - 1 - 8) + (2.0 * m > 1.75)
+    e = np.clip(e, -127, 127)
     return np.where(amax == 0.0, -127, e).astype(np.int64)
 
 

@@ -102,20 +102,37 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     if (rc) return rc;
     if (!offsets || !a) return MOE_ERR_INVALID_ARG;
     if ((stages & ~(unsigned)MOE_STAGES_FWD) || stages == 0) return MOE_ERR_INVALID_ARG;
-    if (mx) return MOE_ERR_UNSUPPORTED;
+    if (mx) {
+        if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
+        if (!mx->a_q || !mx->a_s || !aligned16(mx->a_q) || !aligned16(mx->a_s)) return MOE_ERR_INVALID_ARG;
+        if ((mx->at_q == nullptr) != (mx->at_s == nullptr)) return MOE_ERR_INVALID_ARG;
+        if (mx->at_q && (!aligned16(mx->at_q) || !aligned16(mx->at_s))) return MOE_ERR_INVALID_ARG;
+        if ((stages & MOE_STAGE_FC2) &&
+            (!mx->w2t_q || !mx->w2t_s || !aligned16(mx->w2t_q) || !aligned16(mx->w2t_s)))
+            return MOE_ERR_INVALID_ARG;
+    }
     if (stages & MOE_STAGE_FC1) {
         if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
         if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
     }
     if (!aligned16(a)) return MOE_ERR_INVALID_ARG;
     if (stages & MOE_STAGE_FC2) {
-        if (!w2 || !y || !aligned16(w2) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+        if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+        if (!mx && (!w2 || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
     }
     hipStream_t s = S(stream);
-    if (stages & MOE_STAGE_FC1)
-        if (moe::launch_fc1_swiglu(x_perm, w1, offsets, E, d, n, M_cap, h, a, s)) return MOE_ERR_LAUNCH;
-    if (stages & MOE_STAGE_FC2)
-        if (moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, s)) return MOE_ERR_LAUNCH;
+    if (stages & MOE_STAGE_FC1) {
+        const int rc1 = mx ? moe::launch_fc1_swiglu_mx(x_perm, w1, offsets, E, d, n, M_cap, h, a, mx->a_q,
+                                                        mx->a_s, mx->at_q, mx->at_s, s)
+                           : moe::launch_fc1_swiglu(x_perm, w1, offsets, E, d, n, M_cap, h, a, s);
+        if (rc1) return MOE_ERR_LAUNCH;
+    }
+    if (stages & MOE_STAGE_FC2) {
+        const int rc2 = mx ? moe::launch_mx_fc2(mx->a_q, mx->a_s, mx->w2t_q, mx->w2t_s, offsets, E, d, n,
+                                                 M_cap, y, s)
+                           : moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, s);
+        if (rc2) return MOE_ERR_LAUNCH;
+    }
     return MOE_OK;
 }
 
@@ -176,9 +193,14 @@ int moe_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, 
     if (mode <= 0 || (mode & ~(MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE))) return MOE_ERR_INVALID_ARG;
     if ((mode & MOE_QUANT_ROWWISE) && (!q_row || !s_row)) return MOE_ERR_INVALID_ARG;
     if ((mode & MOE_QUANT_COLWISE) && (!q_col || !s_col)) return MOE_ERR_INVALID_ARG;
-    if ((mode & MOE_QUANT_ROWWISE) && C % MOE_MX_BLOCK) return MOE_ERR_UNSUPPORTED;
+    if (C % MOE_MX_BLOCK) return MOE_ERR_UNSUPPORTED;
     if ((mode & MOE_QUANT_COLWISE) && R % MOE_MX_BLOCK) return MOE_ERR_UNSUPPORTED;
-    return MOE_ERR_UNSUPPORTED;  // not built yet
+    if (!aligned16(src) || (q_row && !aligned16(q_row)) || (q_col && !aligned16(q_col)))
+        return MOE_ERR_INVALID_ARG;
+    if (R * C * batch >= ((int64_t)1 << 40) || (R + 127) / 128 > 65535 || batch > 65535)
+        return MOE_ERR_UNSUPPORTED;
+    const int rc = moe::launch_quant_mxfp8(src, batch, R, C, mode, q_row, s_row, q_col, s_col, S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
 }  // extern "C"

@@ -27,19 +27,15 @@
 // memory. The MFMA is issued with the B fragment as its first operand, which
 // leaves each lane holding one output row and 4-column runs: the epilogues
 // read/write 8-byte vectors per lane and reduce rows mostly in registers.
-#include "common.hpp"
-#include "launch.hpp"
+#include "gemm_common.hpp"
+#include "mx_common.hpp"
 
 namespace moe {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWaves = 8;                 // 2 x 4 wavefronts, 2 per SIMD
-constexpr int kThreads = kWaves * 64;
-constexpr int WN = 64;                    // columns per wavefront (2 MFMA tiles)
-constexpr int TNW = WN / 32;
+constexpr int BK = 64;                    // K elements per LDS slab
 constexpr int kLoads = BM * BK * 2 / (kThreads * 16);  // 16-byte copies per thread per slab
 
-enum Epi { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_F32 = 3 };
+enum Epi { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_F32 = 3, EPI_SWIGLU_MX = 4 };
 
 struct GemmArgs {
     const uint16_t* A;  // activations (token rows)
@@ -64,34 +60,16 @@ struct GemmArgs {
     const float* topk_w;
     const int32_t* src_of;
     int n_part;  // dS partial columns per row
+    uint8_t* q_row;  // MXFP8 copy of A: codes [M_cap, n], scales [M_cap, n/32]
+    uint8_t* s_row;
+    uint8_t* q_col;  // transposed: codes [n, M_cap], scales [n, M_cap/32] (nullable)
+    uint8_t* s_col;
+    int64_t M_cap;
 };
 
-// LDS layouts (offsets in bf16 elements). 16-byte chunks are XOR-swizzled
-// with row bits so that the fragment reads of a wavefront spread over the LDS
-// banks: a 256-byte bank window holds two 128-byte K-major rows, so rows r and
-// r + 2 must differ in chunk, i.e. the swizzle uses bits 1..3 of the row.
-__device__ __forceinline__ int kmaj_swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int kmaj_off(int r, int chunk) {  // [256 rows][64 k]
-    return r * BK + ((chunk ^ kmaj_swz(r)) << 3);
-}
-__device__ __forceinline__ int mnmaj_off(int k, int chunk) {  // [64 k][256 mn]
-    return k * 256 + ((chunk ^ ((k & 7) << 2)) << 3);
-}
-
-// Workgroup order -> tile order: consecutive workgroups land on different
-// XCDs (round robin over 8); give each XCD a contiguous range of tiles so
-// tiles that share operands share an L2.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-    const int x = b & 7, i = b >> 3;
-    const int q = total >> 3, r = total & 7;
-    return x * q + min(x, r) + i;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
+// Element offsets (bf16) inside the LDS slabs.
+__device__ __forceinline__ int kmaj_off(int r, int chunk) { return kmaj_byte(r, chunk) >> 1; }
+__device__ __forceinline__ int mnmaj_off(int k, int chunk) { return mnmaj_byte(k, chunk) >> 1; }
 
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
@@ -108,48 +86,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // ---------------------------------------------------------- tile decode
     int e, row0, row_end, n0, m0 = 0, k_begin, k_end;
     if constexpr (!RAGGED_K) {
-        // prefix sum of per-expert M tiles (exclusive), E <= 1024
-        for (int i = tid; i < p.E; i += kThreads) {
-            const int rows = p.offsets[i + 1] - p.offsets[i];
-            s_tiles[i + 1] = (rows + BM - 1) / BM;
-        }
-        if (tid == 0) s_tiles[0] = 0;
-        __syncthreads();
-        if (tid < 64) {
-            int carry = 0;
-            for (int base = 0; base < p.E; base += 64) {
-                const int i = base + lane;
-                int v = (i < p.E) ? s_tiles[i + 1] : 0;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int u = __shfl_up(v, o, 64);
-                    if (lane >= o) v += u;
-                }
-                if (i < p.E) s_tiles[i + 1] = v + carry;
-                carry += __shfl(v, 63, 64);
-            }
-        }
-        __syncthreads();
-        const int mtiles = s_tiles[p.E];
-        const int total = mtiles * ntn;
-        if ((int)blockIdx.x >= total) return;
-        const int t = xcd_remap(blockIdx.x, total);
-        // bands of 8 M tiles, N tiles inner: neighbours share B column slabs
-        constexpr int G = 8;
-        const int band = t / (G * ntn);
-        const int within = t - band * G * ntn;
-        const int bm = min(G, mtiles - band * G);
-        const int mt = band * G + within % bm;
-        const int nt = within / bm;
-        int lo = 0, hi = p.E;  // last expert with s_tiles[e] <= mt
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_tiles[mid] <= mt) lo = mid; else hi = mid;
-        }
-        e = lo;
-        row0 = p.offsets[e] + (mt - s_tiles[e]) * BM;
-        row_end = p.offsets[e + 1];
-        n0 = nt * BN;
+        RaggedTile tile;
+        if (!ragged_m_tile(p.offsets, p.E, ntn, s_tiles, tile)) return;
+        e = tile.e;
+        row0 = tile.row0;
+        row_end = tile.row_end;
+        n0 = tile.n0;
         k_begin = 0;
         k_end = p.K;
     } else {
@@ -359,6 +301,75 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             }
         });
+    } else if constexpr (EPI == EPI_SWIGLU_MX) {
+        // SwiGLU as below, then the MXFP8 copies of the bf16-rounded A: row-wise
+        // blocks (32 columns of a row: 16 in this lane, 16 in lane l ^ 32) and
+        // column-wise blocks (32 rows of a column: one per lane of a half-wave).
+        // 32-row blocks never straddle experts (regions are 128-row aligned).
+        const int n = p.N / 2;
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            const int mb = row0 + wm * 128 + 32 * I;  // first row of this 32-row block
+            if (mb < row_end) {
+                static_for<TNW / 2>([&](auto U) {
+                    const int hc = n0 + wn * WN + 64 * U;
+                    if (hc < p.N) {
+                        const int ac = hc / 2;  // first A column of the 32-column block
+                        const f32x16_t& G = acc[I][2 * U];
+                        const f32x16_t& Up = acc[I][2 * U + 1];
+                        uint32_t ab[16];
+                        uint32_t amax = 0;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float g = G[r];
+                            ab[r] = f32_to_bf16(g / (1.f + __expf(-g)) * Up[r]);
+                            amax = max(amax, ab[r] & 0x7fffu);
+                        }
+                        static_for<4>([&](auto Q) {
+                            uint2 v;
+                            v.x = ab[4 * Q] | (ab[4 * Q + 1] << 16);
+                            v.y = ab[4 * Q + 2] | (ab[4 * Q + 3] << 16);
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) = v;
+                            if (p.out0) {
+                                uint2 g2, u2;
+                                g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
+                                g2.y = pack_bf16x2(G[4 * Q + 2], G[4 * Q + 3]);
+                                u2.x = pack_bf16x2(Up[4 * Q], Up[4 * Q + 1]);
+                                u2.y = pack_bf16x2(Up[4 * Q + 2], Up[4 * Q + 3]);
+                                const int64_t rowp = (int64_t)m * p.ld0;
+                                *(uint2*)(p.out0 + rowp + hc + 4 * h + 8 * Q) = g2;
+                                *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * Q) = u2;
+                            }
+                        });
+                        // row-wise block
+                        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+                        const int er = mx_block_exp(amax);
+                        const float invr = mx_inv_scale(er);
+                        static_for<4>([&](auto Q) {
+                            const uint32_t w = e4m3_rne(bf16_to_f32(ab[4 * Q]) * invr) |
+                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 1]) * invr) << 8) |
+                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 2]) * invr) << 16) |
+                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 3]) * invr) << 24);
+                            *(uint32_t*)(p.q_row + (int64_t)m * n + ac + 4 * h + 8 * Q) = w;
+                        });
+                        if (h == 0) p.s_row[(int64_t)m * (n / 32) + ac / 32] = (uint8_t)(er + 127);
+                        // column-wise blocks, stored transposed
+                        if (p.q_col) {
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                uint32_t cm = ab[r] & 0x7fffu;
+#pragma unroll
+                                for (int o = 1; o < 32; o <<= 1) cm = max(cm, (uint32_t)__shfl_xor((int)cm, o, 64));
+                                const int ec = mx_block_exp(cm);
+                                const int c = ac + 8 * (r >> 2) + 4 * h + (r & 3);
+                                p.q_col[(int64_t)c * p.M_cap + m] = (uint8_t)e4m3_rne(bf16_to_f32(ab[r]) * mx_inv_scale(ec));
+                                if ((lane & 31) == 0) p.s_col[(int64_t)c * (p.M_cap / 32) + mb / 32] = (uint8_t)(ec + 127);
+                            }
+                        }
+                    }
+                });
+            }
+        });
     } else if constexpr (EPI == EPI_SWIGLU) {
         // columns come in (gate 32, up 32) pairs: tiles j = 2u (gate), 2u+1 (up)
         static_for<4>([&](auto I) {
@@ -466,14 +477,6 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-static int ragged_m_grid(int64_t M_cap, int E, int N) {
-    // upper bound on M tiles: every expert region is 128-row aligned, so
-    // sum_e ceil(rows_e / 256) <= M_cap / 256 + E
-    const int64_t mt = M_cap / BM + E + 1;
-    int64_t g = mt * ((N + BN - 1) / BN);
-    return (int)g;
-}
-
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
 static int run(const GemmArgs& a, int grid, hipStream_t s) {
     if (grid <= 0) return 0;
@@ -498,6 +501,19 @@ int launch_fc1_swiglu(const uint16_t* x_perm, const uint16_t* w1, const int32_t*
     g.out0 = h; g.ld0 = 2 * n;
     g.out1 = a; g.ld1 = n;
     return run<false, true, false, EPI_SWIGLU>(g, ragged_m_grid(M_cap, E, 2 * n), s);
+}
+
+int launch_fc1_swiglu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
+                         int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, uint8_t* a_q,
+                         uint8_t* a_s, uint8_t* at_q, uint8_t* at_s, hipStream_t s) {
+    GemmArgs g = zero_args();
+    g.A = x_perm; g.lda = d;
+    g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;
+    g.offsets = offsets; g.E = E; g.N = 2 * n; g.K = d;
+    g.out0 = h; g.ld0 = 2 * n;
+    g.out1 = a; g.ld1 = n;
+    g.q_row = a_q; g.s_row = a_s; g.q_col = at_q; g.s_col = at_s; g.M_cap = M_cap;
+    return run<false, true, false, EPI_SWIGLU_MX>(g, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,

@@ -1,0 +1,103 @@
+// Pieces shared by the grouped-GEMM kernels (bf16 and MXFP8): the LDS slab
+// layouts, the XCD-aware tile order, buffer resources and the ragged-M tile
+// scheduler that turns device-side expert offsets into a tile.
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int BM = 256, BN = 256;  // workgroup tile (rows x columns)
+constexpr int kWaves = 8;          // 2 x 4 wavefronts, two per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int WN = 64;             // columns per wavefront (two 32-column MFMA tiles)
+constexpr int TNW = WN / 32;
+
+// A K-major slab row holds 128 bytes (8 chunks of 16 B). Chunks are XOR-
+// swizzled with row bits 1..3: a 256-byte LDS bank window holds two rows, so
+// rows r and r + 2 must differ in chunk for conflict-free ds_read_b128.
+__device__ __forceinline__ int kmaj_swz(int r) { return (r >> 1) & 7; }
+// byte offset of 16-byte chunk `chunk` of row r in a [rows][128 B] slab
+__device__ __forceinline__ int kmaj_byte(int r, int chunk) { return r * 128 + ((chunk ^ kmaj_swz(r)) << 4); }
+// byte offset of chunk `chunk` of k-row k in an MN-major [64][512 B] slab
+__device__ __forceinline__ int mnmaj_byte(int k, int chunk) { return k * 512 + ((chunk ^ ((k & 7) << 2)) << 4); }
+
+// Workgroup order -> tile order: consecutive workgroups land on different
+// XCDs (round robin over 8); give each XCD a contiguous range of tiles so
+// tiles that share operands share an L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int x = b & 7, i = b >> 3;
+    const int q = total >> 3, r = total & 7;
+    return x * q + min(x, r) + i;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
+
+struct RaggedTile {
+    int e, row0, row_end, n0;
+};
+
+// Ragged-M scheduling: expert e owns rows [offsets[e], offsets[e+1]) split
+// into ceil(rows / BM) M tiles; the N dimension has ntn tiles. Every
+// workgroup derives the prefix of M tiles from the device offsets (no host
+// copy) and picks its tile; workgroups past the real tile count return false.
+// s_tiles: LDS scratch of E + 1 ints. Must be called by the whole workgroup.
+__device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int ntn, int* s_tiles,
+                                              RaggedTile& t) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < E; i += blockDim.x) {
+        const int rows = offsets[i + 1] - offsets[i];
+        s_tiles[i + 1] = (rows + BM - 1) / BM;
+    }
+    if (tid == 0) s_tiles[0] = 0;
+    __syncthreads();
+    if (tid < 64) {
+        int carry = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int i = base + lane;
+            int v = (i < E) ? s_tiles[i + 1] : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(v, o, 64);
+                if (lane >= o) v += u;
+            }
+            if (i < E) s_tiles[i + 1] = v + carry;
+            carry += __shfl(v, 63, 64);
+        }
+    }
+    __syncthreads();
+    const int mtiles = s_tiles[E];
+    const int total = mtiles * ntn;
+    if ((int)blockIdx.x >= total) return false;
+    const int tt = xcd_remap(blockIdx.x, total);
+    // bands of 8 M tiles, N tiles inner: neighbours share B column slabs
+    constexpr int G = 8;
+    const int band = tt / (G * ntn);
+    const int within = tt - band * G * ntn;
+    const int bm = min(G, mtiles - band * G);
+    const int mt = band * G + within % bm;
+    const int nt = within / bm;
+    int lo = 0, hi = E;  // last expert with s_tiles[e] <= mt
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tiles[mid] <= mt) lo = mid; else hi = mid;
+    }
+    t.e = lo;
+    t.row0 = offsets[lo] + (mt - s_tiles[lo]) * BM;
+    t.row_end = offsets[lo + 1];
+    t.n0 = nt * BN;
+    return true;
+}
+
+// Upper bound on ragged-M workgroups: every expert region is 128-row aligned,
+// so sum_e ceil(rows_e / BM) <= M_cap / BM + E.
+inline int ragged_m_grid(int64_t M_cap, int E, int N) {
+    return (int)((M_cap / BM + E + 1) * ((N + BN - 1) / BN));
+}
+
+}  // namespace moe

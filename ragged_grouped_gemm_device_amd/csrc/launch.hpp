@@ -26,6 +26,12 @@ int launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, int
 // Grouped GEMMs. All take the device offsets [E+1] of the ragged layout.
 int launch_fc1_swiglu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
                       int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, hipStream_t s);
+int launch_fc1_swiglu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
+                         int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, uint8_t* a_q,
+                         uint8_t* a_s, uint8_t* at_q, uint8_t* at_s, hipStream_t s);
+int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
+                  const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
+                  hipStream_t s);
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
                int64_t M_cap, uint16_t* y, hipStream_t s);
 int launch_dgrad2_dswiglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,

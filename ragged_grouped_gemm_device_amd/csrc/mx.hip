@@ -1,0 +1,284 @@
+// MXFP8 kernels: standalone block quantization and the MX-scaled grouped FC2.
+//
+// [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, three-components
+// section: group-aware MXFP8 quantization and MXFP8 grouped GEMM; NVIDIA CuTe
+// DSL fusion-kernel page, problem section: the BF16 -> MXFP8 pass writes a
+// low-precision copy and a transposed copy.]
+#include "gemm_common.hpp"
+#include "mx_common.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------ quant
+// One workgroup quantizes a 128 x 128 bf16 tile staged in LDS: row-wise blocks
+// (32 consecutive columns) and/or column-wise blocks (32 consecutive rows,
+// written transposed). Loads and the row-wise stores are 16-byte vectors.
+constexpr int QT = 128;          // tile edge
+constexpr int QP = QT + 8;       // LDS row pitch (elements): shifts rows across banks
+
+template <bool ROW, bool COL>
+__global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t R,
+                                                          int C, uint8_t* __restrict__ q_row,
+                                                          uint8_t* __restrict__ s_row,
+                                                          uint8_t* __restrict__ q_col,
+                                                          uint8_t* __restrict__ s_col) {
+    __shared__ __attribute__((aligned(16))) uint16_t t[QT * QP];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.z;
+    const int c0 = blockIdx.x * QT;
+    const int64_t r0 = (int64_t)blockIdx.y * QT;
+    const int cols = min(QT, C - c0);
+    const int rows = (int)min((int64_t)QT, R - r0);
+    src += b * R * C;
+    // stage: 128 rows x 16 chunks of 8 elements; chunks past the edge read as 0
+    for (int id = tid; id < QT * (QT / 8); id += 256) {
+        const int r = id >> 4, c = (id & 15) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < rows && c < cols) v = *(const uint4*)(src + (r0 + r) * C + c0 + c);
+        *(uint4*)(t + r * QP + c) = v;
+    }
+    __syncthreads();
+    if constexpr (ROW) {
+        uint8_t* qr = q_row + b * R * C;
+        uint8_t* sr = s_row + b * R * (C / 32);
+        for (int id = tid; id < QT * (QT / 32); id += 256) {  // (row, 32-column block)
+            const int r = id >> 2, cb = id & 3;
+            if (r >= rows || cb * 32 >= cols) continue;
+            const uint16_t* p = t + r * QP + cb * 32;
+            uint32_t v[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 w = *(const uint4*)(p + 8 * j);
+                v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
+            }
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                amax = max(amax, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+            const int e = mx_block_exp(amax);
+            const float inv = mx_inv_scale(e);
+            uint32_t packed[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t lo = v[2 * j], hi = v[2 * j + 1];
+                packed[j] = e4m3_rne(bf16_to_f32(lo & 0xffffu) * inv) |
+                            (e4m3_rne(bf16_to_f32(lo >> 16) * inv) << 8) |
+                            (e4m3_rne(bf16_to_f32(hi & 0xffffu) * inv) << 16) |
+                            (e4m3_rne(bf16_to_f32(hi >> 16) * inv) << 24);
+            }
+            uint8_t* dst = qr + (r0 + r) * C + c0 + cb * 32;
+            *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            *(uint4*)(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+            sr[(r0 + r) * (C / 32) + (c0 / 32) + cb] = (uint8_t)(e + 127);
+        }
+    }
+    if constexpr (COL) {
+        uint8_t* qc = q_col + b * R * C;
+        uint8_t* sc = s_col + b * R * (C / 32);
+        const int64_t RB = R / 32;
+        for (int id = tid; id < QT * (QT / 32); id += 256) {  // (column, 32-row block)
+            const int c = id & (QT - 1), rb = id >> 7;
+            if (c >= cols || rb * 32 >= rows) continue;
+            const uint16_t* p = t + rb * 32 * QP + c;
+            uint32_t amax = 0;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = max(amax, (uint32_t)p[j * QP] & 0x7fffu);
+            const int e = mx_block_exp(amax);
+            const float inv = mx_inv_scale(e);
+            uint32_t packed[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                packed[j] = e4m3_rne(bf16_to_f32(p[(4 * j) * QP]) * inv) |
+                            (e4m3_rne(bf16_to_f32(p[(4 * j + 1) * QP]) * inv) << 8) |
+                            (e4m3_rne(bf16_to_f32(p[(4 * j + 2) * QP]) * inv) << 16) |
+                            (e4m3_rne(bf16_to_f32(p[(4 * j + 3) * QP]) * inv) << 24);
+            uint8_t* dst = qc + (int64_t)(c0 + c) * R + r0 + rb * 32;
+            *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+            *(uint4*)(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+            sc[(int64_t)(c0 + c) * RB + r0 / 32 + rb] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
+                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s) {
+    const dim3 grid((C + QT - 1) / QT, (unsigned)((R + QT - 1) / QT), batch);
+    if ((mode & 3) == 3)
+        quant_mxfp8_kernel<true, true><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+    else if (mode & 1)
+        quant_mxfp8_kernel<true, false><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+    else
+        quant_mxfp8_kernel<false, true><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// ------------------------------------------------------------------ MX FC2
+// Y[R_e] = MX(A[R_e]) x MX(W2_e) on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x
+// E4M3, one E8M0 scale per lane and 32-element K block). Same workgroup tile,
+// wavefront grid and ragged-M scheduling as the bf16 grouped GEMM; both
+// operands are K-major fp8 ([rows][K] bytes), streamed global -> LDS in
+// 128-byte K slabs (two MFMA K steps of 64).
+struct MxArgs {
+    const uint8_t* A;    // [M_cap, K] codes
+    const uint8_t* As;   // [M_cap, K/32] scales
+    const uint8_t* B;    // [E, N, K] codes (W2_e^T)
+    const uint8_t* Bs;   // [E, N, K/32] scales
+    const int32_t* offsets;
+    int E, N, K;
+    uint16_t* out;       // [M_cap, N] bf16
+};
+
+constexpr int MBK = 128;  // K bytes per LDS slab
+constexpr int kMxLoads = BM * MBK / (kThreads * 16);
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][(BM + BN) * MBK];
+    __shared__ int s_tiles[MOE_MAX_E + 1];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int ntn = (p.N + BN - 1) / BN;
+    RaggedTile tile;
+    if (!ragged_m_tile(p.offsets, p.E, ntn, s_tiles, tile)) return;
+    const int e = tile.e, row0 = tile.row0, row_end = tile.row_end, n0 = tile.n0;
+    const int KB = p.K / 32;  // scale blocks per row
+
+    const __amdgpu_buffer_rsrc_t rsrc_a =
+        make_rsrc(p.A + (int64_t)row0 * p.K, (uint32_t)((int64_t)(row_end - row0) * p.K));
+    const __amdgpu_buffer_rsrc_t rsrc_b =
+        make_rsrc(p.B + ((int64_t)e * p.N + n0) * p.K, (uint32_t)((int64_t)(p.N - n0) * p.K));
+    const __amdgpu_buffer_rsrc_t rsrc_as =
+        make_rsrc(p.As + (int64_t)row0 * KB, (uint32_t)((int64_t)(row_end - row0) * KB));
+    const __amdgpu_buffer_rsrc_t rsrc_bs =
+        make_rsrc(p.Bs + ((int64_t)e * p.N + n0) * KB, (uint32_t)((int64_t)(p.N - n0) * KB));
+
+    uint32_t off[kMxLoads];
+#pragma unroll
+    for (int i = 0; i < kMxLoads; ++i) {
+        const int q = (i * kWaves + wave) * 64 + lane;
+        const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
+        off[i] = (uint32_t)(r * p.K + c * 16);
+    }
+    auto issue = [&](int kt, int buf) {
+        LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
+        const uint32_t dk = (uint32_t)kt * MBK;
+#pragma unroll
+        for (int i = 0; i < kMxLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024),
+                                                     16, off[i] + dk, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kMxLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc_b, (LDS_AS void*)(lds + BM * MBK + (i * kWaves + wave) * 1024), 16, off[i] + dk,
+                0, 0, 0);
+    };
+    // per-lane scale words: 4 consecutive K blocks (one slab) of this lane's rows/columns,
+    // shifted by this half-wave's block so that K step ks uses byte 2*ks
+    const int h = lane >> 5;
+    auto load_scales = [&](int kt, uint32_t* sa, uint32_t* sb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wm * 128 + 32 * i + (lane & 31);
+            sa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc_as, (uint32_t)(r * KB + kt * 4), 0, 0) >> (8 * h);
+        }
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) {
+            const int c = wn * WN + 32 * j + (lane & 31);
+            sb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc_bs, (uint32_t)(c * KB + kt * 4), 0, 0) >> (8 * h);
+        }
+    };
+    // Operand fragment of row `base + (lane & 31)` for K step ks (64 bytes = K
+    // blocks 2ks and 2ks+1): the instruction reads a lane's first 16 bytes as
+    // part of the step's first 32-element block and its last 16 bytes as part
+    // of the second, lane halves h = 0, 1 supplying 16-byte chunks h and 2 + h
+    // (measured); the scale of block b comes from lane half b.
+    auto frag = [&](const uint8_t* s, int base, int ks) -> i32x8_t {
+        const int r = base + (lane & 31);
+        const i32x4_t lo = *(const i32x4_t*)(s + kmaj_byte(r, 4 * ks + h));
+        const i32x4_t hi = *(const i32x4_t*)(s + kmaj_byte(r, 4 * ks + 2 + h));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x16_t acc[4][TNW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
+
+    const int nk = p.K / MBK;
+    uint32_t sa[4], sb[TNW], na[4], nb[TNW];
+    issue(0, 0);
+    load_scales(0, sa, sb);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) {
+            issue(kt + 1, cur ^ 1);
+            load_scales(kt + 1, na, nb);
+        }
+        const uint8_t* sA = s_ab[cur];
+        const uint8_t* sB = s_ab[cur] + BM * MBK;
+        static_for<MBK / 64>([&](auto KS) {
+            constexpr int ks = KS;
+            i32x8_t fa[4], fb[TNW];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[i] = frag(sA, wm * 128 + 32 * i, ks);
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks);
+            __builtin_amdgcn_s_setprio(1);
+            static_for<4>([&](auto I) {
+                static_for<TNW>([&](auto J) {
+                    // the instruction reads byte 0 of each scale register, so the
+                    // block of this K step is shifted there (OPSEL stays 0)
+                    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
+                        (int)(sa[I] >> (16 * ks)));
+                });
+            });
+            __builtin_amdgcn_s_setprio(0);
+        });
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) sb[j] = nb[j];
+        }
+    }
+
+    // epilogue: bf16 Y, lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
+    const int rbase = row0 + wm * 128 + (lane & 31);
+    static_for<4>([&](auto I) {
+        const int m = rbase + 32 * I;
+        if (m < row_end) {
+            static_for<TNW>([&](auto J) {
+                if (n0 + wn * WN + 32 * J < p.N) {
+                    static_for<4>([&](auto Q) {
+                        const int c = n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
+                        uint2 v;
+                        v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                        v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                        *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
+                    });
+                }
+            });
+        }
+    });
+}
+
+int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
+                  const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
+                  hipStream_t s) {
+    MxArgs a;
+    a.A = a_q; a.As = a_s; a.B = w2t_q; a.Bs = w2t_s;
+    a.offsets = offsets; a.E = E; a.N = d; a.K = n;
+    a.out = y;
+    mx_fc2_kernel<<<ragged_m_grid(M_cap, E, d), kThreads, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace moe

@@ -3,8 +3,8 @@
 The E4M3 encoder is checked exhaustively against a nearest-value search over
 the code table decoded from the bit-field definition (OCP 8-bit floating
 point, E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, S.1111.111
-is NaN, no infinities). Block scales follow OCP MX v1.0 (E8M0 shared exponent
-floor(log2 amax) - emax_elem, emax of E4M3 = 8).
+is NaN, no infinities). Block scales are E8M0 powers of two chosen as the
+smallest 2^e with amax <= 448 * 2^e, so no element saturates.
 """
 import numpy as np
 import pytest
@@ -82,9 +82,9 @@ def test_mx_hand_vectors():
     v[0, 0] = 448.0
     q, s, _, _ = O.quant_mxfp8(v, colwise=False)
     assert s[0, 0] == 0x7F and q[0, 0] == 0x7E and np.all(q[0, 1:] == 0)
-    v[0, 0] = 480.0
+    v[0, 0] = 480.0                                       # > 448: next scale, no clipping
     q, s, _, _ = O.quant_mxfp8(v, colwise=False)
-    assert s[0, 0] == 0x7F and q[0, 0] == 0x7E          # saturates
+    assert s[0, 0] == 0x80 and q[0, 0] == 0x77            # 480 / 2 = 240 = 1.875 * 2^7
     v = np.zeros((1, 32))
     v[0, 0], v[0, 1] = 1.0, 2.0 ** -17
     q, s, _, _ = O.quant_mxfp8(v, colwise=False)
@@ -109,12 +109,14 @@ def test_mx_quant_error_bound_and_transposed_layout():
         blk_e = np.repeat(e, 32, axis=1)
         bound = np.maximum(2.0 ** -4 * np.abs(ref), np.ldexp(1.0, blk_e - 10))
         scaled = np.abs(ref) * np.ldexp(1.0, -blk_e)
-        sat = scaled > 448.0
-        # OCP scale rule: the block maximum scales into [256, 512); magnitudes
-        # above 448 clip to the largest finite code (error < 64 * 2^e)
-        assert np.all(scaled < 512)
-        assert np.all(np.abs(deq[sat]) == np.ldexp(448.0, blk_e[sat]))
-        assert np.all(np.abs(deq - ref)[~sat] <= bound[~sat])
+        # the block maximum scales into (224, 448]: nothing saturates
+        assert np.all(scaled <= 448.0)
+        amax = np.abs(ref).reshape(ref.shape[0], -1, 32).max(2)
+        nz = amax > 0
+        assert np.all(amax[nz] * np.ldexp(1.0, -e[nz]) > 224.0)
+        assert np.all(np.abs(deq - ref) <= bound)
+    # and the relative error is within the MXFP8 tolerance everywhere
+    assert O.max_abs_normalised_error(O.mx_dequant(q_r, s_r), v) <= 2.0 ** -4
     # colwise = rowwise of the transpose
     q_t, s_t, _, _ = O.quant_mxfp8(v.T.copy(), colwise=False)
     assert np.array_equal(q_t, q_c) and np.array_equal(s_t, s_c)
@@ -123,6 +125,19 @@ def test_mx_quant_error_bound_and_transposed_layout():
 def dataclass_replace(w, **kw):
     import dataclasses
     return dataclasses.replace(w, **kw)
+
+
+def test_block_exponent_is_minimal_and_sufficient():
+    """Brute force over every positive finite bf16 amax: the chosen e is the
+    smallest integer in [-127, 127] with amax <= 448 * 2^e."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = (bits << np.uint32(16)).view(np.float32).astype(np.float64)
+    e = O.mx_block_exponent(amax)
+    fits = amax <= 448.0 * np.ldexp(1.0, e)
+    tighter = amax <= 448.0 * np.ldexp(1.0, e - 1)
+    assert np.all(fits | (e == 127))
+    assert np.all(~tighter | (e == -127))
+    assert O.mx_block_exponent(0.0) == -127
 
 
 def test_mx_gemm_integer_exact():
