@@ -28,7 +28,36 @@ sys.path.insert(0, ROOT)
 
 METRIC = "grouped-MLP TFLOP/s fwd & bwd (% of MFMA peak); permute/quant GB/s (% HBM)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_MXFP8_TFLOPS = 5000.0    # MI355X dense MXFP8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# HBM traffic of the FC1 kernel measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# (calibrated on a plain device copy); valid only for the kernel sources it names
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fc1_swiglu_balanced_traffic.txt")
+KERNEL_SOURCES = ["gemm.hip", "gemm_common.hpp", "common.hpp", "mx_common.hpp", "launch.hpp"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ragged_grouped_gemm_device_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Bytes per FC1 launch from the committed counter summary, or None when the
+    kernel sources changed since it was taken (or it does not exist)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def _t16(a, torch):
@@ -76,6 +105,8 @@ def main():
     ap.add_argument("--workload", default="balanced")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time every stage alone (stderr)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -90,6 +121,14 @@ def main():
 
     M.load()
     wl = W.WORKLOADS[args.workload]
+    mx_mode = args.workload == "mxfp8"
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_gen = time.perf_counter()
     inp = W.make_inputs(wl)
     print(f"[bench] inputs for {wl.name} generated in {time.perf_counter() - t_gen:.1f} s",
@@ -97,8 +136,14 @@ def main():
     torch.cuda.set_device(0)
     x, w1, w2, dout = (_t16(inp[key], torch) for key in ("x", "w1", "w2", "dout"))
     logits = torch.from_numpy(inp["logits"]).cuda()
-    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n)
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=mx_mode)
     stream = torch.cuda.current_stream()
+    mx = None
+    if mx_mode:
+        # W2 quantized once (weights), outside the timed step
+        M.moe_quant_mxfp8(w2, M.MOE_QUANT_COLWISE, None, None, buf.w2t_q, buf.w2t_s)
+        mx = dict(a_q=buf.a_q, a_s=buf.a_s, at_q=buf.at_q, at_s=buf.at_s, w2t_q=buf.w2t_q,
+                  w2t_s=buf.w2t_s)
 
     ev = []  # (start, end) of the FC1 launch in each timed step
 
@@ -109,11 +154,13 @@ def main():
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1,
+                              mx=mx)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
-        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
+                              mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
         M.backward(buf, dout, w1, w2)
 
@@ -144,7 +191,7 @@ def main():
           f"FC1+SwiGLU {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     if args.detail:
-        _detail(M, torch, wl, buf, x, w1, w2, dout, stream)
+        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -161,12 +208,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+mxfp8-fc2" if mx_mode else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
-                        f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+SwiGLU->FC2->combine"
-                        f" + full backward with dSwiGLU, dS and ragged wgrads",
+                        f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+SwiGLU"
+                        + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
+                        + "->combine + full backward with dSwiGLU, dS and ragged wgrads (bf16)",
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
@@ -177,14 +225,15 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fc1_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
+            "traffic_unit": "bytes per launch",
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, reps=10):
+def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
     """Time each stage alone (stderr only)."""
     def timeit(fn):
         fn()
@@ -210,16 +259,33 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, reps=10):
         ("combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out), None,
          2.0 * Mr * d + 2.0 * wl.T * d + 8.0 * Mr),
     ]
+    if mx is not None:
+        qr = torch.empty(end, n, dtype=torch.uint8, device="cuda")
+        sr = torch.empty(end, n // 32, dtype=torch.uint8, device="cuda")
+        qc = torch.empty(n, end, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(n, end // 32, dtype=torch.uint8, device="cuda")
+        rows += [
+            ("FC1+SwiGLU+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
+                                                             buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx),
+             4.0 * Mr * d * n, None),
+            ("FC2 MXFP8", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a,
+                                                        buf.y, M.MOE_STAGE_FC2, mx=mx),
+             2.0 * Mr * d * n, None, PEAK_MXFP8_TFLOPS),
+            ("quant A row+col", lambda: M.moe_quant_mxfp8(buf.a[:end], 3, qr, sr, qc, sc), None,
+             2.0 * end * n + 2.0 * (end * n + end * n // 32)),
+        ]
     for st, fl in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n), (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n),
                    (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n), (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n)):
         rows.append((f"bwd stage 0x{st:02x}", (lambda s=st: M.moe_grouped_mlp_bwd(
             buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
             buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s)), fl, None))
-    for name, fn, fl, by in rows:
+    for row in rows:
+        name, fn, fl, by = row[:4]
+        peak = row[4] if len(row) > 4 else PEAK_BF16_TFLOPS
         ms = timeit(fn)
         msg = f"[detail] {name:16s} {ms * 1e3:9.1f} us"
         if fl:
-            msg += f"  {fl / ms / 1e9:8.1f} TFLOP/s ({100 * fl / ms / 1e9 / PEAK_BF16_TFLOPS:.1f}% bf16 peak)"
+            msg += f"  {fl / ms / 1e9:8.1f} TFLOP/s ({100 * fl / ms / 1e9 / peak:.1f}% of {peak:.0f})"
         if by:
             msg += f"  {by / ms / 1e6:8.1f} GB/s ({100 * by / ms / 1e6 / PEAK_HBM_GBS:.1f}% HBM)"
         print(msg, file=sys.stderr, flush=True)
