@@ -27,6 +27,14 @@
 // memory. The MFMA is issued with the B fragment as its first operand, which
 // leaves each lane holding one output row and 4-column runs: the epilogues
 // read/write 8-byte vectors per lane and reduce rows mostly in registers.
+//
+// The kernel is persistent: one workgroup per compute unit walks a static
+// tile order, and the first K slab of its next tile is fetched during the
+// last slab of the current one, so that load runs under the final MFMAs and
+// the epilogue stores. Ragged-K tiles are ordered by their expert's row count,
+// longest first, so the short tiles fill the tail of the schedule.
+#include <algorithm>
+
 #include "gemm_common.hpp"
 #include "mx_common.hpp"
 
@@ -71,115 +79,175 @@ struct GemmArgs {
 __device__ __forceinline__ int kmaj_off(int r, int chunk) { return kmaj_byte(r, chunk) >> 1; }
 __device__ __forceinline__ int mnmaj_off(int k, int chunk) { return mnmaj_byte(k, chunk) >> 1; }
 
+// Where one operand slab comes from: base and readable size (the buffer
+// resource is rebuilt from them at each issue, a few scalar ops), the byte
+// step per K slab and per copy index, and this lane's offset for copy 0.
+struct SlabSrc {
+    const uint16_t* a_base;
+    const uint16_t* b_base;
+    uint32_t a_bytes, b_bytes;
+    uint32_t a_step, b_step;
+    uint32_t a_istep, b_istep;
+    uint32_t a_off, b_off;
+};
+
+// Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
+// into the LDS stage at `lds`. Copy i of wavefront w fills LDS block i * 8 + w
+// (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the
+// buffer end: the API bounds keep every operand region under 2^31 bytes, so
+// the sums cannot wrap.
+__device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave) {
+    const uint32_t da = (uint32_t)ks * sr.a_step, db = (uint32_t)ks * sr.b_step;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(sr.a_base, sr.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(sr.b_base, sr.b_bytes);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024), 16,
+                                                 sr.a_off + (da + i * sr.a_istep), 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(lds + BM * BK * 2 + (i * kWaves + wave) * 1024),
+                                                 16, sr.b_off + (db + i * sr.b_istep), 0, 0, 0);
+}
+
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
     __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
-    __shared__ int s_tiles[MOE_MAX_E + 1];
+    __shared__ int s_tiles[MOE_MAX_E + 1];  // ragged M: tile prefix; ragged K: experts by work
+    __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int ntn = (p.N + BN - 1) / BN;
+    const int ntm = RAGGED_K ? (p.M + BM - 1) / BM : 0;
 
-    // ---------------------------------------------------------- tile decode
-    int e, row0, row_end, n0, m0 = 0, k_begin, k_end;
+    // ---------------------------------------------------------- schedule
+    // Persistent workgroups walk a logical tile order. Ragged M: bands of 8 M
+    // tiles with N tiles inner, and each XCD (workgroups are dealt to the 8
+    // XCDs round robin) takes a contiguous run of 1/8 of every round. Ragged
+    // K: experts by descending row count (longest tiles first), so the tail
+    // of the schedule holds the short tiles.
+    int total;
     if constexpr (!RAGGED_K) {
-        RaggedTile tile;
-        if (!ragged_m_tile(p.offsets, p.E, ntn, s_tiles, tile)) return;
-        e = tile.e;
-        row0 = tile.row0;
-        row_end = tile.row_end;
-        n0 = tile.n0;
-        k_begin = 0;
-        k_end = p.K;
+        total = ragged_m_prefix(p.offsets, p.E, s_tiles) * ntn;
     } else {
-        const int ntm = (p.M + BM - 1) / BM;
-        const int total = gridDim.x;
-        const int t = xcd_remap(blockIdx.x, total);
-        e = t / (ntm * ntn);
-        const int r = t - e * ntm * ntn;
-        const int mt = r / ntn, nt = r - (r / ntn) * ntn;
-        m0 = mt * BM;
-        n0 = nt * BN;
-        row0 = 0;
-        row_end = 0;
-        k_begin = p.offsets[e];
-        k_end = p.offsets[e + 1];
+        for (int i = tid; i < p.E; i += kThreads) s_rows[i] = p.offsets[i + 1] - p.offsets[i];
+        __syncthreads();
+        for (int i = tid; i < p.E; i += kThreads) {
+            const int ri = s_rows[i];
+            int rank = 0;
+            for (int j = 0; j < p.E; ++j) {
+                const int rj = s_rows[j];
+                rank += (rj > ri) || (rj == ri && j < i);
+            }
+            s_tiles[rank] = i;
+        }
+        __syncthreads();
+        total = p.E * ntm * ntn;
     }
+    // Round r covers tiles [r nb, (r + 1) nb); within it, XCD x (workgroups
+    // b with b % 8 == x) takes the contiguous run starting at x nb / 8, so the
+    // tiles live on one XCD at a time are neighbours that share operands in
+    // its L2.
+    const int nb = gridDim.x;  // a multiple of 8
+    auto logical = [&](int round) -> int {
+        const int b = blockIdx.x;
+        return round * nb + (b & 7) * (nb >> 3) + (b >> 3);
+    };
+
+    struct Tile {
+        int e, row0, row_end, n0, m0, k_begin, k_end;
+    };
+    auto get_tile = [&](int t) -> Tile {
+        Tile tl;
+        if constexpr (!RAGGED_K) {
+            const RaggedTile r = ragged_m_decode(p.offsets, p.E, ntn, total / ntn, s_tiles, t);
+            tl.e = __builtin_amdgcn_readfirstlane(r.e);
+            tl.row0 = __builtin_amdgcn_readfirstlane(r.row0);
+            tl.row_end = __builtin_amdgcn_readfirstlane(r.row_end);
+            tl.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+            tl.m0 = 0;
+            tl.k_begin = 0;
+            tl.k_end = p.K;
+        } else {
+            const int per = ntm * ntn;
+            const int slot = t / per;
+            const int r = t - slot * per;
+            tl.e = __builtin_amdgcn_readfirstlane(s_tiles[slot]);
+            tl.m0 = (r / ntn) * BM;
+            tl.n0 = (r % ntn) * BN;
+            tl.row0 = tl.row_end = 0;
+            tl.k_begin = __builtin_amdgcn_readfirstlane(p.offsets[tl.e]);
+            tl.k_end = __builtin_amdgcn_readfirstlane(p.offsets[tl.e + 1]);
+        }
+        return tl;
+    };
 
     // ---------------------------------------------------------- operand sources
     // Buffer resources bound the readable bytes: rows past the expert's region
     // (ragged M) or past N read as zero; masked lanes use an offset past the end.
-    const uint16_t* a_base;
-    uint32_t a_bytes, a_step;
-    if constexpr (!RAGGED_K) {
-        a_base = p.A + (int64_t)row0 * p.lda;
-        a_bytes = (uint32_t)((int64_t)(row_end - row0) * p.lda * 2);
-        a_step = BK * 2;
-    } else {
-        a_base = p.A + (int64_t)k_begin * p.lda;
-        a_bytes = (uint32_t)((int64_t)(k_end - k_begin) * p.lda * 2);
-        a_step = (uint32_t)(BK * p.lda * 2);
-    }
-    const uint16_t* b_base;
-    uint32_t b_bytes, b_step;
-    if constexpr (RAGGED_K) {
-        b_base = p.B + (int64_t)k_begin * p.ldb;
-        b_bytes = (uint32_t)((int64_t)(k_end - k_begin) * p.ldb * 2);
-        b_step = (uint32_t)(BK * p.ldb * 2);
-    } else if constexpr (B_KMAJ) {
-        b_base = p.B + (int64_t)e * p.b_estride + (int64_t)n0 * p.ldb;
-        b_bytes = (uint32_t)((int64_t)(p.N - n0) * p.ldb * 2);
-        b_step = BK * 2;
-    } else {
-        b_base = p.B + (int64_t)e * p.b_estride;
-        b_bytes = (uint32_t)((int64_t)p.K * p.ldb * 2);
-        b_step = (uint32_t)(BK * p.ldb * 2);
-    }
-    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a_base, a_bytes);
-    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(b_base, b_bytes);
-
-    // Lane byte offsets of the 8 x 16 B chunks this thread moves per slab.
-    // Instruction i of wavefront w fills LDS block i*4 + w (1 KiB); lane l
-    // writes chunk l of it, so the lane loads whichever global chunk the
-    // swizzled layout puts there.
-    uint32_t a_off[kLoads], b_off[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-        const int q = (i * kWaves + wave) * 64 + lane;
+    // Copy i of wavefront w fills LDS block i * 8 + w (1 KiB) and lane l writes
+    // chunk l of it, so the lane loads whichever global 16-byte chunk the
+    // swizzled layout puts there. The swizzle depends only on wave and lane, so
+    // a lane's source offset for copy i is its offset for copy 0 plus a
+    // uniform stride of i blocks (64 K-major rows or 16 MN-major k rows).
+    auto make_src = [&](const Tile& tl) -> SlabSrc {
+        SlabSrc sr;
+        const uint16_t*& a_base = sr.a_base;
+        uint32_t& a_bytes = sr.a_bytes;
+        if constexpr (!RAGGED_K) {
+            a_base = p.A + (int64_t)tl.row0 * p.lda;
+            a_bytes = (uint32_t)((int64_t)(tl.row_end - tl.row0) * p.lda * 2);
+            sr.a_step = BK * 2;
+        } else {
+            a_base = p.A + (int64_t)tl.k_begin * p.lda;
+            a_bytes = (uint32_t)((int64_t)(tl.k_end - tl.k_begin) * p.lda * 2);
+            sr.a_step = (uint32_t)(BK * p.lda * 2);
+        }
+        const uint16_t*& b_base = sr.b_base;
+        uint32_t& b_bytes = sr.b_bytes;
+        if constexpr (RAGGED_K) {
+            b_base = p.B + (int64_t)tl.k_begin * p.ldb;
+            b_bytes = (uint32_t)((int64_t)(tl.k_end - tl.k_begin) * p.ldb * 2);
+            sr.b_step = (uint32_t)(BK * p.ldb * 2);
+        } else if constexpr (B_KMAJ) {
+            b_base = p.B + (int64_t)tl.e * p.b_estride + (int64_t)tl.n0 * p.ldb;
+            b_bytes = (uint32_t)((int64_t)(p.N - tl.n0) * p.ldb * 2);
+            sr.b_step = BK * 2;
+        } else {
+            b_base = p.B + (int64_t)tl.e * p.b_estride;
+            b_bytes = (uint32_t)((int64_t)p.K * p.ldb * 2);
+            sr.b_step = (uint32_t)(BK * p.ldb * 2);
+        }
+        const int q = wave * 64 + lane;  // copy 0
         if constexpr (A_KMAJ) {
             const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
-            a_off[i] = (uint32_t)((r * p.lda + c * 8) * 2);
+            sr.a_off = (uint32_t)((r * p.lda + c * 8) * 2);
+            sr.a_istep = (uint32_t)(kThreads / 8 * p.lda * 2);
         } else {
             const int kr = q >> 5, c = (q & 31) ^ ((kr & 7) << 2);
-            const int col = m0 + c * 8;
-            a_off[i] = col < p.M ? (uint32_t)((kr * p.lda + col) * 2) : kMasked;
+            const int col = tl.m0 + c * 8;
+            sr.a_off = col < p.M ? (uint32_t)((kr * p.lda + col) * 2) : kMasked;
+            sr.a_istep = (uint32_t)(kThreads / 32 * p.lda * 2);
         }
         if constexpr (B_KMAJ) {
             const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
-            b_off[i] = (uint32_t)((r * p.ldb + c * 8) * 2);
+            sr.b_off = (uint32_t)((r * p.ldb + c * 8) * 2);
+            sr.b_istep = (uint32_t)(kThreads / 8 * p.ldb * 2);
         } else {
             const int kr = q >> 5, c = (q & 31) ^ ((kr & 7) << 2);
-            const int col = n0 + c * 8;
-            b_off[i] = col < p.N ? (uint32_t)((kr * p.ldb + col) * 2) : kMasked;
+            const int col = tl.n0 + c * 8;
+            sr.b_off = col < p.N ? (uint32_t)((kr * p.ldb + col) * 2) : kMasked;
+            sr.b_istep = (uint32_t)(kThreads / 32 * p.ldb * 2);
         }
-    }
+        return sr;
+    };
 
-    // Enqueue the direct global -> LDS copies of K slab `ks_idx` into buffer `buf`.
-    auto issue = [&](int ks_idx, int buf) {
-        const uint32_t da = (uint32_t)ks_idx * a_step, db = (uint32_t)ks_idx * b_step;
-        LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024),
-                                                     16, a_off[i] + da, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kLoads; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_b, (LDS_AS void*)(lds + BM * BK * 2 + (i * kWaves + wave) * 1024), 16,
-                b_off[i] + db, 0, 0, 0);
+    auto issue = [&](const SlabSrc& sr, int ks_idx, int buf) {
+        issue_slab(sr, ks_idx, (LDS_AS char*)(&s_ab[buf][0]), wave);
     };
 
     // ---------------------------------------------------------- fragments
@@ -201,65 +269,87 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
+    bf16x8_t fa[2][4], fb[2][TNW];
+    auto load_frags = [&](int set, int buf, int ks) {
+        const uint16_t* sa = s_ab[buf];
+        const uint16_t* sb = s_ab[buf] + BM * BK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[set][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks);
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) fb[set][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks);
+    };
 
     f32x16_t acc[4][TNW];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
 
-    // ---------------------------------------------------------- main loop
-    // Slab kt+1 streams into the other LDS buffer while slab kt is multiplied;
-    // the fragments of K step ks+1 are read while the MFMAs of ks run.
-    const int nk = (k_end - k_begin) / BK;
-    if (nk > 0) {
-        bf16x8_t fa[2][4], fb[2][TNW];
-        issue(0, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        {
-            const uint16_t* sa = s_ab[0];
-            const uint16_t* sb = s_ab[0] + BM * BK;
+    // ---------------------------------------------------------- tile loop
+    int round = 0;
+    int t = logical(0);
+    if (t >= total) return;
+    Tile tl = get_tile(t);
+    SlabSrc src = make_src(tl);
+    int nk = (tl.k_end - tl.k_begin) / BK;
+    int buf0 = 0;  // LDS buffer holding slab 0 of the current tile
+    if (nk > 0) issue(src, 0, 0);
+    bool have_next = false;
+    for (;;) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[0][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, 0);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < TNW; ++j) fb[0][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, 0);
+            for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
+        // the next tile of this workgroup; its first slab is fetched while the
+        // current tile finishes, so its latency hides behind MFMAs and stores
+        const int tn = logical(round + 1);
+        have_next = tn < total;
+        Tile tl_next = tl;
+        SlabSrc src_next = src;
+        int nk_next = 0;
+        if (have_next) {
+            tl_next = get_tile(tn);
+            src_next = make_src(tl_next);
+            nk_next = (tl_next.k_end - tl_next.k_begin) / BK;
         }
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) issue(kt + 1, cur ^ 1);
-            const uint16_t* sa = s_ab[cur];
-            const uint16_t* sb = s_ab[cur] + BM * BK;
-            static_for<BK / 16>([&](auto KS) {
-                constexpr int ks = KS;
-                constexpr int c = ks & 1;
-                if constexpr (ks + 1 < BK / 16) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
-#pragma unroll
-                    for (int j = 0; j < TNW; ++j) fb[c ^ 1][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks + 1);
-                }
-                __builtin_amdgcn_s_setprio(1);  // the MFMA phase wins issue over the sibling wavefront
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < TNW; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
-                __builtin_amdgcn_s_setprio(0);
-            });
+        int next_buf0 = buf0;
+        if (nk > 0) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (kt + 1 < nk) {
-                const uint16_t* na = s_ab[cur ^ 1];
-                const uint16_t* nb = s_ab[cur ^ 1] + BM * BK;
+            load_frags(0, buf0, 0);
+            for (int kt = 0; kt < nk; ++kt) {
+                const int cur = (buf0 + kt) & 1;
+                const bool last = kt + 1 == nk;
+                if (!last) issue(src, kt + 1, cur ^ 1);
+                else if (nk_next > 0) issue(src_next, 0, cur ^ 1);
+                const uint16_t* sa = s_ab[cur];
+                const uint16_t* sb = s_ab[cur] + BM * BK;
+                static_for<BK / 16>([&](auto KS) {
+                    constexpr int ks = KS;
+                    constexpr int c = ks & 1;
+                    if constexpr (ks + 1 < BK / 16) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fa[0][i] = frag(na, A_KMAJ, wm * 128 + 32 * i, 0);
+                        for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) fb[0][j] = frag(nb, B_KMAJ, wn * WN + 32 * j, 0);
+                        for (int j = 0; j < TNW; ++j) fb[c ^ 1][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks + 1);
+                    }
+                    __builtin_amdgcn_s_setprio(1);  // the MFMA phase wins issue over the sibling wavefront
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < TNW; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_s_setprio(0);
+                });
+                if (!last) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    load_frags(0, cur ^ 1, 0);
+                } else {
+                    next_buf0 = cur ^ 1;
+                }
             }
+        } else if (nk_next > 0) {
+            issue(src_next, 0, buf0);
         }
-    }
-
+        const int e = tl.e, row0 = tl.row0, row_end = tl.row_end, n0 = tl.n0, m0 = tl.m0;
+        (void)m0;
     // ---------------------------------------------------------- epilogue
     // lane holds row (l & 31) of each 32 x 32 tile and, in register 4q + s,
     // column 8q + 4h + s with h = l >> 5.
@@ -461,6 +551,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
         });
     }
+        if (!have_next) break;
+        ++round;
+        tl = tl_next;
+        src = src_next;
+        nk = nk_next;
+        buf0 = next_buf0;
+    }
 }
 
 // dS[t, j] = sum of the partials of row row_of[t*k+j] in ascending order.
@@ -477,10 +574,32 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
+// Persistent grid: one workgroup per compute unit (the LDS footprint allows
+// one), never more than the upper bound on tiles, always a multiple of 8.
+static int persistent_grid(int64_t tile_bound) {
+    const int64_t cus = (device_cus() + 7) & ~7;
+    const int64_t bound = (tile_bound + 7) & ~(int64_t)7;
+    return (int)std::max<int64_t>(8, std::min(cus, bound));
+}
+
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
-static int run(const GemmArgs& a, int grid, hipStream_t s) {
-    if (grid <= 0) return 0;
-    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI><<<grid, kThreads, 0, s>>>(a);
+static int run(const GemmArgs& a, int64_t tile_bound, hipStream_t s) {
+    if (tile_bound <= 0) return 0;
+    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI><<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -567,8 +686,8 @@ int launch_wgrad(const uint16_t* act, int Ma, const uint16_t* grad, int Nb, cons
     g.B = grad; g.ldb = Nb;
     g.offsets = offsets; g.E = E; g.M = Ma; g.N = Nb;
     g.outf = dw; g.ldf = Nb; g.f_estride = (int64_t)Ma * Nb;
-    const int grid = E * ((Ma + BM - 1) / BM) * ((Nb + BN - 1) / BN);
-    return run<true, false, false, EPI_F32>(g, grid, s);
+    const int64_t tiles = (int64_t)E * ((Ma + BM - 1) / BM) * ((Nb + BN - 1) / BN);
+    return run<true, false, false, EPI_F32>(g, tiles, s);
 }
 
 }  // namespace moe

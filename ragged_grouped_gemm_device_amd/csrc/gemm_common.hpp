@@ -43,12 +43,11 @@ struct RaggedTile {
 };
 
 // Ragged-M scheduling: expert e owns rows [offsets[e], offsets[e+1]) split
-// into ceil(rows / BM) M tiles; the N dimension has ntn tiles. Every
-// workgroup derives the prefix of M tiles from the device offsets (no host
-// copy) and picks its tile; workgroups past the real tile count return false.
-// s_tiles: LDS scratch of E + 1 ints. Must be called by the whole workgroup.
-__device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int ntn, int* s_tiles,
-                                              RaggedTile& t) {
+// into ceil(rows / BM) M tiles. Every workgroup derives the prefix of M tiles
+// from the device offsets (no host copy): s_tiles[e] = first M tile of expert
+// e, s_tiles[E] = total. s_tiles: LDS scratch of E + 1 ints. Must be called by
+// the whole workgroup; returns the total number of M tiles.
+__device__ __forceinline__ int ragged_m_prefix(const int32_t* offsets, int E, int* s_tiles) {
     const int tid = threadIdx.x, lane = tid & 63;
     for (int i = tid; i < E; i += blockDim.x) {
         const int rows = offsets[i + 1] - offsets[i];
@@ -71,26 +70,40 @@ __device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int
         }
     }
     __syncthreads();
-    const int mtiles = s_tiles[E];
-    const int total = mtiles * ntn;
-    if ((int)blockIdx.x >= total) return false;
-    const int tt = xcd_remap(blockIdx.x, total);
-    // bands of 8 M tiles, N tiles inner: neighbours share B column slabs
+    return s_tiles[E];
+}
+
+// Tile number tt (of mtiles * ntn) -> tile: bands of 8 M tiles with the N
+// tiles inner, so neighbouring tiles share B column slabs; the expert is the
+// last one whose first M tile is <= the tile's M index.
+__device__ __forceinline__ RaggedTile ragged_m_decode(const int32_t* offsets, int E, int ntn, int mtiles,
+                                                      const int* s_tiles, int tt) {
     constexpr int G = 8;
     const int band = tt / (G * ntn);
     const int within = tt - band * G * ntn;
     const int bm = min(G, mtiles - band * G);
     const int mt = band * G + within % bm;
     const int nt = within / bm;
-    int lo = 0, hi = E;  // last expert with s_tiles[e] <= mt
+    int lo = 0, hi = E;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (s_tiles[mid] <= mt) lo = mid; else hi = mid;
     }
+    RaggedTile t;
     t.e = lo;
     t.row0 = offsets[lo] + (mt - s_tiles[lo]) * BM;
     t.row_end = offsets[lo + 1];
     t.n0 = nt * BN;
+    return t;
+}
+
+// One tile per workgroup: workgroups past the real tile count return false.
+__device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int ntn, int* s_tiles,
+                                              RaggedTile& t) {
+    const int mtiles = ragged_m_prefix(offsets, E, s_tiles);
+    const int total = mtiles * ntn;
+    if ((int)blockIdx.x >= total) return false;
+    t = ragged_m_decode(offsets, E, ntn, mtiles, s_tiles, xcd_remap(blockIdx.x, total));
     return true;
 }
 
