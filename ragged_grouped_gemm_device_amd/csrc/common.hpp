@@ -28,17 +28,21 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): gfx950 converts
+// in hardware (v_cvt_pk_bf16_f32), two values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// Logistic sigmoid 1 / (1 + e^-x) with the hardware exp and reciprocal
+// (about 1 ulp each); saturates to 0 / 1 for large |x|.
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // Unpack 4 bf16 held in a uint2 into floats.
 __device__ __forceinline__ void unpack_bf16x4(uint2 v, float* f) {

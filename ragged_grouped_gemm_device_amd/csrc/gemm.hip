@@ -91,6 +91,32 @@ struct SlabSrc {
     uint32_t a_off, b_off;
 };
 
+// One 16-byte-per-lane direct global -> LDS copy: lane l's 16 bytes land at
+// LDS byte address lds + 16 l. Written as inline assembly on purpose: the
+// compiler cannot tell which LDS bytes the builtin form writes, so it waits
+// for every outstanding copy before the next LDS read, which would serialise
+// the prefetch of slab k + 1 with the multiply of slab k. Here the kernel
+// owns the ordering: it waits on the vector-memory counter and a barrier
+// before any wave reads a slab.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = (int32_t)(uint32_t)a;
+    r.y = (int32_t)((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+    r.z = (int32_t)bytes;                            // reads at or past this offset return 0
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
 // Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
 // into the LDS stage at `lds`. Copy i of wavefront w fills LDS block i * 8 + w
 // (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the
@@ -98,16 +124,14 @@ struct SlabSrc {
 // the sums cannot wrap.
 __device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave) {
     const uint32_t da = (uint32_t)ks * sr.a_step, db = (uint32_t)ks * sr.b_step;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(sr.a_base, sr.a_bytes);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(sr.b_base, sr.b_bytes);
+    const i32x4_t ra = rsrc_words(sr.a_base, sr.a_bytes);
+    const i32x4_t rb = rsrc_words(sr.b_base, sr.b_bytes);
+    const uint32_t l0 = (uint32_t)(uintptr_t)lds + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) lds_copy16(ra, l0 + i * kWaves * 1024, sr.a_off + (da + i * sr.a_istep));
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024), 16,
-                                                 sr.a_off + (da + i * sr.a_istep), 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(lds + BM * BK * 2 + (i * kWaves + wave) * 1024),
-                                                 16, sr.b_off + (db + i * sr.b_istep), 0, 0, 0);
+        lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024, sr.b_off + (db + i * sr.b_istep));
 }
 
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
@@ -412,7 +436,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float g = G[r];
-                            ab[r] = f32_to_bf16(g / (1.f + __expf(-g)) * Up[r]);
+                            ab[r] = f32_to_bf16(g * sigmoid_f(g) * Up[r]);
                             amax = max(amax, ab[r] & 0x7fffu);
                         }
                         static_for<4>([&](auto Q) {
@@ -476,7 +500,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 const float g = G[4 * Q + s];
-                                av[s] = g / (1.f + __expf(-g)) * Up[4 * Q + s];
+                                av[s] = g * sigmoid_f(g) * Up[4 * Q + s];
                             }
                             uint2 v;
                             v.x = pack_bf16x2(av[0], av[1]);
@@ -523,7 +547,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             float dg[4], du[4], aw[4];
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
-                                const float sg = 1.f / (1.f + __expf(-g[s]));
+                                const float sg = sigmoid_f(g[s]);
                                 const float sl = g[s] * sg;
                                 const float a = sl * uu[s];
                                 const float dap = acc[I][J][4 * Q + s];
