@@ -36,6 +36,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// One 16-byte-per-lane direct global -> LDS copy: lane l's 16 bytes land at
+// LDS byte address lds + 16 l. Written as inline assembly on purpose: the
+// compiler cannot tell which LDS bytes the builtin form writes, so it waits
+// for every outstanding copy before the next LDS read, which would serialise
+// the prefetch of slab k + 1 with the multiply of slab k. Here the kernel
+// owns the ordering: it waits on the vector-memory counter and a barrier
+// before any wave reads a slab.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r.x = (int32_t)(uint32_t)a;
+    r.y = (int32_t)((uint32_t)(a >> 32) & 0xffffu);  // stride 0
+    r.z = (int32_t)bytes;                            // reads at or past this offset return 0
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
+    // resource and LDS address are wave-uniform; readfirstlane pins them to
+    // scalar registers when the compiler cannot prove it (free otherwise)
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    r.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    r.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    r.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+
 constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
 
 struct RaggedTile {

@@ -131,24 +131,21 @@ struct MxArgs {
 constexpr int MBK = 128;  // K bytes per LDS slab
 constexpr int kMxLoads = BM * MBK / (kThreads * 16);
 
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
 __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][(BM + BN) * MBK];
     __shared__ int s_tiles[MOE_MAX_E + 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / (kWaves / 2), wn = wave % (kWaves / 2);  // 2 x (kWaves / 2) wavefront grid
     const int ntn = (p.N + BN - 1) / BN;
     RaggedTile tile;
     if (!ragged_m_tile(p.offsets, p.E, ntn, s_tiles, tile)) return;
     const int e = tile.e, row0 = tile.row0, row_end = tile.row_end, n0 = tile.n0;
     const int KB = p.K / 32;  // scale blocks per row
 
-    const __amdgpu_buffer_rsrc_t rsrc_a =
-        make_rsrc(p.A + (int64_t)row0 * p.K, (uint32_t)((int64_t)(row_end - row0) * p.K));
-    const __amdgpu_buffer_rsrc_t rsrc_b =
-        make_rsrc(p.B + ((int64_t)e * p.N + n0) * p.K, (uint32_t)((int64_t)(p.N - n0) * p.K));
+    const i32x4_t rsrc_a = rsrc_words(p.A + (int64_t)row0 * p.K, (uint32_t)((int64_t)(row_end - row0) * p.K));
+    const i32x4_t rsrc_b =
+        rsrc_words(p.B + ((int64_t)e * p.N + n0) * p.K, (uint32_t)((int64_t)(p.N - n0) * p.K));
     const __amdgpu_buffer_rsrc_t rsrc_as =
         make_rsrc(p.As + (int64_t)row0 * KB, (uint32_t)((int64_t)(row_end - row0) * KB));
     const __amdgpu_buffer_rsrc_t rsrc_bs =
@@ -162,17 +159,12 @@ __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
         off[i] = (uint32_t)(r * p.K + c * 16);
     }
     auto issue = [&](int kt, int buf) {
-        LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
+        const uint32_t l0 = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_ab[buf][0]) + wave * 1024;
         const uint32_t dk = (uint32_t)kt * MBK;
 #pragma unroll
-        for (int i = 0; i < kMxLoads; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (LDS_AS void*)(lds + (i * kWaves + wave) * 1024),
-                                                     16, off[i] + dk, 0, 0, 0);
+        for (int i = 0; i < kMxLoads; ++i) lds_copy16(rsrc_a, l0 + i * kWaves * 1024, off[i] + dk);
 #pragma unroll
-        for (int i = 0; i < kMxLoads; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc_b, (LDS_AS void*)(lds + BM * MBK + (i * kWaves + wave) * 1024), 16, off[i] + dk,
-                0, 0, 0);
+        for (int i = 0; i < kMxLoads; ++i) lds_copy16(rsrc_b, l0 + BM * MBK + i * kWaves * 1024, off[i] + dk);
     };
     // per-lane scale words: 4 consecutive K blocks (one slab) of this lane's rows/columns,
     // shifted by this half-wave's block so that K step ks uses byte 2*ks
