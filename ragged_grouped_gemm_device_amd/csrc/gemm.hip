@@ -91,32 +91,6 @@ struct SlabSrc {
     uint32_t a_off, b_off;
 };
 
-// One 16-byte-per-lane direct global -> LDS copy: lane l's 16 bytes land at
-// LDS byte address lds + 16 l. Written as inline assembly on purpose: the
-// compiler cannot tell which LDS bytes the builtin form writes, so it waits
-// for every outstanding copy before the next LDS read, which would serialise
-// the prefetch of slab k + 1 with the multiply of slab k. Here the kernel
-// owns the ordering: it waits on the vector-memory counter and a barrier
-// before any wave reads a slab.
-typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)base;
-    i32x4_t r;
-    r.x = (int32_t)(uint32_t)a;
-    r.y = (int32_t)((uint32_t)(a >> 32) & 0xffffu);  // stride 0
-    r.z = (int32_t)bytes;                            // reads at or past this offset return 0
-    r.w = 0x00020000;
-    return r;
-}
-
-__device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-
 // Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
 // into the LDS stage at `lds`. Copy i of wavefront w fills LDS block i * 8 + w
 // (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the

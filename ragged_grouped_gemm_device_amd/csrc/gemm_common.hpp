@@ -66,7 +66,10 @@ __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t 
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(r)
-                 : "memory", "m0");
+                 : "memory");
+    // M0 is a reserved register the compiler would not preserve for us; these
+    // kernels give it no other use (no compiler-issued LDS DMA, GWS or
+    // message instructions), so the value written here is simply dead after.
 }
 
 constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
