@@ -10,11 +10,37 @@
 namespace moe {
 
 // ------------------------------------------------------------------ quant
-// One workgroup quantizes a 128 x 128 bf16 tile staged in LDS: row-wise blocks
-// (32 consecutive columns) and/or column-wise blocks (32 consecutive rows,
-// written transposed). Loads and the row-wise stores are 16-byte vectors.
-constexpr int QT = 128;          // tile edge
-constexpr int QP = QT + 8;       // LDS row pitch (elements): shifts rows across banks
+// One workgroup quantizes a 128 x 128 bf16 tile straight from registers.
+// Thread (w, l) of the 4 wavefronts holds 8 rows x 8 columns: columns
+// 8 (l & 15) + [0, 8), rows 8 (4 w + (l >> 4)) + [0, 8), loaded as eight
+// 16-byte row pieces (16 lanes cover a 256-byte row segment). A row-wise
+// block (32 columns) spans 4 neighbouring lanes, a column-wise block (32 rows)
+// the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 of one wavefront, so both block maxima
+// are two lane exchanges away, and a column's 8 codes leave as one 8-byte
+// store of the transposed copy. Conversion uses gfx950's packed E4M3
+// instruction, which rounds to nearest-even like the codec above (the scale
+// keeps every value within +-448, so it never saturates).
+constexpr int QT = 128;  // tile edge
+
+// largest magnitude bit pattern (sign cleared) among 8 bf16 values
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
+    const uint32_t m = 0x7fff7fffu;
+    const u16x2_t a = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & m), __builtin_bit_cast(u16x2_t, v.y & m));
+    const u16x2_t c = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.z & m), __builtin_bit_cast(u16x2_t, v.w & m));
+    const u16x2_t d = __builtin_elementwise_max(a, c);
+    return max((uint32_t)d.x, (uint32_t)d.y);
+}
+
+// four fp32 values -> four E4M3 codes, first value in the low byte
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int u = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    u = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, u, true);
+    return (uint32_t)u;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <bool ROW, bool COL>
 __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t R,
@@ -22,80 +48,64 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
                                                           uint8_t* __restrict__ s_row,
                                                           uint8_t* __restrict__ q_col,
                                                           uint8_t* __restrict__ s_col) {
-    __shared__ __attribute__((aligned(16))) uint16_t t[QT * QP];
-    const int tid = threadIdx.x;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cc = l & 15, rg = 4 * w + (l >> 4);
     const int64_t b = blockIdx.z;
-    const int c0 = blockIdx.x * QT;
-    const int64_t r0 = (int64_t)blockIdx.y * QT;
-    const int cols = min(QT, C - c0);
-    const int rows = (int)min((int64_t)QT, R - r0);
+    const int c = blockIdx.x * QT + 8 * cc;              // first column of this thread
+    const int64_t r = (int64_t)blockIdx.y * QT + 8 * rg;  // first row
+    const bool cok = c < C;
     src += b * R * C;
-    // stage: 128 rows x 16 chunks of 8 elements; chunks past the edge read as 0
-    for (int id = tid; id < QT * (QT / 8); id += 256) {
-        const int r = id >> 4, c = (id & 15) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r < rows && c < cols) v = *(const uint4*)(src + (r0 + r) * C + c0 + c);
-        *(uint4*)(t + r * QP + c) = v;
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (cok && r + i < R) v[i] = *(const uint4*)(src + (r + i) * C + c);
     }
-    __syncthreads();
     if constexpr (ROW) {
         uint8_t* qr = q_row + b * R * C;
         uint8_t* sr = s_row + b * R * (C / 32);
-        for (int id = tid; id < QT * (QT / 32); id += 256) {  // (row, 32-column block)
-            const int r = id >> 2, cb = id & 3;
-            if (r >= rows || cb * 32 >= cols) continue;
-            const uint16_t* p = t + r * QP + cb * 32;
-            uint32_t v[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint4 w = *(const uint4*)(p + 8 * j);
-                v[4 * j] = w.x; v[4 * j + 1] = w.y; v[4 * j + 2] = w.z; v[4 * j + 3] = w.w;
-            }
-            uint32_t amax = 0;
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                amax = max(amax, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+        for (int i = 0; i < 8; ++i) {
+            uint32_t amax = abs_max_bf16x8(v[i]);
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
             const int e = mx_block_exp(amax);
             const float inv = mx_inv_scale(e);
-            uint32_t packed[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = v[2 * j], hi = v[2 * j + 1];
-                packed[j] = e4m3_rne(bf16_to_f32(lo & 0xffffu) * inv) |
-                            (e4m3_rne(bf16_to_f32(lo >> 16) * inv) << 8) |
-                            (e4m3_rne(bf16_to_f32(hi & 0xffffu) * inv) << 16) |
-                            (e4m3_rne(bf16_to_f32(hi >> 16) * inv) << 24);
+            const uint4 x = v[i];
+            uint2 q;
+            q.x = e4m3x4(bf16_lo(x.x) * inv, bf16_hi(x.x) * inv, bf16_lo(x.y) * inv, bf16_hi(x.y) * inv);
+            q.y = e4m3x4(bf16_lo(x.z) * inv, bf16_hi(x.z) * inv, bf16_lo(x.w) * inv, bf16_hi(x.w) * inv);
+            if (cok && r + i < R) {
+                *(uint2*)(qr + (r + i) * C + c) = q;
+                if ((cc & 3) == 0) sr[(r + i) * (C / 32) + c / 32] = (uint8_t)(e + 127);
             }
-            uint8_t* dst = qr + (r0 + r) * C + c0 + cb * 32;
-            *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-            *(uint4*)(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-            sr[(r0 + r) * (C / 32) + (c0 / 32) + cb] = (uint8_t)(e + 127);
         }
     }
     if constexpr (COL) {
+        // R is a multiple of 32 here, so a wavefront's 32-row block is whole or absent
+        if (!cok || r >= R) return;
         uint8_t* qc = q_col + b * R * C;
         uint8_t* sc = s_col + b * R * (C / 32);
         const int64_t RB = R / 32;
-        for (int id = tid; id < QT * (QT / 32); id += 256) {  // (column, 32-row block)
-            const int c = id & (QT - 1), rb = id >> 7;
-            if (c >= cols || rb * 32 >= rows) continue;
-            const uint16_t* p = t + rb * 32 * QP + c;
+        // element (row i, column j) of this thread
+        auto elt = [&](int i, int j) -> float {
+            const uint32_t word = j < 2 ? v[i].x : j < 4 ? v[i].y : j < 6 ? v[i].z : v[i].w;
+            return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+        };
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
             uint32_t amax = 0;
 #pragma unroll
-            for (int j = 0; j < 32; ++j) amax = max(amax, (uint32_t)p[j * QP] & 0x7fffu);
+            for (int i = 0; i < 8; ++i) amax = max(amax, (__float_as_uint(elt(i, j)) >> 16) & 0x7fffu);
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
             const int e = mx_block_exp(amax);
             const float inv = mx_inv_scale(e);
-            uint32_t packed[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                packed[j] = e4m3_rne(bf16_to_f32(p[(4 * j) * QP]) * inv) |
-                            (e4m3_rne(bf16_to_f32(p[(4 * j + 1) * QP]) * inv) << 8) |
-                            (e4m3_rne(bf16_to_f32(p[(4 * j + 2) * QP]) * inv) << 16) |
-                            (e4m3_rne(bf16_to_f32(p[(4 * j + 3) * QP]) * inv) << 24);
-            uint8_t* dst = qc + (int64_t)(c0 + c) * R + r0 + rb * 32;
-            *(uint4*)dst = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-            *(uint4*)(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-            sc[(int64_t)(c0 + c) * RB + r0 / 32 + rb] = (uint8_t)(e + 127);
+            uint2 q;
+            q.x = e4m3x4(elt(0, j) * inv, elt(1, j) * inv, elt(2, j) * inv, elt(3, j) * inv);
+            q.y = e4m3x4(elt(4, j) * inv, elt(5, j) * inv, elt(6, j) * inv, elt(7, j) * inv);
+            *(uint2*)(qc + (int64_t)(c + j) * R + r) = q;
+            if ((l >> 4) == 0) sc[(int64_t)(c + j) * RB + r / 32] = (uint8_t)(e + 127);
         }
     }
 }
