@@ -434,10 +434,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         const int er = mx_block_exp(amax);
                         const float invr = mx_inv_scale(er);
                         static_for<4>([&](auto Q) {
-                            const uint32_t w = e4m3_rne(bf16_to_f32(ab[4 * Q]) * invr) |
-                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 1]) * invr) << 8) |
-                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 2]) * invr) << 16) |
-                                               (e4m3_rne(bf16_to_f32(ab[4 * Q + 3]) * invr) << 24);
+                            const uint32_t w = e4m3x4(bf16_to_f32(ab[4 * Q]) * invr, bf16_to_f32(ab[4 * Q + 1]) * invr,
+                                                      bf16_to_f32(ab[4 * Q + 2]) * invr, bf16_to_f32(ab[4 * Q + 3]) * invr);
                             *(uint32_t*)(p.q_row + (int64_t)m * n + ac + 4 * h + 8 * Q) = w;
                         });
                         if (h == 0) p.s_row[(int64_t)m * (n / 32) + ac / 32] = (uint8_t)(er + 127);
@@ -450,7 +448,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                                 for (int o = 1; o < 32; o <<= 1) cm = max(cm, (uint32_t)__shfl_xor((int)cm, o, 64));
                                 const int ec = mx_block_exp(cm);
                                 const int c = ac + 8 * (r >> 2) + 4 * h + (r & 3);
-                                p.q_col[(int64_t)c * p.M_cap + m] = (uint8_t)e4m3_rne(bf16_to_f32(ab[r]) * mx_inv_scale(ec));
+                                p.q_col[(int64_t)c * p.M_cap + m] = (uint8_t)e4m3_hw(bf16_to_f32(ab[r]) * mx_inv_scale(ec));
                                 if ((lane & 31) == 0) p.s_col[(int64_t)c * (p.M_cap / 32) + mb / 32] = (uint8_t)(ec + 127);
                             }
                         }

@@ -32,16 +32,6 @@ __device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
     return max((uint32_t)d.x, (uint32_t)d.y);
 }
 
-// four fp32 values -> four E4M3 codes, first value in the low byte
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    int u = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    u = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, u, true);
-    return (uint32_t)u;
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 template <bool ROW, bool COL>
 __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t R,
                                                           int C, uint8_t* __restrict__ q_row,

@@ -57,4 +57,24 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
     return sign | q;  // q == 8 is the smallest normal, code 0x08
 }
 
+// The kernels encode with gfx950's packed conversion instruction instead:
+// it rounds to nearest-even and gives e4m3_rne's code for every finite
+// |y| <= 448, which the block scale guarantees (checked exhaustively over
+// bf16 inputs); e4m3_rne stays as the written-out definition.
+
+// four fp32 values -> four E4M3 codes, first value in the low byte
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int u = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    u = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, u, true);
+    return (uint32_t)u;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// one fp32 value -> its E4M3 code
+__device__ __forceinline__ uint32_t e4m3_hw(float y) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xffu;
+}
+
 }  // namespace moe
