@@ -570,28 +570,6 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] <= 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cache[dev] = v;
-    }
-    return cache[dev];
-}
-
-// Persistent grid: one workgroup per compute unit (the LDS footprint allows
-// one), never more than the upper bound on tiles, always a multiple of 8.
-static int persistent_grid(int64_t tile_bound) {
-    const int64_t cus = (device_cus() + 7) & ~7;
-    const int64_t bound = (tile_bound + 7) & ~(int64_t)7;
-    return (int)std::max<int64_t>(8, std::min(cus, bound));
-}
-
 template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
 static int run(const GemmArgs& a, int64_t tile_bound, hipStream_t s) {
     if (tile_bound <= 0) return 0;

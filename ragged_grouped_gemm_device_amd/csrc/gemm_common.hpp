@@ -3,6 +3,8 @@
 // scheduler that turns device-side expert offsets into a tile.
 #pragma once
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -141,6 +143,28 @@ __device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int
     if ((int)blockIdx.x >= total) return false;
     t = ragged_m_decode(offsets, E, ntn, mtiles, s_tiles, xcd_remap(blockIdx.x, total));
     return true;
+}
+
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
+// Persistent grid: one workgroup per compute unit (the LDS footprint allows
+// one), never more than the upper bound on tiles, always a multiple of 8.
+inline int persistent_grid(int64_t tile_bound) {
+    const int64_t cus = (device_cus() + 7) & ~7;
+    const int64_t bound = (tile_bound + 7) & ~(int64_t)7;
+    return (int)std::max<int64_t>(8, std::min(cus, bound));
 }
 
 // Upper bound on ragged-M workgroups: every expert region is 128-row aligned,

@@ -131,54 +131,78 @@ struct MxArgs {
 constexpr int MBK = 128;  // K bytes per LDS slab
 constexpr int kMxLoads = BM * MBK / (kThreads * 16);
 
+// Persistent like the bf16 grouped GEMM: one workgroup per compute unit walks
+// the XCD-aware tile order and fetches the next tile's first slab (codes and
+// scales) during the current tile's last one.
 __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][(BM + BN) * MBK];
     __shared__ int s_tiles[MOE_MAX_E + 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / (kWaves / 2), wn = wave % (kWaves / 2);  // 2 x (kWaves / 2) wavefront grid
-    const int ntn = (p.N + BN - 1) / BN;
-    RaggedTile tile;
-    if (!ragged_m_tile(p.offsets, p.E, ntn, s_tiles, tile)) return;
-    const int e = tile.e, row0 = tile.row0, row_end = tile.row_end, n0 = tile.n0;
-    const int KB = p.K / 32;  // scale blocks per row
-
-    const i32x4_t rsrc_a = rsrc_words(p.A + (int64_t)row0 * p.K, (uint32_t)((int64_t)(row_end - row0) * p.K));
-    const i32x4_t rsrc_b =
-        rsrc_words(p.B + ((int64_t)e * p.N + n0) * p.K, (uint32_t)((int64_t)(p.N - n0) * p.K));
-    const __amdgpu_buffer_rsrc_t rsrc_as =
-        make_rsrc(p.As + (int64_t)row0 * KB, (uint32_t)((int64_t)(row_end - row0) * KB));
-    const __amdgpu_buffer_rsrc_t rsrc_bs =
-        make_rsrc(p.Bs + ((int64_t)e * p.N + n0) * KB, (uint32_t)((int64_t)(p.N - n0) * KB));
-
-    uint32_t off[kMxLoads];
-#pragma unroll
-    for (int i = 0; i < kMxLoads; ++i) {
-        const int q = (i * kWaves + wave) * 64 + lane;
-        const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
-        off[i] = (uint32_t)(r * p.K + c * 16);
-    }
-    auto issue = [&](int kt, int buf) {
-        const uint32_t l0 = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_ab[buf][0]) + wave * 1024;
-        const uint32_t dk = (uint32_t)kt * MBK;
-#pragma unroll
-        for (int i = 0; i < kMxLoads; ++i) lds_copy16(rsrc_a, l0 + i * kWaves * 1024, off[i] + dk);
-#pragma unroll
-        for (int i = 0; i < kMxLoads; ++i) lds_copy16(rsrc_b, l0 + BM * MBK + i * kWaves * 1024, off[i] + dk);
-    };
-    // per-lane scale words: 4 consecutive K blocks (one slab) of this lane's rows/columns,
-    // shifted by this half-wave's block so that K step ks uses byte 2*ks
     const int h = lane >> 5;
-    auto load_scales = [&](int kt, uint32_t* sa, uint32_t* sb) {
+    const int ntn = (p.N + BN - 1) / BN;
+    const int KB = p.K / 32;  // scale blocks per row
+    const int nk = p.K / MBK;
+    const int mtiles = ragged_m_prefix(p.offsets, p.E, s_tiles);
+    const int total = mtiles * ntn;
+    const int nb = gridDim.x;  // a multiple of 8
+    auto logical = [&](int round) -> int {
+        const int b = blockIdx.x;
+        return round * nb + (b & 7) * (nb >> 3) + (b >> 3);
+    };
+    auto get_tile = [&](int t) -> RaggedTile {
+        RaggedTile r = ragged_m_decode(p.offsets, p.E, ntn, mtiles, s_tiles, t);
+        r.e = __builtin_amdgcn_readfirstlane(r.e);
+        r.row0 = __builtin_amdgcn_readfirstlane(r.row0);
+        r.row_end = __builtin_amdgcn_readfirstlane(r.row_end);
+        r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+        return r;
+    };
+    // operand regions of a tile: codes and scales, rows past the region read 0
+    struct MxSrc {
+        const uint8_t *a, *b, *as, *bs;
+        uint32_t a_bytes, b_bytes, as_bytes, bs_bytes;
+    };
+    auto make_src = [&](const RaggedTile& t) -> MxSrc {
+        MxSrc s;
+        s.a = p.A + (int64_t)t.row0 * p.K;
+        s.a_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * p.K);
+        s.b = p.B + ((int64_t)t.e * p.N + t.n0) * p.K;
+        s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * p.K);
+        s.as = p.As + (int64_t)t.row0 * KB;
+        s.as_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * KB);
+        s.bs = p.Bs + ((int64_t)t.e * p.N + t.n0) * KB;
+        s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB);
+        return s;
+    };
+    // this lane's source offset for copy 0 of a slab; copy i adds 64 rows
+    const int q0 = wave * 64 + lane;
+    const uint32_t off0 = (uint32_t)((q0 >> 3) * p.K + (((q0 & 7) ^ kmaj_swz(q0 >> 3)) * 16));
+    const uint32_t istep = (uint32_t)(kThreads / 8 * p.K);
+    auto issue = [&](const MxSrc& s, int kt, int buf) {
+        const uint32_t l0 = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_ab[buf][0]) + wave * 1024;
+        const uint32_t o = off0 + (uint32_t)kt * MBK;
+        const i32x4_t ra = rsrc_words(s.a, s.a_bytes), rb = rsrc_words(s.b, s.b_bytes);
+#pragma unroll
+        for (int i = 0; i < kMxLoads; ++i) lds_copy16(ra, l0 + i * kWaves * 1024, o + i * istep);
+#pragma unroll
+        for (int i = 0; i < kMxLoads; ++i) lds_copy16(rb, l0 + BM * MBK + i * kWaves * 1024, o + i * istep);
+    };
+    // per-lane scale words: the 4 K blocks of one slab for this lane's rows
+    // and columns (raw: they are consumed only after the slab barrier, so the
+    // loads wait no earlier than the slab copies issued before them)
+    auto load_scales = [&](const MxSrc& s, int kt, uint32_t* sa, uint32_t* sb) {
+        const __amdgpu_buffer_rsrc_t ras = make_rsrc(s.as, s.as_bytes), rbs = make_rsrc(s.bs, s.bs_bytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wm * 128 + 32 * i + (lane & 31);
-            sa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc_as, (uint32_t)(r * KB + kt * 4), 0, 0) >> (8 * h);
+            sa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ras, (uint32_t)(r * KB + kt * 4), 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < TNW; ++j) {
             const int c = wn * WN + 32 * j + (lane & 31);
-            sb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc_bs, (uint32_t)(c * KB + kt * 4), 0, 0) >> (8 * h);
+            sb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbs, (uint32_t)(c * KB + kt * 4), 0, 0);
         }
     };
     // Operand fragment of row `base + (lane & 31)` for K step ks (64 bytes = K
@@ -193,73 +217,109 @@ __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
+    int round = 0;
+    int t = logical(0);
+    if (t >= total) return;
+    RaggedTile tl = get_tile(t);
+    MxSrc src = make_src(tl);
+    uint32_t sa[4], sb[TNW], na[4], nb_[TNW];
+    issue(src, 0, 0);
+    load_scales(src, 0, na, nb_);
+    int buf0 = 0;
     f32x16_t acc[4][TNW];
+    for (;;) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
-
-    const int nk = p.K / MBK;
-    uint32_t sa[4], sb[TNW], na[4], nb[TNW];
-    issue(0, 0);
-    load_scales(0, sa, sb);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            issue(kt + 1, cur ^ 1);
-            load_scales(kt + 1, na, nb);
+            for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
+        const int tn = logical(round + 1);
+        const bool have_next = tn < total;
+        RaggedTile tl_next = tl;
+        MxSrc src_next = src;
+        if (have_next) {
+            tl_next = get_tile(tn);
+            src_next = make_src(tl_next);
         }
-        const uint8_t* sA = s_ab[cur];
-        const uint8_t* sB = s_ab[cur] + BM * MBK;
-        static_for<MBK / 64>([&](auto KS) {
-            constexpr int ks = KS;
-            i32x8_t fa[4], fb[TNW];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = frag(sA, wm * 128 + 32 * i, ks);
-#pragma unroll
-            for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks);
-            __builtin_amdgcn_s_setprio(1);
-            static_for<4>([&](auto I) {
-                static_for<TNW>([&](auto J) {
-                    // the instruction reads byte 0 of each scale register, so the
-                    // block of this K step is shifted there (OPSEL stays 0)
-                    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
-                        (int)(sa[I] >> (16 * ks)));
-                });
-            });
-            __builtin_amdgcn_s_setprio(0);
-        });
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (kt + 1 < nk) {
+        // shifted by this half-wave's block: K step ks then finds its scale
+        // in byte 0 after a further shift by 16 ks
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sa[i] = na[i];
+        for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
 #pragma unroll
-            for (int j = 0; j < TNW; ++j) sb[j] = nb[j];
-        }
-    }
-
-    // epilogue: bf16 Y, lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
-    const int rbase = row0 + wm * 128 + (lane & 31);
-    static_for<4>([&](auto I) {
-        const int m = rbase + 32 * I;
-        if (m < row_end) {
-            static_for<TNW>([&](auto J) {
-                if (n0 + wn * WN + 32 * J < p.N) {
-                    static_for<4>([&](auto Q) {
-                        const int c = n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
-                        uint2 v;
-                        v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
-                        v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
-                        *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
+        for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = (buf0 + kt) & 1;
+            // scale loads first: any wait the compiler places on their
+            // registers then precedes (and cannot stall on) the slab copies
+            if (kt + 1 < nk) {
+                load_scales(src, kt + 1, na, nb_);
+                issue(src, kt + 1, cur ^ 1);
+            } else if (have_next) {
+                load_scales(src_next, 0, na, nb_);
+                issue(src_next, 0, cur ^ 1);
+            }
+            const uint8_t* sA = s_ab[cur];
+            const uint8_t* sB = s_ab[cur] + BM * MBK;
+            static_for<MBK / 64>([&](auto KS) {
+                constexpr int ks = KS;
+                i32x8_t fa[4], fb[TNW];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fa[i] = frag(sA, wm * 128 + 32 * i, ks);
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks);
+                __builtin_amdgcn_s_setprio(1);
+                static_for<4>([&](auto I) {
+                    static_for<TNW>([&](auto J) {
+                        // the instruction reads byte 0 of each scale register, so the
+                        // block of this K step is shifted there (OPSEL stays 0)
+                        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
+                            (int)(sa[I] >> (16 * ks)));
                     });
-                }
+                });
+                __builtin_amdgcn_s_setprio(0);
             });
+            // Pin the MFMAs here: left alone, the compiler sinks them below the
+            // barrier that waits for the next slab's copies (they touch no
+            // memory), which serialises that wait with the multiply.
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) asm volatile("" : "+v"(acc[i][j]));
+            if (kt + 1 < nk) {
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
+            }
         }
-    });
+        // epilogue: bf16 Y, lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
+        const int rbase = tl.row0 + wm * 128 + (lane & 31);
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            if (m < tl.row_end) {
+                static_for<TNW>([&](auto J) {
+                    if (tl.n0 + wn * WN + 32 * J < p.N) {
+                        static_for<4>([&](auto Q) {
+                            const int c = tl.n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
+                            uint2 v;
+                            v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                            v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                            *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
+                        });
+                    }
+                });
+            }
+        });
+        if (!have_next) break;
+        ++round;
+        buf0 = (buf0 + nk) & 1;
+        tl = tl_next;
+        src = src_next;
+    }
 }
 
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
@@ -269,7 +329,7 @@ int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, 
     a.A = a_q; a.As = a_s; a.B = w2t_q; a.Bs = w2t_s;
     a.offsets = offsets; a.E = E; a.N = d; a.K = n;
     a.out = y;
-    mx_fc2_kernel<<<ragged_m_grid(M_cap, E, d), kThreads, 0, s>>>(a);
+    mx_fc2_kernel<<<persistent_grid(ragged_m_grid(M_cap, E, d)), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
