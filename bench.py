@@ -150,7 +150,7 @@ def main():
     def step(record=False):
         M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-        M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -250,7 +250,7 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
     d, n = wl.d, wl.n
     end = int(buf.offsets[-1].item())
     rows = [
-        ("permute", lambda: M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm),
+        ("permute", lambda: M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm),
          None, 2.0 * wl.T * d + 2.0 * end * d + 4.0 * end),
         ("FC1+SwiGLU", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a,
                                                      buf.y, M.MOE_STAGE_FC1), 4.0 * Mr * d * n, None),

@@ -134,18 +134,21 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm,
 
 /*
  * moe_permute -- gather token rows into the expert-major buffer
- *   x_perm[r] = x[src_of[r] / k] for r < offsets[E] with src_of[r] >= 0, and
- *   x_perm[r] = 0 for the padding rows of every expert region.
+ *   x_perm[row_of[t*k + j]] = x[t] for every token t and slot j, and
+ *   x_perm[r] = 0 for the padding rows of every expert region (the rows
+ *   r < offsets[E] with src_of[r] < 0). Each token row is read once and
+ *   written to its k rows.
  *   [P2, SonicMoE section: the gather sub-kernel; P3, EP section: dispatch
  *   permutes tokens expert-major.] Used for activations (forward) and for the
  *   upstream gradient dO (backward; no weighting).
- *   x [T, d] bf16 (in), src_of [M_cap], offsets [E+1] (in),
+ *   x [T, d] bf16 (in); row_of [T*k], src_of [M_cap], offsets [E+1] (in, as
+ *   written by moe_route_counts: row_of and src_of are inverse maps);
  *   x_perm [M_cap, d] bf16 (out; rows >= offsets[E] untouched).
  * Requires d % 8 == 0; x and x_perm 16-byte aligned.
  */
-int moe_permute(const uint16_t* x, const int32_t* src_of, const int32_t* offsets,
-                int T, int k, int E, int d, int64_t M_cap, uint16_t* x_perm,
-                moe_stream_t stream);
+int moe_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_of,
+                const int32_t* offsets, int T, int k, int E, int d, int64_t M_cap,
+                uint16_t* x_perm, moe_stream_t stream);
 
 /*
  * moe_combine -- weighted un-permute: out[t] = sum over j ascending of

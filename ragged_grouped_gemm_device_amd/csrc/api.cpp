@@ -72,15 +72,16 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm, int32
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
-int moe_permute(const uint16_t* x, const int32_t* src_of, const int32_t* offsets, int T, int k,
-                int E, int d, int64_t M_cap, uint16_t* x_perm, moe_stream_t stream) {
+int moe_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_of,
+                const int32_t* offsets, int T, int k, int E, int d, int64_t M_cap, uint16_t* x_perm,
+                moe_stream_t stream) {
     const int64_t cap = capacity(T, k, E);
     if (cap < 0 || d <= 0) return MOE_ERR_INVALID_ARG;
-    if (!x || !src_of || !offsets || !x_perm) return MOE_ERR_INVALID_ARG;
+    if (!x || !row_of || !src_of || !offsets || !x_perm) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
     if (d % 8) return MOE_ERR_UNSUPPORTED;
     if (M_cap < cap) return MOE_ERR_WORKSPACE;
-    const int rc = moe::launch_permute(x, src_of, offsets, k, E, d, M_cap, x_perm, S(stream));
+    const int rc = moe::launch_permute(x, row_of, src_of, offsets, T, k, E, d, M_cap, x_perm, S(stream));
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 

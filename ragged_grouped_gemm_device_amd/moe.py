@@ -48,7 +48,7 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_mlp_bwd_workspace_bytes": (_SZ, [_I, _I64]),
     "moe_route_counts": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
-    "moe_permute": (_I, [_P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
+    "moe_permute": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P, _P, _P]),
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I,
@@ -130,10 +130,10 @@ def moe_route_counts(logits, k, topk_idx, topk_w, counts, offsets, row_of, src_o
     _check("moe_route_counts", rc)
 
 
-def moe_permute(x, src_of, offsets, k, E, x_perm):
+def moe_permute(x, row_of, src_of, offsets, k, E, x_perm):
     T, d = x.shape
-    rc = _lib().moe_permute(_ptr(x), _ptr(src_of), _ptr(offsets), T, k, E, d, x_perm.shape[0],
-                            _ptr(x_perm), _stream())
+    rc = _lib().moe_permute(_ptr(x), _ptr(row_of), _ptr(src_of), _ptr(offsets), T, k, E, d,
+                            x_perm.shape[0], _ptr(x_perm), _stream())
     _check("moe_permute", rc)
 
 
@@ -224,7 +224,7 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
     """route -> permute -> FC1+SwiGLU -> FC2 -> combine (all enqueued, no sync)."""
     moe_route_counts(logits, buf.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                      buf.src_of, buf.M_cap, buf.err, buf.route_ws, renorm)
-    moe_permute(x, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
+    moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
     moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
                         fwd_stages)
     moe_combine(buf.y, buf.row_of, buf.topk_w, buf.k, buf.out)
@@ -232,7 +232,7 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
 
 def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD):
     """gather dO -> dgrad2+dSwiGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum."""
-    moe_permute(dout, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
+    moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
     moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
                         buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
                         buf.bwd_ws, stages)

@@ -81,9 +81,11 @@ def test_host_validation_returns_before_launch():
     rc = lib.moe_route_counts(f, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, _fake(0x1004), 1 << 20, None)
     assert rc == M.MOE_ERR_INVALID_ARG
     # permute: d not a multiple of 8
-    rc = lib.moe_permute(f, f, f, 8, 2, 4, 12, 1024, f, None)
+    rc = lib.moe_permute(f, f, f, f, 8, 2, 4, 12, 1024, f, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
-    rc = lib.moe_permute(_fake(0x1002), f, f, 8, 2, 4, 16, 1024, f, None)
+    rc = lib.moe_permute(_fake(0x1002), f, f, f, 8, 2, 4, 16, 1024, f, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_permute(f, None, f, f, 8, 2, 4, 16, 1024, f, None)  # NULL row_of
     assert rc == M.MOE_ERR_INVALID_ARG
     # combine: NULL output
     rc = lib.moe_combine(f, f, None, 8, 2, 16, None, None)

@@ -43,7 +43,7 @@ def _gpu(M, wl, inp, mx=False):
                    w2t_s=buf.w2t_s)
         M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-        M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
                               M.MOE_STAGES_FWD, mx=mxd)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)

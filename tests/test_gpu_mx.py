@@ -116,7 +116,7 @@ def _run_mx_forward(M, wl, inp):
     mx = dict(a_q=buf.a_q, a_s=buf.a_s, at_q=buf.at_q, at_s=buf.at_s, w2t_q=buf.w2t_q, w2t_s=buf.w2t_s)
     M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                        buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-    M.moe_permute(x, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+    M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
     M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD, mx=mx)
     M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
     torch.cuda.synchronize()

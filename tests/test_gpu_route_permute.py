@@ -110,7 +110,7 @@ def test_permute_and_combine(M, T, E, k, d):
     offsets = torch.from_numpy(g["offsets"]).cuda()
     row_of = torch.from_numpy(g["row_of"]).cuda()
     x_perm = torch.full((cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
-    M.moe_permute(x, src_of, offsets, k, E, x_perm)
+    M.moe_permute(x, row_of, src_of, offsets, k, E, x_perm)
     torch.cuda.synchronize()
     # the oracle derives its own routing and layout from the same logits
     o_idx, o_w = O.route(lg, k)
