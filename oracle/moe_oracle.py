@@ -25,7 +25,8 @@ Readings where the pages are silent (each listed in the design notes):
     each expert segment padded to a multiple of 128 rows, empty experts
     take zero rows;
   * interleave granularity g = 32 columns, gate block first;
-  * Swish with beta = 1 (SiLU);
+  * Swish with beta = 1 (SiLU); GeGLU's GELU in its exact (erf) form,
+    gelu(x) = x * Phi(x) with Phi the standard normal CDF;
   * storage points that the path keeps in bf16 (X_perm, H, A, Y, O, dY_u,
     dH, A', dX_perm, dX) are rounded to the nearest bf16 (ties to even);
     every other value is fp64;
@@ -40,6 +41,7 @@ Parity pins live in tests/test_oracle_*.py.
 from __future__ import annotations
 
 import numpy as np
+from scipy.special import erf as _erf
 
 ALIGN = 128
 GLU_INTERLEAVE = 32
@@ -209,6 +211,26 @@ def sigmoid(v):
     return 1.0 / (1.0 + np.exp(-v))
 
 
+def gelu(v):
+    """GELU, exact form: v * Phi(v), Phi(v) = (1 + erf(v / sqrt 2)) / 2."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * 0.5 * (1.0 + _erf(v / np.sqrt(2.0)))
+
+
+def gelu_grad(v):
+    """d gelu / dv = Phi(v) + v * phi(v), phi the standard normal density."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(v / np.sqrt(2.0))) + v * np.exp(-0.5 * v * v) / np.sqrt(2.0 * np.pi)
+
+
+# the gate activation of each GLU variant and its derivative  [P1 problem
+# section: SwiGLU and GeGLU epilogues and their backward]
+GLU_ACTS = {
+    "swiglu": (silu, lambda v: sigmoid(v) * (1.0 + v * (1.0 - sigmoid(v)))),
+    "geglu": (gelu, gelu_grad),
+}
+
+
 # --------------------------------------------------------------------------
 # O5/O6: per-expert FC1 + SwiGLU and FC2  [P1 problem and core-idea sections:
 # the GLU activation applied to the FC1 output inside the GEMM epilogue;
@@ -219,14 +241,17 @@ def expert_segments(counts, offsets):
     return [(e, int(offsets[e]), int(offsets[e]) + int(counts[e])) for e in range(len(counts))]
 
 
-def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, rounding: bool = True):
-    """Grouped FC1 -> SwiGLU -> FC2 over the ragged expert-major rows.
+def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, rounding: bool = True,
+                act: str = "swiglu"):
+    """Grouped FC1 -> GLU (SwiGLU or GeGLU) -> FC2 over the ragged expert-major rows.
 
     x_perm fp64 [M_cap, d], w1 fp64 [E, d, 2n] (interleaved), w2 fp64 [E, n, d].
     Returns H [M_cap, 2n] (bf16-rounded when stored), A [M_cap, n], Y [M_cap, d];
     rows outside the real segments are zero.
-    A is computed from the unrounded FC1 output: A = silu(gate) * up.
+    A is computed from the unrounded FC1 output: A = act(gate) * up, act = silu
+    (SwiGLU) or gelu (GeGLU).
     """
+    act_fn = GLU_ACTS[act][0]
     x_perm = np.asarray(x_perm, dtype=np.float64)
     M_cap, d = x_perm.shape
     E, _, n2 = w1.shape
@@ -239,7 +264,7 @@ def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, roundi
             continue
         h = x_perm[r0:r1] @ w1[e]
         hg, hu = deinterleave(h, g)
-        a = _maybe_round(silu(hg) * hu, rounding)
+        a = _maybe_round(act_fn(hg) * hu, rounding)
         H[r0:r1] = _maybe_round(h, rounding)
         A[r0:r1] = a
         Y[r0:r1] = _maybe_round(a @ w2[e], rounding)
@@ -247,7 +272,7 @@ def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, roundi
 
 
 def forward(x, logits, w1, w2, k: int, renorm: bool = False, rounding: bool = True,
-            g: int = GLU_INTERLEAVE):
+            g: int = GLU_INTERLEAVE, act: str = "swiglu"):
     """Whole forward: route -> layout -> permute -> FC1+SwiGLU -> FC2 -> combine.
 
     x fp64 [T, d] (bf16 values), logits float32 [T, E]. Returns a dict with
@@ -259,7 +284,7 @@ def forward(x, logits, w1, w2, k: int, renorm: bool = False, rounding: bool = Tr
     M_cap = capacity_rows(T, k, E)
     counts, offsets, row_of, src_of = layout(idx, E, M_cap)
     x_perm = permute(x, row_of, k, M_cap)
-    H, A, Y = mlp_forward(x_perm, w1, w2, counts, offsets, g, rounding)
+    H, A, Y = mlp_forward(x_perm, w1, w2, counts, offsets, g, rounding, act)
     out = combine(Y, row_of, k, w, rounding)
     return dict(topk_idx=idx, topk_w=w, counts=counts, offsets=offsets, row_of=row_of,
                 src_of=src_of, M_cap=M_cap, x_perm=x_perm, H=H, A=A, Y=Y, out=out)
@@ -271,7 +296,7 @@ def forward(x, logits, w1, w2, k: int, renorm: bool = False, rounding: bool = Tr
 # evidence section: dSwiGLU fused into the dgrad GEMM]
 # --------------------------------------------------------------------------
 def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k: int,
-                 g: int = GLU_INTERLEAVE, rounding: bool = True):
+                 g: int = GLU_INTERLEAVE, rounding: bool = True, act: str = "swiglu"):
     """Manual backward of the MLP for fixed routing weights.
 
     The routing weights w are treated as inputs: dS[t,j] = dL/dw[t,j] is the
@@ -306,11 +331,12 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
             continue
         da_u = dy_u[r0:r1] @ w2[e].T                     # dA' (unweighted)
         hg, hu = deinterleave(H[r0:r1], g)
-        sg = sigmoid(hg)
-        a = hg * sg * hu
+        f, f_grad = GLU_ACTS[act]
+        fg = f(hg)
+        a = fg * hu
         da = w_row[r0:r1, None] * da_u
-        dg = da * hu * sg * (1.0 + hg * (1.0 - sg))
-        du = da * hg * sg
+        dg = da * hu * f_grad(hg)
+        du = da * fg
         dh = _maybe_round(interleave(dg, du, g), rounding)
         aw = _maybe_round(w_row[r0:r1, None] * a, rounding)
         dH[r0:r1] = dh
