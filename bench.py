@@ -64,7 +64,7 @@ def _t16(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _cpu_baseline(wl, inp, target_s=15.0):
+def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
     """Time the oracle on the first R tokens (routed like the full batch)."""
     from threadpoolctl import threadpool_info
 
@@ -75,9 +75,10 @@ def _cpu_baseline(wl, inp, target_s=15.0):
         w1 = O.from_bf16(inp["w1"])
         w2 = O.from_bf16(inp["w2"])
         t0 = time.perf_counter()
-        f = O.forward(x, inp["logits"][:R], w1, w2, wl.k)
+        f = O.forward(x, inp["logits"][:R], w1, w2, wl.k, act=act)
         O.mlp_backward(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"][:R]),
-                       f["topk_w"], f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k)
+                       f["topk_w"], f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k,
+                       act=act)
         return time.perf_counter() - t0
 
     R = 128
@@ -103,6 +104,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="balanced")
+    ap.add_argument("--act", choices=["swiglu", "geglu"], default="swiglu",
+                    help="gate activation of the GLU epilogues")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time every stage alone (stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -122,6 +125,8 @@ def main():
     M.load()
     wl = W.WORKLOADS[args.workload]
     mx_mode = args.workload == "mxfp8"
+    act = M.MOE_ACT_GEGLU if args.act == "geglu" else M.MOE_ACT_SWIGLU
+    glu = "GeGLU" if args.act == "geglu" else "SwiGLU"
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -155,14 +160,14 @@ def main():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1,
-                              mx=mx)
+                              mx=mx, act=act)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
                               mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
-        M.backward(buf, dout, w1, w2)
+        M.backward(buf, dout, w1, w2, act=act)
 
     for _ in range(args.warmup):
         step()
@@ -188,14 +193,14 @@ def main():
     fc1_tf = fc1_flops / (fc1_ms * 1e-3) / 1e12
     value = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
-          f"FC1+SwiGLU {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+          f"FC1+{glu} {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     if args.detail:
-        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx)
+        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(wl, inp)
+        cpu = _cpu_baseline(wl, inp, act=args.act)
 
     out = {
         "metric": METRIC,
@@ -212,20 +217,20 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
-                        f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+SwiGLU"
+                        f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+{glu}"
                         + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
-                        + "->combine + full backward with dSwiGLU, dS and ragged wgrads (bf16)",
+                        + f"->combine + full backward with d{glu}, dS and ragged wgrads (bf16)",
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
         "roofline": {
-            "kernel": "grouped_gemm FC1+SwiGLU",
+            "kernel": f"grouped_gemm FC1+{glu}",
             "bound": "mfma",
             "achieved": round(fc1_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fc1_tf / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(wl.name),
+            "traffic": measured_traffic(wl.name) if act == M.MOE_ACT_SWIGLU else None,
             "traffic_unit": "bytes per launch",
         },
         "cpu_baseline": cpu,
@@ -233,7 +238,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
+def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0, glu="SwiGLU"):
     """Time each stage alone (stderr only)."""
     def timeit(fn):
         fn()
@@ -252,8 +257,9 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
     rows = [
         ("permute", lambda: M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm),
          None, 2.0 * wl.T * d + 2.0 * end * d + 4.0 * end),
-        ("FC1+SwiGLU", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a,
-                                                     buf.y, M.MOE_STAGE_FC1), 4.0 * Mr * d * n, None),
+        (f"FC1+{glu}", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a,
+                                                     buf.y, M.MOE_STAGE_FC1, act=act),
+         4.0 * Mr * d * n, None),
         ("FC2", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, buf.y,
                                               M.MOE_STAGE_FC2), 2.0 * Mr * d * n, None),
         ("combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out), None,
@@ -265,8 +271,9 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
         qc = torch.empty(n, end, dtype=torch.uint8, device="cuda")
         sc = torch.empty(n, end // 32, dtype=torch.uint8, device="cuda")
         rows += [
-            ("FC1+SwiGLU+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
-                                                             buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx),
+            (f"FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
+                                                             buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx,
+                                                             act=act),
              4.0 * Mr * d * n, None),
             ("FC2 MXFP8", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a,
                                                         buf.y, M.MOE_STAGE_FC2, mx=mx),
@@ -278,7 +285,7 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10):
                    (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n), (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n)):
         rows.append((f"bwd stage 0x{st:02x}", (lambda s=st: M.moe_grouped_mlp_bwd(
             buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
-            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s)), fl, None))
+            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s, act=act)), fl, None))
     for row in rows:
         name, fn, fl, by = row[:4]
         peak = row[4] if len(row) > 4 else PEAK_BF16_TFLOPS

@@ -69,11 +69,12 @@ extern "C" {
 
 /* activation of the gated MLP */
 #define MOE_ACT_SWIGLU 0       /* silu(gate) * up, silu(x) = x / (1 + e^-x) */
+#define MOE_ACT_GEGLU 1        /* gelu(gate) * up, gelu(x) = x * Phi(x) (exact, erf form) */
 
 /* stage bits of moe_grouped_mlp_fwd / moe_grouped_mlp_bwd */
-#define MOE_STAGE_FC1 0x01     /* H = X_perm W1_e, A = SwiGLU(H)            */
+#define MOE_STAGE_FC1 0x01     /* H = X_perm W1_e, A = GLU(H)               */
 #define MOE_STAGE_FC2 0x02     /* Y = A W2_e                                */
-#define MOE_STAGE_DGRAD2 0x04  /* dA' = dY_u W2_e^T + dSwiGLU epilogue, dS  */
+#define MOE_STAGE_DGRAD2 0x04  /* dA' = dY_u W2_e^T + dGLU epilogue, dS     */
 #define MOE_STAGE_WGRAD2 0x08  /* dW2_e = A'^T dY_u                          */
 #define MOE_STAGE_DGRAD1 0x10  /* dX_perm = dH W1_e^T                        */
 #define MOE_STAGE_WGRAD1 0x20  /* dW1_e = X_perm^T dH                        */
@@ -176,14 +177,16 @@ typedef struct moe_mx_fwd {
 } moe_mx_fwd;
 
 /*
- * moe_grouped_mlp_fwd -- grouped FC1 + SwiGLU epilogue, then grouped FC2,
+ * moe_grouped_mlp_fwd -- grouped FC1 + GLU epilogue, then grouped FC2,
  * one launch each over all experts, tiles scheduled from device offsets;
  * empty experts take no tiles.
  *   [P1, problem and core-idea sections: the GLU activation fused into the
  *   FC1 GEMM epilogue over interleaved weights; P3, grouped-GEMM section: one
  *   call for all experts computing only the real rows.]
- *   FC1: H = X_perm[R_e] W1_e (fp32 accumulate); A = bf16(silu(g) * u) from
- *        the fp32 accumulators; H is stored (bf16) when h != NULL.
+ *   FC1: H = X_perm[R_e] W1_e (fp32 accumulate); A = bf16(f(g) * u) from
+ *        the fp32 accumulators, f = silu (act = MOE_ACT_SWIGLU) or exact
+ *        gelu (act = MOE_ACT_GEGLU) [P1, problem section: SwiGLU and GeGLU
+ *        epilogues]; H is stored (bf16) when h != NULL.
  *   FC2: Y = bf16(A[R_e] W2_e); with mx != NULL the FC1 epilogue also writes
  *        the MXFP8 row-wise (and, if at_q != NULL, transposed) copy of the
  *        bf16 A [P1, core-idea section: MXFP8 and transposed output fused in
@@ -194,7 +197,7 @@ typedef struct moe_mx_fwd {
  *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out),
  *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
  *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a).
- * Requires d % 64 == 0, n % 64 == 0, act == MOE_ACT_SWIGLU,
+ * Requires d % 64 == 0, n % 64 == 0, act MOE_ACT_SWIGLU or MOE_ACT_GEGLU,
  * M_cap % 128 == 0, M_cap * max(d, 2n) * 2 < 2^31 and d * 2n * 2 < 2^31
  * (operands are addressed with 32-bit byte offsets); 16-byte aligned
  * pointers. Otherwise MOE_ERR_UNSUPPORTED.
@@ -208,12 +211,14 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
  * moe_grouped_mlp_bwd -- backward of the expert MLP for fixed routing.
  *   [P2, backward-rewrite section: dS_{t,e} = <dO_t, Y> = <dO_t W2^T, A>;
  *   GEMM-overlapping section: the dH kernel reloads H in its epilogue and
- *   stores dH, dS and A'; P1, published-evidence section: dSwiGLU fused into
- *   the dgrad GEMM.]
- *   DGRAD2: dA' = dY_u[R_e] W2_e^T (fp32); epilogue with a = silu(g) u from
- *           the stored H and w = topk_w of the row's pair (0 for padding):
+ *   stores dH, dS and A'; P1, published-evidence section: dSwiGLU and dGeGLU
+ *   fused into the dgrad GEMM.]
+ *   DGRAD2: dA' = dY_u[R_e] W2_e^T (fp32); epilogue with a = f(g) u from
+ *           the stored H (f the gate activation selected by act) and
+ *           w = topk_w of the row's pair (0 for padding):
  *           dS partials += dA' . a per row; dA = w dA';
- *           dg = dA u s (1 + g (1 - s)), s = sigmoid(g); du = dA silu(g);
+ *           dg = dA u f'(g) (silu' = s (1 + g (1 - s)), s = sigmoid(g);
+ *           gelu' = Phi(g) + g phi(g)); du = dA f(g);
  *           dH = bf16 interleaved (dg, du); A' = bf16(w a);
  *           then ds[t, j] = sum of the row's partials in a fixed order.
  *   WGRAD2: dW2_e = A'[R_e]^T dY_u[R_e] (fp32; exactly 0 for empty experts).

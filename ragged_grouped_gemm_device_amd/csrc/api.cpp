@@ -20,7 +20,7 @@ int64_t capacity(int T, int k, int E) {
 // Shapes of the grouped MLP that the kernels support.
 int check_mlp_shape(int E, int d, int n, int64_t M_cap, int act) {
     if (E <= 0 || E > MOE_MAX_EXPERTS || d <= 0 || n <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
-    if (act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+    if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
     if (d % 64 || n % 64 || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
     // the GEMMs address operands with 32-bit buffer offsets (bytes)
     const int64_t widest = d > 2 * n ? d : 2 * n;
@@ -123,9 +123,9 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     }
     hipStream_t s = S(stream);
     if (stages & MOE_STAGE_FC1) {
-        const int rc1 = mx ? moe::launch_fc1_swiglu_mx(x_perm, w1, offsets, E, d, n, M_cap, h, a, mx->a_q,
-                                                        mx->a_s, mx->at_q, mx->at_s, s)
-                           : moe::launch_fc1_swiglu(x_perm, w1, offsets, E, d, n, M_cap, h, a, s);
+        const int rc1 = mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, h, a,
+                                                     mx->a_q, mx->a_s, mx->at_q, mx->at_s, s)
+                           : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, h, a, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_FC2) {
@@ -174,8 +174,8 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     hipStream_t s = S(stream);
     float* part = static_cast<float*>(workspace);
     if (stages & MOE_STAGE_DGRAD2) {
-        if (moe::launch_dgrad2_dswiglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, dh,
-                                       a_w, part, s))
+        if (moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, act, dh,
+                                    a_w, part, s))
             return MOE_ERR_LAUNCH;
         if (moe::launch_ds_reduce(part, row_of, T, k, n, ds, s)) return MOE_ERR_LAUNCH;
     }

@@ -44,6 +44,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f,
 // (about 1 ulp each); saturates to 0 / 1 for large |x|.
 __device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
+// GLU gate activations. ACT 0: SiLU (SwiGLU), x * sigmoid(x). ACT 1: GELU in
+// its exact form (GeGLU), x * Phi(x) with Phi(x) = (1 + erf(x / sqrt 2)) / 2.
+template <int ACT>
+__device__ __forceinline__ float glu_gate(float x) {
+    if constexpr (ACT == 0) return x * sigmoid_f(x);
+    else return 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+}
+
+// The gate activation f(x) and its derivative f'(x):
+// SiLU' = s (1 + x (1 - s)), s = sigmoid(x); GELU' = Phi(x) + x phi(x).
+template <int ACT>
+__device__ __forceinline__ void glu_gate_grad(float x, float& f, float& df) {
+    if constexpr (ACT == 0) {
+        const float s = sigmoid_f(x);
+        f = x * s;
+        df = s * (1.f + x * (1.f - s));
+    } else {
+        const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+        f = x * cdf;
+        df = cdf + x * (0.39894228040143268f * __expf(-0.5f * x * x));
+    }
+}
+
 // Unpack 4 bf16 held in a uint2 into floats.
 __device__ __forceinline__ void unpack_bf16x4(uint2 v, float* f) {
     f[0] = __uint_as_float(v.x << 16);

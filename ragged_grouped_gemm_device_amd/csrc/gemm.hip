@@ -3,7 +3,8 @@
 // One kernel template covers every GEMM of the path:
 //   ragged-M (rows of the expert-major buffer are the M dimension; the expert
 //   of a tile is found from the device offsets):
-//     FC1 + SwiGLU epilogue, FC2, FC2 dgrad + dSwiGLU epilogue, FC1 dgrad;
+//     FC1 + GLU epilogue (SwiGLU or GeGLU), FC2, FC2 dgrad + dGLU epilogue,
+//     FC1 dgrad;
 //   ragged-K (the expert's rows are the reduction dimension): both wgrads.
 // [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, grouped-GEMM section:
 // one call for all experts over their real token counts, empty groups pass
@@ -43,7 +44,7 @@ namespace moe {
 constexpr int BK = 64;                    // K elements per LDS slab
 constexpr int kLoads = BM * BK * 2 / (kThreads * 16);  // 16-byte copies per thread per slab
 
-enum Epi { EPI_BF16 = 0, EPI_SWIGLU = 1, EPI_DSWIGLU = 2, EPI_F32 = 3, EPI_SWIGLU_MX = 4 };
+enum Epi { EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4 };
 
 struct GemmArgs {
     const uint16_t* A;  // activations (token rows)
@@ -58,12 +59,12 @@ struct GemmArgs {
     int K;  // ragged-M: reduction length
     uint16_t* out0;  // bf16 C / H / dH
     int64_t ld0;
-    uint16_t* out1;  // A (SwiGLU) / A' (dSwiGLU)
+    uint16_t* out1;  // A (GLU) / A' (dGLU)
     int64_t ld1;
     float* outf;  // fp32 C (wgrad) / dS partials
     int64_t ldf;
     int64_t f_estride;
-    const uint16_t* aux;  // H for the dSwiGLU epilogue
+    const uint16_t* aux;  // H for the dGLU epilogue
     int64_t ld_aux;
     const float* topk_w;
     const int32_t* src_of;
@@ -108,7 +109,7 @@ __device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS cha
         lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024, sr.b_off + (db + i * sr.b_istep));
 }
 
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
     __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
@@ -389,8 +390,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             }
         });
-    } else if constexpr (EPI == EPI_SWIGLU_MX) {
-        // SwiGLU as below, then the MXFP8 copies of the bf16-rounded A: row-wise
+    } else if constexpr (EPI == EPI_GLU_MX) {
+        // GLU as below, then the MXFP8 copies of the bf16-rounded A: row-wise
         // blocks (32 columns of a row: 16 in this lane, 16 in lane l ^ 32) and
         // column-wise blocks (32 rows of a column: one per lane of a half-wave).
         // 32-row blocks never straddle experts (regions are 128-row aligned).
@@ -410,7 +411,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float g = G[r];
-                            ab[r] = f32_to_bf16(g * sigmoid_f(g) * Up[r]);
+                            ab[r] = f32_to_bf16(glu_gate<ACT>(g) * Up[r]);
                             amax = max(amax, ab[r] & 0x7fffu);
                         }
                         static_for<4>([&](auto Q) {
@@ -456,7 +457,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             }
         });
-    } else if constexpr (EPI == EPI_SWIGLU) {
+    } else if constexpr (EPI == EPI_GLU) {
         // columns come in (gate 32, up 32) pairs: tiles j = 2u (gate), 2u+1 (up)
         static_for<4>([&](auto I) {
             const int m = rbase + 32 * I;
@@ -472,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 const float g = G[4 * Q + s];
-                                av[s] = g * sigmoid_f(g) * Up[4 * Q + s];
+                                av[s] = glu_gate<ACT>(g) * Up[4 * Q + s];
                             }
                             uint2 v;
                             v.x = pack_bf16x2(av[0], av[1]);
@@ -493,7 +494,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             }
         });
-    } else if constexpr (EPI == EPI_DSWIGLU) {
+    } else if constexpr (EPI == EPI_DGLU) {
         // acc = dA' over activation columns c; H holds (gate, up) interleaved.
         static_for<4>([&](auto I) {
             const int m = rbase + 32 * I;
@@ -519,14 +520,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             float dg[4], du[4], aw[4];
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
-                                const float sg = sigmoid_f(g[s]);
-                                const float sl = g[s] * sg;
-                                const float a = sl * uu[s];
+                                float fg, dfg;
+                                glu_gate_grad<ACT>(g[s], fg, dfg);
+                                const float a = fg * uu[s];
                                 const float dap = acc[I][J][4 * Q + s];
                                 dsum = fmaf(dap, a, dsum);
                                 const float da = w * dap;
-                                dg[s] = da * uu[s] * sg * (1.f + g[s] * (1.f - sg));
-                                du[s] = da * sl;
+                                dg[s] = da * uu[s] * dfg;
+                                du[s] = da * fg;
                                 aw[s] = w * a;
                             }
                             uint2 v;
@@ -570,10 +571,10 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI>
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT = 0>
 static int run(const GemmArgs& a, int64_t tile_bound, hipStream_t s) {
     if (tile_bound <= 0) return 0;
-    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI><<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI, ACT><<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -585,19 +586,20 @@ static GemmArgs zero_args() {
 
 int ds_partials_per_row(int n) { return (BN / WN) * ((n + BN - 1) / BN); }
 
-int launch_fc1_swiglu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
-                      int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, hipStream_t s) {
+int launch_fc1_glu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E, int d,
+                   int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = x_perm; g.lda = d;
     g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;
     g.offsets = offsets; g.E = E; g.N = 2 * n; g.K = d;
     g.out0 = h; g.ld0 = 2 * n;
     g.out1 = a; g.ld1 = n;
-    return run<false, true, false, EPI_SWIGLU>(g, ragged_m_grid(M_cap, E, 2 * n), s);
+    return act ? run<false, true, false, EPI_GLU, 1>(g, ragged_m_grid(M_cap, E, 2 * n), s)
+               : run<false, true, false, EPI_GLU, 0>(g, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
-int launch_fc1_swiglu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
-                         int d, int n, int64_t M_cap, uint16_t* h, uint16_t* a, uint8_t* a_q,
+int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
+                      int d, int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, uint8_t* a_q,
                          uint8_t* a_s, uint8_t* at_q, uint8_t* at_s, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = x_perm; g.lda = d;
@@ -606,7 +608,8 @@ int launch_fc1_swiglu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32
     g.out0 = h; g.ld0 = 2 * n;
     g.out1 = a; g.ld1 = n;
     g.q_row = a_q; g.s_row = a_s; g.q_col = at_q; g.s_col = at_s; g.M_cap = M_cap;
-    return run<false, true, false, EPI_SWIGLU_MX>(g, ragged_m_grid(M_cap, E, 2 * n), s);
+    return act ? run<false, true, false, EPI_GLU_MX, 1>(g, ragged_m_grid(M_cap, E, 2 * n), s)
+               : run<false, true, false, EPI_GLU_MX, 0>(g, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
@@ -619,10 +622,10 @@ int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, in
     return run<false, true, false, EPI_BF16>(g, ragged_m_grid(M_cap, E, d), s);
 }
 
-int launch_dgrad2_dswiglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
-                          const float* topk_w, const int32_t* src_of, const int32_t* offsets,
-                          int E, int d, int n, int64_t M_cap, uint16_t* dh, uint16_t* a_w,
-                          float* ds_part, hipStream_t s) {
+int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
+                       const float* topk_w, const int32_t* src_of, const int32_t* offsets, int E,
+                       int d, int n, int64_t M_cap, int act, uint16_t* dh, uint16_t* a_w,
+                       float* ds_part, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = dy_u; g.lda = d;
     g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;  // row c of W2_e is column c of W2_e^T
@@ -632,7 +635,8 @@ int launch_dgrad2_dswiglu(const uint16_t* dy_u, const uint16_t* w2, const uint16
     g.outf = ds_part; g.n_part = ds_partials_per_row(n);
     g.aux = h; g.ld_aux = 2 * n;
     g.topk_w = topk_w; g.src_of = src_of;
-    return run<false, true, true, EPI_DSWIGLU>(g, ragged_m_grid(M_cap, E, n), s);
+    return act ? run<false, true, true, EPI_DGLU, 1>(g, ragged_m_grid(M_cap, E, n), s)
+               : run<false, true, true, EPI_DGLU, 0>(g, ragged_m_grid(M_cap, E, n), s);
 }
 
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,

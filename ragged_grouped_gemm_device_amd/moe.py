@@ -25,6 +25,7 @@ MOE_MX_BLOCK = 32
 MOE_GLU_INTERLEAVE = 32
 MOE_MAX_EXPERTS = 1024
 MOE_ACT_SWIGLU = 0
+MOE_ACT_GEGLU = 1
 MOE_STAGE_FC1 = 0x01
 MOE_STAGE_FC2 = 0x02
 MOE_STAGE_DGRAD2 = 0x04
@@ -220,20 +221,21 @@ class Buffers:
             self.w2t_s = torch.empty(E, d, n // 32, dtype=u8, device=dev)
 
 
-def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True):
-    """route -> permute -> FC1+SwiGLU -> FC2 -> combine (all enqueued, no sync)."""
+def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True,
+            act=MOE_ACT_SWIGLU):
+    """route -> permute -> FC1+GLU -> FC2 -> combine (all enqueued, no sync)."""
     moe_route_counts(logits, buf.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                      buf.src_of, buf.M_cap, buf.err, buf.route_ws, renorm)
     moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
     moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
-                        fwd_stages)
+                        fwd_stages, act=act)
     moe_combine(buf.y, buf.row_of, buf.topk_w, buf.k, buf.out)
 
 
-def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD):
-    """gather dO -> dgrad2+dSwiGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum."""
+def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU):
+    """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum."""
     moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
     moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
                         buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                        buf.bwd_ws, stages)
+                        buf.bwd_ws, stages, act=act)
     moe_combine(buf.dx_perm, buf.row_of, None, buf.k, buf.dx)

@@ -34,7 +34,7 @@ def test_constants_match_header():
     for name in ("MOE_ALIGN", "MOE_MX_BLOCK", "MOE_GLU_INTERLEAVE", "MOE_MAX_EXPERTS",
                  "MOE_STAGE_FC1", "MOE_STAGE_FC2", "MOE_STAGE_DGRAD2", "MOE_STAGE_WGRAD2",
                  "MOE_STAGE_DGRAD1", "MOE_STAGE_WGRAD1", "MOE_QUANT_ROWWISE", "MOE_QUANT_COLWISE",
-                 "MOE_ERRBIT_NONFINITE_LOGIT", "MOE_ACT_SWIGLU"):
+                 "MOE_ERRBIT_NONFINITE_LOGIT", "MOE_ACT_SWIGLU", "MOE_ACT_GEGLU"):
         m = re.search(r"#define\s+%s\s+(\(?-?[0-9a-fx]+\)?)" % name, src)
         assert m, name
         assert int(m.group(1).strip("()"), 0) == getattr(M, name), name

@@ -42,7 +42,7 @@ def _poison(buf):
         getattr(buf, name).fill_(float("nan"))
 
 
-def _run_gpu(M, wl, inp, constant_logits=False):
+def _run_gpu(M, wl, inp, act=0):
     buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n)
     _poison(buf)
     x = bf16_tensor(inp["x"])
@@ -50,19 +50,19 @@ def _run_gpu(M, wl, inp, constant_logits=False):
     w1 = bf16_tensor(inp["w1"])
     w2 = bf16_tensor(inp["w2"])
     dout = bf16_tensor(inp["dout"])
-    M.forward(buf, x, logits, w1, w2)
-    M.backward(buf, dout, w1, w2)
+    M.forward(buf, x, logits, w1, w2, act=act)
+    M.backward(buf, dout, w1, w2, act=act)
     torch.cuda.synchronize()
     return buf
 
 
-def _oracle(wl, inp):
+def _oracle(wl, inp, act="swiglu"):
     x = O.from_bf16(inp["x"])
     w1 = O.from_bf16(inp["w1"])
     w2 = O.from_bf16(inp["w2"])
-    f = O.forward(x, inp["logits"], w1, w2, wl.k)
+    f = O.forward(x, inp["logits"], w1, w2, wl.k, act=act)
     b = O.mlp_backward(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"]), f["topk_w"],
-                       f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k)
+                       f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k, act=act)
     return f, b
 
 
@@ -75,12 +75,17 @@ def _check(name, got, ref, rows=None, tol=TOL):
     assert err <= tol, f"{name}: {err}"
 
 
-@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
-def test_forward_backward_parity(M, wl):
-    print(f"mlp case {wl}", flush=True)
+GEGLU_CASES = [CASES[1], CASES[2], CASES[4]]
+
+
+@pytest.mark.parametrize(
+    "wl,act", [(c, "swiglu") for c in CASES] + [(c, "geglu") for c in GEGLU_CASES],
+    ids=[c.name for c in CASES] + [c.name + "-geglu" for c in GEGLU_CASES])
+def test_forward_backward_parity(M, wl, act):
+    print(f"mlp case {wl} act={act}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _run_gpu(M, wl, inp)
-    f, b = _oracle(wl, inp)
+    buf = _run_gpu(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
+    f, b = _oracle(wl, inp, act)
     end = int(f["offsets"][-1])
 
     assert np.array_equal(buf.topk_idx.cpu().numpy(), f["topk_idx"])

@@ -105,7 +105,7 @@ def _mx_buffers(M, wl):
     return M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
 
 
-def _run_mx_forward(M, wl, inp):
+def _run_mx_forward(M, wl, inp, act=0):
     buf = _mx_buffers(M, wl)
     for t in (buf.a_q, buf.a_s, buf.at_q, buf.at_s):
         t.fill_(0xAB)
@@ -117,7 +117,8 @@ def _run_mx_forward(M, wl, inp):
     M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                        buf.src_of, buf.M_cap, buf.err, buf.route_ws)
     M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
-    M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD, mx=mx)
+    M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD, mx=mx,
+                          act=act)
     M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
     torch.cuda.synchronize()
     return buf
@@ -129,11 +130,12 @@ MX_CASES = [
 ]
 
 
-@pytest.mark.parametrize("wl", MX_CASES, ids=[c.name for c in MX_CASES])
-def test_fused_quant_epilogue(M, wl):
-    print(f"fused mx case {wl}", flush=True)
+@pytest.mark.parametrize("wl,act", [(c, "swiglu") for c in MX_CASES] + [(MX_CASES[1], "geglu")],
+                         ids=[c.name for c in MX_CASES] + [MX_CASES[1].name + "-geglu"])
+def test_fused_quant_epilogue(M, wl, act):
+    print(f"fused mx case {wl} act={act}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _run_mx_forward(M, wl, inp)
+    buf = _run_mx_forward(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
     end = int(buf.offsets[-1].item())
     # GPU-internal: the fused codes equal the standalone quantization of the same A
     a_bits = buf.a.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -144,7 +146,7 @@ def test_fused_quant_epilogue(M, wl):
     assert np.array_equal(buf.at_s.cpu().numpy()[:, :end // 32], g[3][0])
     # against the oracle: dequantized codes approximate the oracle's A
     f = O.forward(O.from_bf16(inp["x"]), inp["logits"], O.from_bf16(inp["w1"]),
-                  O.from_bf16(inp["w2"]), wl.k)
+                  O.from_bf16(inp["w2"]), wl.k, act=act)
     deq = O.mx_dequant(buf.a_q.cpu().numpy()[:end], buf.a_s.cpu().numpy()[:end])
     err = rel_err(deq, f["A"][:end])
     print(f"  dequantized A vs oracle A: {err:.3e}", flush=True)
