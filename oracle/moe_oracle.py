@@ -108,6 +108,38 @@ def route(logits, k: int, renorm: bool = False):
     return idx, w
 
 
+def route_backward(logits, topk_idx, dS, renorm: bool = False):
+    """Gradient of the loss w.r.t. the router logits, given dS = dL/dw.
+
+    The routing weights depend on the logits through the softmax; the chosen
+    experts are a fixed (piecewise constant) function of them. Without
+    renormalisation w_j = p_{e_j}, p = softmax over all E, so
+        dl_e = p_e * (g_e - sum_j p_{e_j} dS_j),  g_e = dS_j if e = e_j else 0.
+    With renormalisation w is the softmax over the k chosen logits, so
+        dl_{e_j} = w_j * (dS_j - sum_i w_i dS_i), and 0 for experts not chosen.
+    [P2 backward-rewrite section: dS is the router-score gradient the MLP
+    backward produces; it flows on through the router's softmax.]
+    """
+    lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    dS = np.asarray(dS, dtype=np.float64)
+    T, E = lg.shape
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    d = np.zeros((T, E))
+    if not renorm:
+        g = np.zeros((T, E))
+        np.put_along_axis(g, idx, dS, axis=1)
+        c = (np.take_along_axis(p, idx, axis=1) * dS).sum(axis=1, keepdims=True)
+        d = p * (g - c)
+    else:
+        w = np.take_along_axis(p, idx, axis=1)
+        w = w / w.sum(axis=1, keepdims=True)
+        c = (w * dS).sum(axis=1, keepdims=True)
+        np.put_along_axis(d, idx, w * (dS - c), axis=1)
+    return d
+
+
 # --------------------------------------------------------------------------
 # O2: counts, aligned offsets, row maps  [P1 core-idea section: per-expert
 # counts kept on the device; P3 dropless section: one contiguous buffer;
