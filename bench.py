@@ -167,7 +167,7 @@ def main():
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
                               mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
-        M.backward(buf, dout, w1, w2, act=act)
+        M.backward(buf, dout, w1, w2, act=act, logits=logits)
 
     for _ in range(args.warmup):
         step()
@@ -219,7 +219,8 @@ def main():
             "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
                         f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+{glu}"
                         + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
-                        + f"->combine + full backward with d{glu}, dS and ragged wgrads (bf16)",
+                        + f"->combine + full backward with d{glu}, dS, ragged wgrads and the router "
+                        "softmax backward (bf16)",
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },

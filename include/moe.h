@@ -134,6 +134,24 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm,
                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
 
 /*
+ * moe_route_bwd -- router backward: gradient of the loss w.r.t. the router
+ *   logits, given ds = dL/dtopk_w from moe_grouped_mlp_bwd, for the experts
+ *   the forward chose (topk_idx). Without renormalisation
+ *     dlogits[t, e] = p_e (g_e - sum_j p_{e_j} ds[t, j]),
+ *   p = softmax(logits[t]) over all E, g_e = ds[t, j] if e = e_j else 0;
+ *   with renorm != 0 (weights renormalised over the chosen k)
+ *     dlogits[t, e_j] = w_j (ds[t, j] - sum_i w_i ds[t, i]), 0 elsewhere.
+ *   Non-finite logits have probability 0 and gradient 0.
+ *   [P2, backward-rewrite section: dS is the router-score gradient and flows
+ *   on through the router.]
+ *   logits [T, E] fp32, topk_idx [T, k] int32 (as written by
+ *   moe_route_counts), ds [T, k] fp32 (in); dlogits [T, E] fp32 (out).
+ * Requires 0 < k <= E <= MOE_MAX_EXPERTS, T > 0; else MOE_ERR_INVALID_ARG.
+ */
+int moe_route_bwd(const float* logits, const int32_t* topk_idx, const float* ds, int T, int E,
+                  int k, int renorm, float* dlogits, moe_stream_t stream);
+
+/*
  * moe_permute -- gather token rows into the expert-major buffer
  *   x_perm[row_of[t*k + j]] = x[t] for every token t and slot j, and
  *   x_perm[r] = 0 for the padding rows of every expert region (the rows

@@ -72,6 +72,14 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm, int32
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
+int moe_route_bwd(const float* logits, const int32_t* topk_idx, const float* ds, int T, int E, int k,
+                  int renorm, float* dlogits, moe_stream_t stream) {
+    if (T <= 0 || E <= 0 || k <= 0 || k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_idx || !ds || !dlogits) return MOE_ERR_INVALID_ARG;
+    const int rc = moe::launch_route_bwd(logits, T, E, k, renorm, topk_idx, ds, dlogits, S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
 int moe_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_of,
                 const int32_t* offsets, int T, int k, int E, int d, int64_t M_cap, uint16_t* x_perm,
                 moe_stream_t stream) {

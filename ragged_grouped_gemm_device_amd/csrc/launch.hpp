@@ -18,6 +18,8 @@ int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* 
                  int32_t* src_of, int64_t M_cap, int32_t* err_word, void* ws, hipStream_t s);
 size_t route_workspace_bytes(int T, int k, int E);
 
+int launch_route_bwd(const float* logits, int T, int E, int k, int renorm, const int32_t* topk_idx,
+                     const float* ds, float* dlogits, hipStream_t s);
 int launch_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_of,
                    const int32_t* offsets, int T, int k, int E, int d, int64_t M_cap, uint16_t* x_perm,
                    hipStream_t s);

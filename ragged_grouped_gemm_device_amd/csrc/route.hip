@@ -3,6 +3,7 @@
 // route_topk_kernel: softmax over E + top-k per token, one wavefront per token.
 //   [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, section on ragged
 //   tensors: a learned router activates each token's top-K experts.]
+// route_bwd_kernel: the router's softmax backward from dS.
 // layout kernels: per-expert counts, 128-aligned offsets and the two row maps,
 //   computed on the device with no host readback, deterministically (a stable
 //   counting sort: per-chunk histograms, an exclusive scan over chunks, then
@@ -203,6 +204,100 @@ __global__ void __launch_bounds__(256) layout_scatter_kernel(const int32_t* __re
             src_of[row] = (int32_t)p;
         }
     }
+}
+
+// Router backward, one wavefront per token: dlogits from dS = dL/dw for the
+// experts the forward chose. Without renormalisation w_j = p_{e_j} (softmax
+// over all E) and dl_e = p_e (g_e - sum_j p_{e_j} dS_j) with g_e = dS_j for
+// e = e_j, else 0; with renormalisation w is the softmax over the chosen
+// logits and dl_{e_j} = w_j (dS_j - sum_i w_i dS_i), 0 elsewhere. The chosen
+// slots are scattered through a per-wavefront LDS row. Non-finite logits
+// count as -inf (probability 0), as in the forward.
+// [SonicMoE로 보는 GPU 커널 최적화, backward-rewrite section: dS is the
+// router-score gradient; it continues through the router's softmax.]
+__global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict__ logits, int T, int E,
+                                                        int k, int renorm,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ ds,
+                                                        float* __restrict__ dlogits) {
+    __shared__ float s_g[4][MOE_MAX_E];
+    const int lane = lane_id();
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const bool live = t < T;  // no early exit: the block barrier below needs every wave
+    float* g = s_g[threadIdx.x >> 6];
+    const float* row = logits + (int64_t)(live ? t : 0) * E;
+    float v[kMaxPerLane];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        float x = -INFINITY;
+        if (live && e < E) {
+            x = row[e];
+            if (!isfinite(x)) x = -INFINITY;
+            g[e] = 0.f;
+        }
+        v[i] = x;
+        mx = fmaxf(mx, x);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+        if (lane + 64 * i < E && v[i] > -INFINITY) s += expf(v[i] - mx);
+    s = wave_sum(s);
+    if (!(mx > -INFINITY)) s = 1.f;
+    const float inv_s = 1.f / s;
+    // chosen slots: probability p_j of e_j; P = sum of the chosen probabilities
+    float pj_sum = 0.f, c = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 64) {
+        const int j = j0 + lane;
+        float pj = 0.f, dj = 0.f;
+        if (live && j < k) {
+            const float x = row[topk_idx[(int64_t)t * k + j]];
+            pj = isfinite(x) ? expf(x - mx) * inv_s : 0.f;
+            dj = ds[(int64_t)t * k + j];
+        }
+        pj_sum += pj;
+        c += pj * dj;
+    }
+    pj_sum = wave_sum(pj_sum);
+    c = wave_sum(c);  // sum_j p_j dS_j
+    if (renorm) c = pj_sum > 0.f ? c / pj_sum : 0.f;  // sum_j w_j dS_j
+    __syncthreads();  // g rows cleared
+    for (int j0 = 0; j0 < k; j0 += 64) {
+        const int j = j0 + lane;
+        if (live && j < k) {
+            const int e = topk_idx[(int64_t)t * k + j];
+            const float dj = ds[(int64_t)t * k + j];
+            if (renorm) {
+                const float x = row[e];
+                const float pj = isfinite(x) ? expf(x - mx) * inv_s : 0.f;
+                const float wj = pj_sum > 0.f ? pj / pj_sum : 0.f;
+                g[e] = wj * (dj - c);
+            } else {
+                g[e] = dj;
+            }
+        }
+    }
+    __syncthreads();  // chosen slots scattered
+    if (!live) return;
+    float* out = dlogits + (int64_t)t * E;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            const float pe = v[i] > -INFINITY ? expf(v[i] - mx) * inv_s : 0.f;
+            out[e] = renorm ? g[e] : pe * (g[e] - c);
+        }
+    }
+}
+
+int launch_route_bwd(const float* logits, int T, int E, int k, int renorm, const int32_t* topk_idx,
+                     const float* ds, float* dlogits, hipStream_t s) {
+    route_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, ds, dlogits);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,

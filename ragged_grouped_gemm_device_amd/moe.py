@@ -49,6 +49,7 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_mlp_bwd_workspace_bytes": (_SZ, [_I, _I64]),
     "moe_route_counts": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
     "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P, _P, _P]),
@@ -131,6 +132,14 @@ def moe_route_counts(logits, k, topk_idx, topk_w, counts, offsets, row_of, src_o
     _check("moe_route_counts", rc)
 
 
+def moe_route_bwd(logits, topk_idx, ds, dlogits, renorm=False):
+    T, E = logits.shape
+    k = topk_idx.shape[1]
+    rc = _lib().moe_route_bwd(_ptr(logits), _ptr(topk_idx), _ptr(ds), T, E, k, int(renorm),
+                              _ptr(dlogits), _stream())
+    _check("moe_route_bwd", rc)
+
+
 def moe_permute(x, row_of, src_of, offsets, k, E, x_perm):
     T, d = x.shape
     rc = _lib().moe_permute(_ptr(x), _ptr(row_of), _ptr(src_of), _ptr(offsets), T, k, E, d,
@@ -211,6 +220,7 @@ class Buffers:
         self.dx = torch.empty(T, d, dtype=bf, device=dev)
         self.dw1 = torch.empty(E, d, 2 * n, dtype=f32, device=dev)
         self.dw2 = torch.empty(E, n, d, dtype=f32, device=dev)
+        self.dlogits = torch.empty(T, E, dtype=f32, device=dev)
         self.bwd_ws = torch.empty(max(16, moe_mlp_bwd_workspace_bytes(n, M)), dtype=u8, device=dev)
         if mx:
             self.a_q = torch.empty(M, n, dtype=u8, device=dev)
@@ -232,10 +242,14 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
     moe_combine(buf.y, buf.row_of, buf.topk_w, buf.k, buf.out)
 
 
-def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU):
-    """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum."""
+def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU, logits=None,
+             renorm=False):
+    """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum, and with
+    the forward's logits also the router backward dS -> dlogits."""
     moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
     moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
                         buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
                         buf.bwd_ws, stages, act=act)
     moe_combine(buf.dx_perm, buf.row_of, None, buf.k, buf.dx)
+    if logits is not None:
+        moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits, renorm)

@@ -87,6 +87,11 @@ def test_host_validation_returns_before_launch():
     assert rc == M.MOE_ERR_INVALID_ARG
     rc = lib.moe_permute(f, None, f, f, 8, 2, 4, 16, 1024, f, None)  # NULL row_of
     assert rc == M.MOE_ERR_INVALID_ARG
+    # router backward: k > E, NULL output
+    rc = lib.moe_route_bwd(f, f, f, 8, 4, 5, 0, f, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_route_bwd(f, f, f, 8, 4, 2, 0, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
     # combine: NULL output
     rc = lib.moe_combine(f, f, None, 8, 2, 16, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG

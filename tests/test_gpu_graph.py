@@ -49,7 +49,7 @@ def test_forward_backward_single_graph_rerouted(M):
 
     def step():
         M.forward(buf, x, logits, w1, w2)
-        M.backward(buf, dout, w1, w2)
+        M.backward(buf, dout, w1, w2, logits=logits)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -75,7 +75,9 @@ def test_forward_backward_single_graph_rerouted(M):
             assert np.array_equal(buf.counts.cpu().numpy(), f["counts"]), name
             assert np.array_equal(buf.offsets.cpu().numpy(), f["offsets"]), name
             assert np.array_equal(buf.row_of.cpu().numpy(), f["row_of"]), name
-            for key, got, ref in (("out", bf16_values(buf.out), f["out"]),
+            dl_ref = O.route_backward(lg, f["topk_idx"], b["dS"])
+            for key, got, ref in (("dlogits", buf.dlogits.cpu().numpy(), dl_ref),
+                                  ("out", bf16_values(buf.out), f["out"]),
                                   ("dx", bf16_values(buf.dx), b["dx"]),
                                   ("dS", buf.ds.cpu().numpy(), b["dS"]),
                                   ("dW1", buf.dw1.cpu().numpy(), b["dW1"]),
