@@ -106,6 +106,8 @@ def main():
     ap.add_argument("--workload", default="balanced")
     ap.add_argument("--act", choices=["swiglu", "geglu"], default="swiglu",
                     help="gate activation of the GLU epilogues")
+    ap.add_argument("--gather", action="store_true",
+                    help="GEMMs read x and dO rows through src_of (no permuted copies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="also time every stage alone (stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -155,19 +157,25 @@ def main():
     def step(record=False):
         M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-        M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        if not args.gather:
+            M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1,
-                              mx=mx, act=act)
+        if args.gather:
+            M.moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
+                                  M.MOE_STAGE_FC1 | M.MOE_GATHER_ROWS, mx=mx, act=act,
+                                  src_of=buf.src_of, k=wl.k)
+        else:
+            M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
+                                  M.MOE_STAGE_FC1, mx=mx, act=act)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
                               mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
-        M.backward(buf, dout, w1, w2, act=act, logits=logits)
+        M.backward(buf, dout, w1, w2, act=act, logits=logits, x=x if args.gather else None)
 
     for _ in range(args.warmup):
         step()
@@ -196,7 +204,8 @@ def main():
           f"FC1+{glu} {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     if args.detail:
-        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu)
+        buf.logits_for_detail = logits
+        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu, gather=args.gather)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -220,7 +229,8 @@ def main():
                         f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+{glu}"
                         + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
                         + f"->combine + full backward with d{glu}, dS, ragged wgrads and the router "
-                        "softmax backward (bf16)",
+                        "softmax backward (bf16)"
+                        + ("; x and dO rows gathered inside the GEMMs (no permute)" if args.gather else ""),
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
@@ -239,7 +249,8 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0, glu="SwiGLU"):
+def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0, glu="SwiGLU",
+            gather=False):
     """Time each stage alone (stderr only)."""
     def timeit(fn):
         fn()
@@ -282,11 +293,16 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
             ("quant A row+col", lambda: M.moe_quant_mxfp8(buf.a[:end], 3, qr, sr, qc, sc), None,
              2.0 * end * n + 2.0 * (end * n + end * n // 32)),
         ]
+    logits = buf.logits_for_detail
+    rows.append(("route bwd", lambda: M.moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits), None,
+                 8.0 * wl.T * wl.E + 8.0 * Mr))
     for st, fl in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n), (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n),
                    (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n), (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n)):
-        rows.append((f"bwd stage 0x{st:02x}", (lambda s=st: M.moe_grouped_mlp_bwd(
-            buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
-            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s, act=act)), fl, None))
+        xa, da, gflag = (x, dout, M.MOE_GATHER_ROWS) if gather else (buf.x_perm, buf.dy_u, 0)
+        rows.append((f"bwd stage 0x{st:02x}", (lambda s=st, xa=xa, da=da, gflag=gflag: M.moe_grouped_mlp_bwd(
+            xa, w1, w2, buf.h, da, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s | gflag, act=act)),
+            fl, None))
     for row in rows:
         name, fn, fl, by = row[:4]
         peak = row[4] if len(row) > 4 else PEAK_BF16_TFLOPS

@@ -80,6 +80,12 @@ extern "C" {
 #define MOE_STAGE_WGRAD1 0x20  /* dW1_e = X_perm^T dH                        */
 #define MOE_STAGES_FWD (MOE_STAGE_FC1 | MOE_STAGE_FC2)
 #define MOE_STAGES_BWD (MOE_STAGE_DGRAD2 | MOE_STAGE_WGRAD2 | MOE_STAGE_DGRAD1 | MOE_STAGE_WGRAD1)
+/* mode bit for moe_grouped_mlp_fwd / _bwd: the x_perm argument (and dy_u in
+ * the backward) is the un-permuted [T, d] tensor, and the GEMMs read its rows
+ * through src_of (row r = token src_of[r] / k; padding rows read zeros), so
+ * no expert-major copy is written or read [P2, IO-hiding section: gather
+ * fused into the GEMM's loads] */
+#define MOE_GATHER_ROWS 0x100
 
 /* bits of the device error word */
 #define MOE_ERRBIT_NONFINITE_LOGIT 0x1
@@ -214,16 +220,19 @@ typedef struct moe_mx_fwd {
  *   x_perm [M_cap, d], w1 [E, d, 2n], w2 [E, n, d] (bf16, in);
  *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out),
  *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
- *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a).
+ *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a), plus
+ *   optionally MOE_GATHER_ROWS: x_perm is then x [T, d] and FC1 reads its
+ *   rows through src_of [M_cap] (T, k: the routing shape; both are ignored
+ *   without the bit; T * d * 2 < 2^31).
  * Requires d % 64 == 0, n % 64 == 0, act MOE_ACT_SWIGLU or MOE_ACT_GEGLU,
  * M_cap % 128 == 0, M_cap * max(d, 2n) * 2 < 2^31 and d * 2n * 2 < 2^31
  * (operands are addressed with 32-bit byte offsets); 16-byte aligned
  * pointers. Otherwise MOE_ERR_UNSUPPORTED.
  */
 int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
-                        const int32_t* offsets, int E, int d, int n, int64_t M_cap,
-                        int act, unsigned stages, uint16_t* h, uint16_t* a, uint16_t* y,
-                        const moe_mx_fwd* mx, moe_stream_t stream);
+                        const int32_t* offsets, const int32_t* src_of, int T, int k, int E, int d,
+                        int n, int64_t M_cap, int act, unsigned stages, uint16_t* h, uint16_t* a,
+                        uint16_t* y, const moe_mx_fwd* mx, moe_stream_t stream);
 
 /*
  * moe_grouped_mlp_bwd -- backward of the expert MLP for fixed routing.
@@ -243,6 +252,8 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
  *   DGRAD1: dX_perm[R_e] = bf16(dH[R_e] W1_e^T).
  *   WGRAD1: dW1_e = X_perm[R_e]^T dH[R_e] (fp32, interleaved like w1).
  *   dy_u = moe_permute of dO (unweighted). Stages run in the order above.
+ *   With MOE_GATHER_ROWS in stages, x_perm is x [T, d] and dy_u is dO [T, d]
+ *   (un-permuted) and every GEMM reads their rows through src_of.
  *   x_perm, dy_u [M_cap, d]; w1 [E, d, 2n]; w2 [E, n, d]; h [M_cap, 2n]
  *   (bf16, in); topk_w [T, k] fp32, src_of [M_cap], row_of [T*k],
  *   offsets [E+1] (in); dh [M_cap, 2n], a_w [M_cap, n], dx_perm [M_cap, d]

@@ -103,14 +103,29 @@ int moe_combine(const uint16_t* y, const int32_t* row_of, const float* w, int T,
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
+// Gathered rows of an un-permuted [T, d] tensor (MOE_GATHER_ROWS): the map,
+// the routing shape and the 32-bit addressing limit of the whole tensor.
+static int gather_spec(unsigned stages, const int32_t* src_of, int T, int k, int E, int d,
+                       moe::GatherSpec& gs) {
+    gs = moe::GatherSpec{nullptr, 0, 0};
+    if (!(stages & MOE_GATHER_ROWS)) return MOE_OK;
+    if (!src_of || capacity(T, k, E) < 0) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T * d * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    gs = moe::GatherSpec{src_of, k, (int64_t)T};
+    return MOE_OK;
+}
+
 int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
-                        const int32_t* offsets, int E, int d, int n, int64_t M_cap, int act,
-                        unsigned stages, uint16_t* h, uint16_t* a, uint16_t* y,
-                        const moe_mx_fwd* mx, moe_stream_t stream) {
+                        const int32_t* offsets, const int32_t* src_of, int T, int k, int E, int d,
+                        int n, int64_t M_cap, int act, unsigned stages, uint16_t* h, uint16_t* a,
+                        uint16_t* y, const moe_mx_fwd* mx, moe_stream_t stream) {
     int rc = check_mlp_shape(E, d, n, M_cap, act);
     if (rc) return rc;
     if (!offsets || !a) return MOE_ERR_INVALID_ARG;
-    if ((stages & ~(unsigned)MOE_STAGES_FWD) || stages == 0) return MOE_ERR_INVALID_ARG;
+    if ((stages & ~(unsigned)(MOE_STAGES_FWD | MOE_GATHER_ROWS)) || !(stages & MOE_STAGES_FWD))
+        return MOE_ERR_INVALID_ARG;
+    moe::GatherSpec gx;
+    if ((rc = gather_spec(stages, src_of, T, k, E, d, gx))) return rc;
     if (mx) {
         if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
         if (!mx->a_q || !mx->a_s || !aligned16(mx->a_q) || !aligned16(mx->a_s)) return MOE_ERR_INVALID_ARG;
@@ -131,9 +146,9 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     }
     hipStream_t s = S(stream);
     if (stages & MOE_STAGE_FC1) {
-        const int rc1 = mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, h, a,
+        const int rc1 = mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a,
                                                      mx->a_q, mx->a_s, mx->at_q, mx->at_s, s)
-                           : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, h, a, s);
+                           : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_FC2) {
@@ -157,8 +172,11 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     const int64_t cap = capacity(T, k, E);
     if (cap < 0) return MOE_ERR_INVALID_ARG;
     if (M_cap < cap) return MOE_ERR_WORKSPACE;
-    if ((stages & ~(unsigned)MOE_STAGES_BWD) || stages == 0) return MOE_ERR_INVALID_ARG;
+    if ((stages & ~(unsigned)(MOE_STAGES_BWD | MOE_GATHER_ROWS)) || !(stages & MOE_STAGES_BWD))
+        return MOE_ERR_INVALID_ARG;
     if (!offsets) return MOE_ERR_INVALID_ARG;
+    moe::GatherSpec gs;
+    if ((rc = gather_spec(stages, src_of, T, k, E, d, gs))) return rc;
     if (stages & MOE_STAGE_DGRAD2) {
         if (!dy_u || !w2 || !h || !topk_w || !src_of || !row_of || !dh || !a_w || !ds || !workspace)
             return MOE_ERR_INVALID_ARG;
@@ -182,17 +200,17 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     hipStream_t s = S(stream);
     float* part = static_cast<float*>(workspace);
     if (stages & MOE_STAGE_DGRAD2) {
-        if (moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, act, dh,
+        if (moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, act, gs, dh,
                                     a_w, part, s))
             return MOE_ERR_LAUNCH;
         if (moe::launch_ds_reduce(part, row_of, T, k, n, ds, s)) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_WGRAD2)
-        if (moe::launch_wgrad(a_w, n, dy_u, d, offsets, E, dw2, s)) return MOE_ERR_LAUNCH;
+        if (moe::launch_wgrad(a_w, n, dy_u, d, offsets, E, 2, gs, dw2, s)) return MOE_ERR_LAUNCH;
     if (stages & MOE_STAGE_DGRAD1)
         if (moe::launch_dgrad1(dh, w1, offsets, E, d, n, M_cap, dx_perm, s)) return MOE_ERR_LAUNCH;
     if (stages & MOE_STAGE_WGRAD1)
-        if (moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, dw1, s)) return MOE_ERR_LAUNCH;
+        if (moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, 1, gs, dw1, s)) return MOE_ERR_LAUNCH;
     return MOE_OK;
 }
 

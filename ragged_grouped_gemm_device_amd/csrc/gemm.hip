@@ -67,7 +67,10 @@ struct GemmArgs {
     const uint16_t* aux;  // H for the dGLU epilogue
     int64_t ld_aux;
     const float* topk_w;
-    const int32_t* src_of;
+    const int32_t* src_of;  // expert-major row -> pair index t*k + j (-1: padding)
+    int gk;                 // top-k of the routing (gathered operands)
+    uint64_t gk_magic;      // ceil(2^64 / gk) for gk > 1: token = src * magic >> 64
+    int64_t g_rows;         // rows of the un-permuted tensor a gathered operand reads
     int n_part;  // dS partial columns per row
     uint8_t* q_row;  // MXFP8 copy of A: codes [M_cap, n], scales [M_cap, n/32]
     uint8_t* s_row;
@@ -75,6 +78,13 @@ struct GemmArgs {
     uint8_t* s_col;
     int64_t M_cap;
 };
+
+// Token of a pair index src = t*k + j without an integer division: with
+// magic = ceil(2^64 / k), floor(src * magic / 2^64) = floor(src / k) for every
+// 32-bit src when k <= 2^32 (the rounding excess stays below 1/k).
+__device__ __forceinline__ int token_of(int src, int k, uint64_t magic) {
+    return k == 1 ? src : (int)__umul64hi((uint64_t)(uint32_t)src, magic);
+}
 
 // Element offsets (bf16) inside the LDS slabs.
 __device__ __forceinline__ int kmaj_off(int r, int chunk) { return kmaj_byte(r, chunk) >> 1; }
@@ -90,6 +100,8 @@ struct SlabSrc {
     uint32_t a_step, b_step;
     uint32_t a_istep, b_istep;
     uint32_t a_off, b_off;
+    uint32_t g_off[kLoads];  // gathered operand: this lane's offset for copy i (slab 0)
+    int g_col0;              // ragged-K gathered operand: first column of the tile
 };
 
 // Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
@@ -97,19 +109,27 @@ struct SlabSrc {
 // (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the
 // buffer end: the API bounds keep every operand region under 2^31 bytes, so
 // the sums cannot wrap.
+template <int GATHER>
 __device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave) {
     const uint32_t da = (uint32_t)ks * sr.a_step, db = (uint32_t)ks * sr.b_step;
     const i32x4_t ra = rsrc_words(sr.a_base, sr.a_bytes);
     const i32x4_t rb = rsrc_words(sr.b_base, sr.b_bytes);
     const uint32_t l0 = (uint32_t)(uintptr_t)lds + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) lds_copy16(ra, l0 + i * kWaves * 1024, sr.a_off + (da + i * sr.a_istep));
+    for (int i = 0; i < kLoads; ++i)
+        lds_copy16(ra, l0 + i * kWaves * 1024, GATHER == 1 ? sr.g_off[i] + da : sr.a_off + (da + i * sr.a_istep));
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024, sr.b_off + (db + i * sr.b_istep));
+        lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024,
+                   GATHER == 2 ? sr.g_off[i] + db : sr.b_off + (db + i * sr.b_istep));
 }
 
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT>
+// GATHER: 0, or the operand (1 = A, 2 = B) whose rows are read from an
+// un-permuted tensor through src_of (row -> token (src_of / k), -1 -> zeros)
+// instead of from an expert-major copy. Ragged M gathers the K-major A rows
+// of a tile once per tile; ragged K gathers the K rows of every slab, with
+// the token indices of the next slab loaded one copy-issue ahead.
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT, int GATHER>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
     __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
@@ -221,7 +241,30 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             b_bytes = (uint32_t)((int64_t)p.K * p.ldb * 2);
             sr.b_step = (uint32_t)(BK * p.ldb * 2);
         }
+        if constexpr (GATHER == 1) {  // A rows from the un-permuted tensor
+            a_base = p.A;
+            a_bytes = (uint32_t)(p.g_rows * p.lda * 2);
+            sr.a_step = RAGGED_K ? 0u : (uint32_t)(BK * 2);  // ragged K: offsets are per slab
+        }
+        if constexpr (GATHER == 2) {
+            b_base = p.B;
+            b_bytes = (uint32_t)(p.g_rows * p.ldb * 2);
+            sr.b_step = RAGGED_K ? 0u : (uint32_t)(BK * 2);
+        }
+        sr.g_col0 = GATHER == 2 ? tl.n0 : tl.m0;
         const int q = wave * 64 + lane;  // copy 0
+        if constexpr (GATHER == 1 && !RAGGED_K) {
+            // K-major A: copy i reads row (q >> 3) + 64 i of the tile; those rows
+            // come from tokens src_of / k (-1: padding row, reads zeros)
+            const int r0 = q >> 3, c = (q & 7) ^ kmaj_swz(r0);
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int gr = tl.row0 + r0 + i * (kThreads / 8);
+                const int src = gr < tl.row_end ? p.src_of[gr] : -1;
+                sr.g_off[i] = src >= 0 ? (uint32_t)(((int64_t)token_of(src, p.gk, p.gk_magic) * p.lda + c * 8) * 2)
+                                       : kMasked;
+            }
+        }
         if constexpr (A_KMAJ) {
             const int r = q >> 3, c = (q & 7) ^ kmaj_swz(r);
             sr.a_off = (uint32_t)((r * p.lda + c * 8) * 2);
@@ -245,8 +288,53 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         return sr;
     };
 
+    // Ragged-K gather: the token rows of a slab are fetched (one global load by
+    // each of the first BK threads) while the slab before it is multiplied,
+    // staged into a two-slot LDS table just before that slab's closing barrier,
+    // and read from there by every lane that copies a row: the copies never
+    // wait on the fetch, and each lane keeps one register for it, not four.
+    // The table holds each row's byte offset in the gathered tensor (token *
+    // leading dimension * 2), or kMasked for a padding row.
+    __shared__ uint32_t s_tok[RAGGED_K && GATHER != 0 ? 2 : 1][BK];
+    int tok_reg = -1;
+    int n_issue = 0;  // copies issued so far: issue n reads slot n & 1
+    auto fetch_toks = [&](const Tile& tl, int ks) {
+        if (tid < BK) {
+            const int gr = tl.k_begin + ks * BK + tid;
+            tok_reg = gr < tl.k_end ? p.src_of[gr] : -1;
+        }
+    };
+    // after a vector-memory wait, before a barrier: the table for the next issue
+    auto stash_toks = [&]() {
+        if constexpr (RAGGED_K && GATHER != 0) {
+            if (tid < BK) {
+                const int64_t ld = GATHER == 1 ? p.lda : p.ldb;
+                s_tok[n_issue & 1][tid] =
+                    tok_reg >= 0 ? (uint32_t)((int64_t)token_of(tok_reg, p.gk, p.gk_magic) * ld * 2) : kMasked;
+            }
+        }
+    };
     auto issue = [&](const SlabSrc& sr, int ks_idx, int buf) {
-        issue_slab(sr, ks_idx, (LDS_AS char*)(&s_ab[buf][0]), wave);
+        LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
+        if constexpr (RAGGED_K && GATHER != 0) {
+            // MN-major gathered operand: chunk (k row, column c) of token tok
+            SlabSrc g = sr;
+            const int q = wave * 64 + lane;
+            const int kr = q >> 5, c = (q & 31) ^ ((kr & 7) << 2);
+            const int col = sr.g_col0 + c * 8;
+            const int lim = GATHER == 1 ? p.M : p.N;
+            const uint32_t* tk = s_tok[n_issue & 1];
+            ++n_issue;
+            // a padding row's kMasked plus the column stays past the buffer end
+            uint32_t ro[kLoads];
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) ro[i] = tk[kr + i * (kThreads / 32)];
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) g.g_off[i] = col < lim ? ro[i] + (uint32_t)(col * 2) : kMasked;
+            issue_slab<GATHER>(g, ks_idx, lds, wave);  // the gathered operand's slab step is 0
+        } else {
+            issue_slab<GATHER>(sr, ks_idx, lds, wave);
+        }
     };
 
     // ---------------------------------------------------------- fragments
@@ -288,7 +376,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     SlabSrc src = make_src(tl);
     int nk = (tl.k_end - tl.k_begin) / BK;
     int buf0 = 0;  // LDS buffer holding slab 0 of the current tile
-    if (nk > 0) issue(src, 0, 0);
+    constexpr bool kTok = RAGGED_K && GATHER != 0;
+    // (a non-empty ragged-K tile has at least two slabs: expert regions are
+    // 128-row multiples, so the token prefetch below never runs past a tile)
+    if (nk > 0) {
+        if constexpr (kTok) {
+            fetch_toks(tl, 0);
+            __builtin_amdgcn_s_waitcnt(0);
+            stash_toks();
+            __syncthreads();
+        }
+        issue(src, 0, 0);
+        if constexpr (kTok) fetch_toks(tl, 1);
+    }
     bool have_next = false;
     for (;;) {
 #pragma unroll
@@ -310,13 +410,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         int next_buf0 = buf0;
         if (nk > 0) {
             __builtin_amdgcn_s_waitcnt(0);
+            stash_toks();
             __syncthreads();
             load_frags(0, buf0, 0);
             for (int kt = 0; kt < nk; ++kt) {
                 const int cur = (buf0 + kt) & 1;
                 const bool last = kt + 1 == nk;
-                if (!last) issue(src, kt + 1, cur ^ 1);
-                else if (nk_next > 0) issue(src_next, 0, cur ^ 1);
+                if (!last) {
+                    issue(src, kt + 1, cur ^ 1);
+                    if constexpr (kTok) {
+                        if (kt + 2 < nk) fetch_toks(tl, kt + 2);
+                        else if (nk_next > 0) fetch_toks(tl_next, 0);
+                    }
+                } else if (nk_next > 0) {
+                    issue(src_next, 0, cur ^ 1);
+                    if constexpr (kTok) fetch_toks(tl_next, 1);
+                }
                 const uint16_t* sa = s_ab[cur];
                 const uint16_t* sb = s_ab[cur] + BM * BK;
                 static_for<BK / 16>([&](auto KS) {
@@ -338,6 +447,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
                 if (!last) {
                     __builtin_amdgcn_s_waitcnt(0);
+                    stash_toks();
                     __syncthreads();
                     load_frags(0, cur ^ 1, 0);
                 } else {
@@ -345,7 +455,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 }
             }
         } else if (nk_next > 0) {
+            if constexpr (kTok) {
+                fetch_toks(tl_next, 0);
+                __builtin_amdgcn_s_waitcnt(0);
+                stash_toks();
+                __syncthreads();
+            }
             issue(src_next, 0, buf0);
+            if constexpr (kTok) fetch_toks(tl_next, 1);
         }
         const int e = tl.e, row0 = tl.row0, row_end = tl.row_end, n0 = tl.n0, m0 = tl.m0;
         (void)m0;
@@ -571,10 +688,11 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT = 0>
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT = 0, int GATHER = 0>
 static int run(const GemmArgs& a, int64_t tile_bound, hipStream_t s) {
     if (tile_bound <= 0) return 0;
-    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI, ACT><<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
+    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI, ACT, GATHER>
+        <<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -586,21 +704,41 @@ static GemmArgs zero_args() {
 
 int ds_partials_per_row(int n) { return (BN / WN) * ((n + BN - 1) / BN); }
 
+// A GLU-epilogue launch with the activation and gather chosen at run time.
+template <bool B_KMAJ, int EPI>
+static int run_glu(const GemmArgs& g, int act, bool gather, int64_t tile_bound, hipStream_t s) {
+    if (gather)
+        return act ? run<false, true, B_KMAJ, EPI, 1, 1>(g, tile_bound, s)
+                   : run<false, true, B_KMAJ, EPI, 0, 1>(g, tile_bound, s);
+    return act ? run<false, true, B_KMAJ, EPI, 1, 0>(g, tile_bound, s)
+               : run<false, true, B_KMAJ, EPI, 0, 0>(g, tile_bound, s);
+}
+
+static void set_gather(GemmArgs& g, const GatherSpec& gs) {
+    if (!gs.src_of) return;
+    g.src_of = gs.src_of;
+    g.gk = gs.k;
+    g.gk_magic = gs.k > 1 ? ~0ull / (uint64_t)gs.k + 1 : 0;  // ceil(2^64 / k)
+    g.g_rows = gs.rows;
+}
+
 int launch_fc1_glu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E, int d,
-                   int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, hipStream_t s) {
+                   int n, int64_t M_cap, int act, const GatherSpec& gx, uint16_t* h, uint16_t* a,
+                   hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = x_perm; g.lda = d;
     g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;
     g.offsets = offsets; g.E = E; g.N = 2 * n; g.K = d;
     g.out0 = h; g.ld0 = 2 * n;
     g.out1 = a; g.ld1 = n;
-    return act ? run<false, true, false, EPI_GLU, 1>(g, ragged_m_grid(M_cap, E, 2 * n), s)
-               : run<false, true, false, EPI_GLU, 0>(g, ragged_m_grid(M_cap, E, 2 * n), s);
+    set_gather(g, gx);
+    return run_glu<false, EPI_GLU>(g, act, gx.src_of != nullptr, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
 int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
-                      int d, int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, uint8_t* a_q,
-                         uint8_t* a_s, uint8_t* at_q, uint8_t* at_s, hipStream_t s) {
+                      int d, int n, int64_t M_cap, int act, const GatherSpec& gx, uint16_t* h,
+                      uint16_t* a, uint8_t* a_q, uint8_t* a_s, uint8_t* at_q, uint8_t* at_s,
+                      hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = x_perm; g.lda = d;
     g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;
@@ -608,8 +746,8 @@ int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t*
     g.out0 = h; g.ld0 = 2 * n;
     g.out1 = a; g.ld1 = n;
     g.q_row = a_q; g.s_row = a_s; g.q_col = at_q; g.s_col = at_s; g.M_cap = M_cap;
-    return act ? run<false, true, false, EPI_GLU_MX, 1>(g, ragged_m_grid(M_cap, E, 2 * n), s)
-               : run<false, true, false, EPI_GLU_MX, 0>(g, ragged_m_grid(M_cap, E, 2 * n), s);
+    set_gather(g, gx);
+    return run_glu<false, EPI_GLU_MX>(g, act, gx.src_of != nullptr, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
@@ -624,8 +762,8 @@ int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, in
 
 int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
                        const float* topk_w, const int32_t* src_of, const int32_t* offsets, int E,
-                       int d, int n, int64_t M_cap, int act, uint16_t* dh, uint16_t* a_w,
-                       float* ds_part, hipStream_t s) {
+                       int d, int n, int64_t M_cap, int act, const GatherSpec& gdy, uint16_t* dh,
+                       uint16_t* a_w, float* ds_part, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = dy_u; g.lda = d;
     g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;  // row c of W2_e is column c of W2_e^T
@@ -635,8 +773,8 @@ int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t*
     g.outf = ds_part; g.n_part = ds_partials_per_row(n);
     g.aux = h; g.ld_aux = 2 * n;
     g.topk_w = topk_w; g.src_of = src_of;
-    return act ? run<false, true, true, EPI_DGLU, 1>(g, ragged_m_grid(M_cap, E, n), s)
-               : run<false, true, true, EPI_DGLU, 0>(g, ragged_m_grid(M_cap, E, n), s);
+    set_gather(g, gdy);
+    return run_glu<true, EPI_DGLU>(g, act, gdy.src_of != nullptr, ragged_m_grid(M_cap, E, n), s);
 }
 
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,
@@ -658,13 +796,18 @@ int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets
 }
 
 int launch_wgrad(const uint16_t* act, int Ma, const uint16_t* grad, int Nb, const int32_t* offsets,
-                 int E, float* dw, hipStream_t s) {
+                 int E, int gather, const GatherSpec& gs, float* dw, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = act; g.lda = Ma;
     g.B = grad; g.ldb = Nb;
     g.offsets = offsets; g.E = E; g.M = Ma; g.N = Nb;
     g.outf = dw; g.ldf = Nb; g.f_estride = (int64_t)Ma * Nb;
     const int64_t tiles = (int64_t)E * ((Ma + BM - 1) / BM) * ((Nb + BN - 1) / BN);
+    if (gather && gs.src_of) {
+        set_gather(g, gs);
+        return gather == 1 ? run<true, false, false, EPI_F32, 0, 1>(g, tiles, s)
+                           : run<true, false, false, EPI_F32, 0, 2>(g, tiles, s);
+    }
     return run<true, false, false, EPI_F32>(g, tiles, s);
 }
 

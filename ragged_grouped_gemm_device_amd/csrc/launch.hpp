@@ -27,12 +27,23 @@ int launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, int
                    uint16_t* out, hipStream_t s);
 
 // Grouped GEMMs. All take the device offsets [E+1] of the ragged layout.
+// Rows of an operand read from an un-permuted [rows, cols] tensor through
+// src_of (row r holds token src_of[r] / k; -1 reads zeros). src_of == nullptr:
+// the operand is the expert-major copy itself.
+struct GatherSpec {
+    const int32_t* src_of;
+    int k;
+    int64_t rows;
+};
+
 // act: 0 = SwiGLU, 1 = GeGLU (the gate activation of the GLU epilogues)
 int launch_fc1_glu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E, int d,
-                   int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, hipStream_t s);
+                   int n, int64_t M_cap, int act, const GatherSpec& gx, uint16_t* h, uint16_t* a,
+                   hipStream_t s);
 int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
-                      int d, int n, int64_t M_cap, int act, uint16_t* h, uint16_t* a, uint8_t* a_q,
-                      uint8_t* a_s, uint8_t* at_q, uint8_t* at_s, hipStream_t s);
+                      int d, int n, int64_t M_cap, int act, const GatherSpec& gx, uint16_t* h,
+                      uint16_t* a, uint8_t* a_q, uint8_t* a_s, uint8_t* at_q, uint8_t* at_s,
+                      hipStream_t s);
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
                   const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
                   hipStream_t s);
@@ -40,14 +51,15 @@ int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, in
                int64_t M_cap, uint16_t* y, hipStream_t s);
 int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
                        const float* topk_w, const int32_t* src_of, const int32_t* offsets, int E,
-                       int d, int n, int64_t M_cap, int act, uint16_t* dh, uint16_t* a_w,
-                       float* ds_part, hipStream_t s);
+                       int d, int n, int64_t M_cap, int act, const GatherSpec& gdy, uint16_t* dh,
+                       uint16_t* a_w, float* ds_part, hipStream_t s);
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,
                      float* ds, hipStream_t s);
 int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets, int E, int d,
                   int n, int64_t M_cap, uint16_t* dx_perm, hipStream_t s);
+// gather: 0 none, 1 = the A operand (act) is gathered, 2 = the B operand (grad)
 int launch_wgrad(const uint16_t* act, int Ma, const uint16_t* grad, int Nb, const int32_t* offsets,
-                 int E, float* dw, hipStream_t s);
+                 int E, int gather, const GatherSpec& gs, float* dw, hipStream_t s);
 int ds_partials_per_row(int n);
 
 // MXFP8

@@ -34,6 +34,7 @@ MOE_STAGE_DGRAD1 = 0x10
 MOE_STAGE_WGRAD1 = 0x20
 MOE_STAGES_FWD = MOE_STAGE_FC1 | MOE_STAGE_FC2
 MOE_STAGES_BWD = MOE_STAGE_DGRAD2 | MOE_STAGE_WGRAD2 | MOE_STAGE_DGRAD1 | MOE_STAGE_WGRAD1
+MOE_GATHER_ROWS = 0x100
 MOE_ERRBIT_NONFINITE_LOGIT = 0x1
 MOE_QUANT_ROWWISE = 0x1
 MOE_QUANT_COLWISE = 0x2
@@ -52,7 +53,8 @@ SIGNATURES = {
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
-    "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P, _P, _P]),
+    "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P,
+                                 _P, _P]),
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I,
                                  C.c_uint, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_quant_mxfp8": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _P]),
@@ -154,15 +156,19 @@ def moe_combine(y, row_of, w, k, out):
 
 
 def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD, mx=None,
-                        act=MOE_ACT_SWIGLU):
+                        act=MOE_ACT_SWIGLU, src_of=None, k=0):
+    """With MOE_GATHER_ROWS in stages, x_perm is the un-permuted x [T, d] and src_of, k are
+    required."""
     E, d, n2 = w1.shape
     M_cap = a.shape[0]
+    T = x_perm.shape[0] if (stages & MOE_GATHER_ROWS) else 0
     mxp = None
     if mx is not None:
         mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s")])
         mxp = C.byref(mxs)
-    rc = _lib().moe_grouped_mlp_fwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(offsets), E, d, n2 // 2,
-                                    M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y), mxp, _stream())
+    rc = _lib().moe_grouped_mlp_fwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(offsets), _ptr(src_of), T,
+                                    k, E, d, n2 // 2, M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y),
+                                    mxp, _stream())
     _check("moe_grouped_mlp_fwd", rc)
 
 
@@ -232,24 +238,35 @@ class Buffers:
 
 
 def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True,
-            act=MOE_ACT_SWIGLU):
-    """route -> permute -> FC1+GLU -> FC2 -> combine (all enqueued, no sync)."""
+            act=MOE_ACT_SWIGLU, gather=False):
+    """route -> permute -> FC1+GLU -> FC2 -> combine (all enqueued, no sync). With gather, FC1
+    reads the rows of x through src_of and no permuted copy is made."""
     moe_route_counts(logits, buf.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                      buf.src_of, buf.M_cap, buf.err, buf.route_ws, renorm)
-    moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
-    moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
-                        fwd_stages, act=act)
+    if gather:
+        moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
+                            fwd_stages | MOE_GATHER_ROWS, act=act, src_of=buf.src_of, k=buf.k)
+    else:
+        moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
+        moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a,
+                            buf.y, fwd_stages, act=act)
     moe_combine(buf.y, buf.row_of, buf.topk_w, buf.k, buf.out)
 
 
 def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU, logits=None,
-             renorm=False):
+             renorm=False, x=None):
     """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum, and with
-    the forward's logits also the router backward dS -> dlogits."""
-    moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
-    moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
-                        buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                        buf.bwd_ws, stages, act=act)
+    the forward's logits also the router backward dS -> dlogits. With x given (the un-permuted
+    input), the GEMMs read x and dO through src_of instead of permuted copies."""
+    if x is not None:
+        moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
+                            buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                            buf.bwd_ws, stages | MOE_GATHER_ROWS, act=act)
+    else:
+        moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
+        moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
+                            buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                            buf.bwd_ws, stages, act=act)
     moe_combine(buf.dx_perm, buf.row_of, None, buf.k, buf.dx)
     if logits is not None:
         moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits, renorm)

@@ -96,16 +96,21 @@ def test_host_validation_returns_before_launch():
     rc = lib.moe_combine(f, f, None, 8, 2, 16, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG
     # mlp fwd: unsupported activation / shapes / stage bits
-    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 7, 3, None, f, f, None, None)
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 7, 3, None, f, f, None, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
-    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 96, 64, 1024, 0, 3, None, f, f, None, None)
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 96, 64, 1024, 0, 3, None, f, f, None, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
-    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1000, 0, 3, None, f, f, None, None)
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1000, 0, 3, None, f, f, None, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
-    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 0, 0x40, None, f, f, None, None)
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 0, 0x40, None, f, f, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG
-    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, 4, 128, 64, 1024, 0, 3, None, f, None, None, None)
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 0, 3, None, f, None, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG              # FC2 without y
+    # gathered rows need src_of, and a valid routing shape
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 8, 2, 4, 128, 64, 1024, 0, 0x101, None, f, f, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, f, 8, 5, 4, 128, 64, 1024, 0, 0x101, None, f, f, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # k > E
     # mlp bwd: workspace too small for the dS partials
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x04,
                                  f, f, f, f, f, f, f, 0, None)

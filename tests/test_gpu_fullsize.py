@@ -33,7 +33,7 @@ def M():
     return moe
 
 
-def _gpu(M, wl, inp, mx=False):
+def _gpu(M, wl, inp, mx=False, gather=False):
     buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=mx)
     x, w1, w2, dout = (bf16_tensor(inp[key]) for key in ("x", "w1", "w2", "dout"))
     logits = f32_tensor(inp["logits"])
@@ -48,8 +48,8 @@ def _gpu(M, wl, inp, mx=False):
                               M.MOE_STAGES_FWD, mx=mxd)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
     else:
-        M.forward(buf, x, logits, w1, w2)
-        M.backward(buf, dout, w1, w2)
+        M.forward(buf, x, logits, w1, w2, gather=gather)
+        M.backward(buf, dout, w1, w2, x=x if gather else None)
     torch.cuda.synchronize()
     return buf
 
@@ -110,12 +110,14 @@ def _sample_tokens(wl, idx, counts, rng, n=12):
     return np.array(sorted(ts))
 
 
-@pytest.mark.parametrize("name", ["balanced", "skewed", "train"])
-def test_fullsize_forward_backward(M, name):
+@pytest.mark.parametrize("name,gather", [("balanced", False), ("skewed", False), ("train", False),
+                                         ("skewed", True)],
+                         ids=["balanced", "skewed", "train", "skewed-gather"])
+def test_fullsize_forward_backward(M, name, gather):
     wl = W.WORKLOADS[name]
-    print(f"full-size case {wl}", flush=True)
+    print(f"full-size case {wl} gather={gather}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _gpu(M, wl, inp)
+    buf = _gpu(M, wl, inp, gather=gather)
     # routing and layout of every token
     idx, w = O.route(inp["logits"], wl.k)
     M_cap = O.capacity_rows(wl.T, wl.k, wl.E)
@@ -162,7 +164,7 @@ def test_fullsize_forward_backward(M, name):
     pad = src_of[:int(offsets[-1])] < 0
     if pad.any():
         prow = torch.from_numpy(np.nonzero(pad)[0][:512]).long().cuda()
-        for t in (buf.x_perm, buf.h, buf.a, buf.y, buf.dh, buf.a_w, buf.dx_perm):
+        for t in (buf.h, buf.a, buf.y, buf.dh, buf.a_w, buf.dx_perm) + (() if gather else (buf.x_perm,)):
             assert torch.all(t[prow].float() == 0)
     for e in np.nonzero(counts == 0)[0]:
         assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)

@@ -42,7 +42,7 @@ def _poison(buf):
         getattr(buf, name).fill_(float("nan"))
 
 
-def _run_gpu(M, wl, inp, act=0):
+def _run_gpu(M, wl, inp, act=0, gather=False):
     buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n)
     _poison(buf)
     x = bf16_tensor(inp["x"])
@@ -50,8 +50,8 @@ def _run_gpu(M, wl, inp, act=0):
     w1 = bf16_tensor(inp["w1"])
     w2 = bf16_tensor(inp["w2"])
     dout = bf16_tensor(inp["dout"])
-    M.forward(buf, x, logits, w1, w2, act=act)
-    M.backward(buf, dout, w1, w2, act=act)
+    M.forward(buf, x, logits, w1, w2, act=act, gather=gather)
+    M.backward(buf, dout, w1, w2, act=act, x=x if gather else None)
     torch.cuda.synchronize()
     return buf
 
@@ -76,15 +76,21 @@ def _check(name, got, ref, rows=None, tol=TOL):
 
 
 GEGLU_CASES = [CASES[1], CASES[2], CASES[4]]
+# gathered rows (MOE_GATHER_ROWS): no permuted copies of x and dO
+GATHER_CASES = [CASES[0], CASES[1], CASES[2], CASES[3]]
 
 
 @pytest.mark.parametrize(
-    "wl,act", [(c, "swiglu") for c in CASES] + [(c, "geglu") for c in GEGLU_CASES],
-    ids=[c.name for c in CASES] + [c.name + "-geglu" for c in GEGLU_CASES])
-def test_forward_backward_parity(M, wl, act):
-    print(f"mlp case {wl} act={act}", flush=True)
+    "wl,act,gather",
+    [(c, "swiglu", False) for c in CASES] + [(c, "geglu", False) for c in GEGLU_CASES]
+    + [(c, "swiglu", True) for c in GATHER_CASES] + [(CASES[1], "geglu", True)],
+    ids=[c.name for c in CASES] + [c.name + "-geglu" for c in GEGLU_CASES]
+    + [c.name + "-gather" for c in GATHER_CASES] + [CASES[1].name + "-geglu-gather"])
+def test_forward_backward_parity(M, wl, act, gather):
+    print(f"mlp case {wl} act={act} gather={gather}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _run_gpu(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
+    buf = _run_gpu(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU,
+                   gather=gather)
     f, b = _oracle(wl, inp, act)
     end = int(f["offsets"][-1])
 
@@ -93,8 +99,9 @@ def test_forward_backward_parity(M, wl, act):
     assert np.array_equal(buf.offsets.cpu().numpy(), f["offsets"])
     assert np.array_equal(buf.row_of.cpu().numpy(), f["row_of"])
     assert np.array_equal(buf.src_of.cpu().numpy(), f["src_of"])
-    assert np.array_equal(bf16_bits(buf.x_perm)[:end], O.bf16_bits(f["x_perm"][:end]))
-    assert np.array_equal(bf16_bits(buf.dy_u)[:end], O.bf16_bits(b["dy_u"][:end]))
+    if not gather:
+        assert np.array_equal(bf16_bits(buf.x_perm)[:end], O.bf16_bits(f["x_perm"][:end]))
+        assert np.array_equal(bf16_bits(buf.dy_u)[:end], O.bf16_bits(b["dy_u"][:end]))
 
     _check("H", bf16_values(buf.h), f["H"], end)
     _check("A", bf16_values(buf.a), f["A"], end)
@@ -110,7 +117,7 @@ def test_forward_backward_parity(M, wl, act):
 
     # padding rows of every permuted tensor are exactly zero
     pad = f["src_of"][:end] < 0
-    for name in ("x_perm", "h", "a", "y", "dy_u", "dh", "a_w", "dx_perm"):
+    for name in ("h", "a", "y", "dh", "a_w", "dx_perm") + (() if gather else ("x_perm", "dy_u")):
         v = bf16_bits(getattr(buf, name))[:end][pad]
         assert np.all((v == 0) | (v == 0x8000)), name
     # empty experts: exactly zero weight gradients

@@ -105,7 +105,7 @@ def _mx_buffers(M, wl):
     return M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
 
 
-def _run_mx_forward(M, wl, inp, act=0):
+def _run_mx_forward(M, wl, inp, act=0, gather=False):
     buf = _mx_buffers(M, wl)
     for t in (buf.a_q, buf.a_s, buf.at_q, buf.at_s):
         t.fill_(0xAB)
@@ -116,9 +116,14 @@ def _run_mx_forward(M, wl, inp, act=0):
     mx = dict(a_q=buf.a_q, a_s=buf.a_s, at_q=buf.at_q, at_s=buf.at_s, w2t_q=buf.w2t_q, w2t_s=buf.w2t_s)
     M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                        buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-    M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
-    M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD, mx=mx,
-                          act=act)
+    if gather:
+        M.moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
+                              M.MOE_STAGES_FWD | M.MOE_GATHER_ROWS, mx=mx, act=act, src_of=buf.src_of,
+                              k=wl.k)
+    else:
+        M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD,
+                              mx=mx, act=act)
     M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
     torch.cuda.synchronize()
     return buf
@@ -130,12 +135,16 @@ MX_CASES = [
 ]
 
 
-@pytest.mark.parametrize("wl,act", [(c, "swiglu") for c in MX_CASES] + [(MX_CASES[1], "geglu")],
-                         ids=[c.name for c in MX_CASES] + [MX_CASES[1].name + "-geglu"])
-def test_fused_quant_epilogue(M, wl, act):
-    print(f"fused mx case {wl} act={act}", flush=True)
+@pytest.mark.parametrize("wl,act,gather",
+                         [(c, "swiglu", False) for c in MX_CASES] + [(MX_CASES[1], "geglu", False),
+                                                                      (MX_CASES[1], "swiglu", True)],
+                         ids=[c.name for c in MX_CASES] + [MX_CASES[1].name + "-geglu",
+                                                           MX_CASES[1].name + "-gather"])
+def test_fused_quant_epilogue(M, wl, act, gather):
+    print(f"fused mx case {wl} act={act} gather={gather}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _run_mx_forward(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
+    buf = _run_mx_forward(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU,
+                          gather=gather)
     end = int(buf.offsets[-1].item())
     # GPU-internal: the fused codes equal the standalone quantization of the same A
     a_bits = buf.a.view(torch.int16).cpu().numpy().view(np.uint16)
