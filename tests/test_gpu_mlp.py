@@ -138,6 +138,26 @@ def test_all_tokens_to_one_expert(M):
     assert torch.all(buf.dw1[1:] == 0) and torch.all(buf.dw2[1:] == 0)
 
 
+def test_max_experts(M):
+    """E = 1024 (the library maximum): most experts get a few rows, many none."""
+    wl = W.small("e1024", T=600, k=4, E=1024, d=128, n=64, seed=33, routing="normal")
+    print(f"mlp case {wl}", flush=True)
+    inp = W.make_inputs(wl)
+    buf = _run_gpu(M, wl, inp)
+    f, b = _oracle(wl, inp)
+    assert np.array_equal(buf.offsets.cpu().numpy(), f["offsets"])
+    assert (f["counts"] == 0).sum() > 0
+    end = int(f["offsets"][-1])
+    _check("Y", bf16_values(buf.y), f["Y"], end)
+    _check("out", bf16_values(buf.out), f["out"])
+    _check("dS", buf.ds.cpu().numpy(), b["dS"])
+    _check("dX", bf16_values(buf.dx), b["dx"])
+    _check("dW1", buf.dw1.cpu().numpy(), b["dW1"])
+    _check("dW2", buf.dw2.cpu().numpy(), b["dW2"])
+    for e in np.nonzero(f["counts"] == 0)[0][:64]:
+        assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
+
+
 def test_determinism(M):
     wl = CASES[1]
     inp = W.make_inputs(wl)
