@@ -514,6 +514,55 @@ def mx_fc2(a_q, a_s, w2t_q, w2t_s, counts, offsets, rounding: bool = True):
 # --------------------------------------------------------------------------
 # O11: tolerance metric
 # --------------------------------------------------------------------------
+def mlp_backward_mx(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k: int,
+                    g: int = GLU_INTERLEAVE, act: str = "swiglu"):
+    """MXFP8 backward of the expert MLP  [P1 core-idea and published-evidence
+    sections: GroupGemm + dActivation + Quantize/Transpose; P3 three-components
+    section: MXFP8 grouped GEMM].
+
+    FC2 dgrad with the dGLU epilogue stays bf16 (dH, A', dS exactly as in
+    mlp_backward). Its outputs are quantized to MXFP8: dH row-wise (32-column
+    blocks: the K of the FC1 dgrad) and column-wise (32-row blocks: the K of
+    the FC1 wgrad), A' column-wise (the K of the FC2 wgrad). dY_u and X_perm
+    are quantized column-wise and W1_e row-wise along 2n. Then
+      dX_perm[R_e] = bf16(MX-GEMM(dH_q, W1q_e)),
+      dW2_e = deq(A'_col)[:, R_e] @ deq(dY_col)[:, R_e]^T,
+      dW1_e = deq(X_col)[:, R_e] @ deq(dH_col)[:, R_e]^T,
+    over each expert's 128-aligned row region R_e (padding rows are zero), and
+    dx = the unweighted combine of dX_perm.
+    """
+    b = mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k, g,
+                     True, act)
+    E = w1.shape[0]
+    end = int(offsets[-1])
+    dh_q, dh_s, dht_q, dht_s = quant_mxfp8(b["dH"][:end], rowwise=True, colwise=True)
+    _, _, awt_q, awt_s = quant_mxfp8(b["a_w"][:end], rowwise=False, colwise=True)
+    _, _, dyt_q, dyt_s = quant_mxfp8(b["dy_u"][:end], rowwise=False, colwise=True)
+    _, _, xt_q, xt_s = quant_mxfp8(np.asarray(x_perm)[:end], rowwise=False, colwise=True)
+    aw_d, dy_d = mx_dequant(awt_q, awt_s), mx_dequant(dyt_q, dyt_s)
+    x_d, dh_d = mx_dequant(xt_q, xt_s), mx_dequant(dht_q, dht_s)
+    M_cap = np.asarray(x_perm).shape[0]
+    dx_perm = np.zeros((M_cap, w1.shape[1]))
+    dW1 = np.zeros(w1.shape)
+    dW2 = np.zeros(w2.shape)
+    w1q = []
+    for e in range(E):
+        q, sc, _, _ = quant_mxfp8(w1[e], rowwise=True, colwise=False)
+        w1q.append((q, sc))
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        dx_perm[r0:r1] = round_bf16(mx_gemm_rows(dh_q[r0:r1], dh_s[r0:r1], q, sc))
+        dW2[e] = aw_d[:, r0:r1] @ dy_d[:, r0:r1].T
+        dW1[e] = x_d[:, r0:r1] @ dh_d[:, r0:r1].T
+    dx = combine(dx_perm, np.asarray(row_of, dtype=np.int64), k, None, True)
+    out = dict(b)
+    out.update(dx_perm=dx_perm, dx=dx, dW1=dW1, dW2=dW2, dh_q=dh_q, dh_s=dh_s, dht_q=dht_q,
+               dht_s=dht_s, awt_q=awt_q, awt_s=awt_s, dyt_q=dyt_q, dyt_s=dyt_s, xt_q=xt_q,
+               xt_s=xt_s, w1q=np.stack([q for q, _ in w1q]), w1s=np.stack([s for _, s in w1q]))
+    return out
+
+
 def max_abs_normalised_error(got, ref) -> float:
     """max|got - ref| / max|ref| (0 when both are all-zero)."""
     got = np.asarray(got, dtype=np.float64)
