@@ -147,10 +147,9 @@ def main():
     stream = torch.cuda.current_stream()
     mx = None
     if mx_mode:
-        # W2 quantized once (weights), outside the timed step
-        M.moe_quant_mxfp8(w2, M.MOE_QUANT_COLWISE, None, None, buf.w2t_q, buf.w2t_s)
-        mx = dict(a_q=buf.a_q, a_s=buf.a_s, at_q=buf.at_q, at_s=buf.at_s, w2t_q=buf.w2t_q,
-                  w2t_s=buf.w2t_s)
+        # W2 (for FC2) and W1 (for the FC1 dgrad) quantized once (weights), outside the timed step
+        buf.quantize_weights(w1, w2)
+        mx = buf.mx_fwd()
 
     ev = []  # (start, end) of the FC1 launch in each timed step
 
@@ -175,7 +174,8 @@ def main():
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
                               mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
-        M.backward(buf, dout, w1, w2, act=act, logits=logits, x=x if args.gather else None)
+        M.backward(buf, dout, w1, w2, act=act, logits=logits, x=x if args.gather else None,
+                   mx=mx_mode)
 
     for _ in range(args.warmup):
         step()
@@ -222,14 +222,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+mxfp8-fc2" if mx_mode else "bf16",
+        "dtype": "bf16+mxfp8" if mx_mode else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
                         f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+{glu}"
                         + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
                         + f"->combine + full backward with d{glu}, dS, ragged wgrads and the router "
-                        "softmax backward (bf16)"
+                        "softmax backward"
+                        + (" (dgrad2+dGLU bf16 with fused MXFP8 quantization of dH and A'; column-wise "
+                           "MXFP8 dY_u and X_perm; FC1 dgrad and both wgrads MXFP8)" if mx_mode else " (bf16)")
                         + ("; x and dO rows gathered inside the GEMMs (no permute)" if args.gather else ""),
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -303,6 +305,19 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
             xa, w1, w2, buf.h, da, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
             buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s | gflag, act=act)),
             fl, None))
+    if mx is not None:
+        mxb = buf.mx_bwd()
+        rows.append(("quant dY_u col", lambda: M.moe_quant_mxfp8(buf.dy_u, M.MOE_QUANT_COLWISE, None, None,
+                                                                 buf.dyt_q, buf.dyt_s),
+                     None, 2.0 * buf.M_cap * d + buf.M_cap * d * 33 / 32))
+        for st, fl, pk in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n, PEAK_BF16_TFLOPS),
+                           (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n, PEAK_MXFP8_TFLOPS),
+                           (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n, PEAK_MXFP8_TFLOPS),
+                           (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n, PEAK_MXFP8_TFLOPS)):
+            rows.append((f"MX bwd 0x{st:02x}", (lambda s=st: M.moe_grouped_mlp_bwd(
+                buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+                buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, s, act=act, mx=mxb)),
+                fl, None, pk))
     for row in rows:
         name, fn, fl, by = row[:4]
         peak = row[4] if len(row) > 4 else PEAK_BF16_TFLOPS

@@ -234,6 +234,24 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
                         int n, int64_t M_cap, int act, unsigned stages, uint16_t* h, uint16_t* a,
                         uint16_t* y, const moe_mx_fwd* mx, moe_stream_t stream);
 
+/* MXFP8 side of the backward (all device pointers; codes and scales as in
+ * moe_mx_fwd). DGRAD2 writes the first six, the others are inputs the caller
+ * quantizes with moe_quant_mxfp8 (column-wise dY_u and X_perm, row-wise W1). */
+typedef struct moe_mx_bwd {
+    uint8_t* dh_q;         /* [M_cap, 2n]     row-wise codes of dH (DGRAD2 out, DGRAD1 in) */
+    uint8_t* dh_s;         /* [M_cap, 2n/32]  its scales                        */
+    uint8_t* dht_q;        /* [2n, M_cap]     column-wise codes of dH, transposed (DGRAD2 out, WGRAD1 in) */
+    uint8_t* dht_s;        /* [2n, M_cap/32]  its scales                        */
+    uint8_t* awt_q;        /* [n, M_cap]      column-wise codes of A', transposed (DGRAD2 out, WGRAD2 in) */
+    uint8_t* awt_s;        /* [n, M_cap/32]   its scales                        */
+    const uint8_t* dyt_q;  /* [d, M_cap]      column-wise codes of dY_u, transposed (WGRAD2 in) */
+    const uint8_t* dyt_s;  /* [d, M_cap/32]                                     */
+    const uint8_t* xt_q;   /* [d, M_cap]      column-wise codes of X_perm, transposed (WGRAD1 in) */
+    const uint8_t* xt_s;   /* [d, M_cap/32]                                     */
+    const uint8_t* w1_q;   /* [E, d, 2n]      W1_e row-wise along 2n (DGRAD1 in) */
+    const uint8_t* w1_s;   /* [E, d, 2n/32]                                     */
+} moe_mx_bwd;
+
 /*
  * moe_grouped_mlp_bwd -- backward of the expert MLP for fixed routing.
  *   [P2, backward-rewrite section: dS_{t,e} = <dO_t, Y> = <dO_t W2^T, A>;
@@ -260,6 +278,14 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
  *   (bf16, out); ds [T, k] fp32 (out); dw1 [E, d, 2n], dw2 [E, n, d]
  *   (fp32, out). Outputs of stages not requested may be NULL.
  *   workspace: >= moe_mlp_bwd_workspace_bytes(n, M_cap) bytes.
+ *   With mx != NULL [P1, core-idea and published-evidence sections:
+ *   GroupGemm + dActivation + Quantize/Transpose; P3, three-components
+ *   section: MXFP8 grouped GEMM]: DGRAD2 stays bf16 and its epilogue also
+ *   writes the MXFP8 copies of the bf16 dH (row-wise, and column-wise
+ *   transposed) and of A' (column-wise transposed); the other three GEMMs
+ *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q, WGRAD2 from awt_q x
+ *   dyt_q, WGRAD1 from xt_q x dht_q (K = the expert's row region). Only the
+ *   rows of expert regions are written in the transposed copies.
  * Requires the shape constraints of moe_grouped_mlp_fwd.
  */
 int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
@@ -268,7 +294,8 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
                         int T, int k, int E, int d, int n, int64_t M_cap, int act,
                         unsigned stages, uint16_t* dh, uint16_t* a_w, float* ds,
                         uint16_t* dx_perm, float* dw1, float* dw2,
-                        void* workspace, size_t workspace_bytes, moe_stream_t stream);
+                        void* workspace, size_t workspace_bytes, const moe_mx_bwd* mx,
+                        moe_stream_t stream);
 
 /*
  * moe_quant_mxfp8 -- standalone MXFP8 quantization of `batch` bf16 matrices

@@ -166,7 +166,7 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
                         int T, int k, int E, int d, int n, int64_t M_cap, int act, unsigned stages,
                         uint16_t* dh, uint16_t* a_w, float* ds, uint16_t* dx_perm, float* dw1,
                         float* dw2, void* workspace, size_t workspace_bytes,
-                        moe_stream_t stream) {
+                        const moe_mx_bwd* mx, moe_stream_t stream) {
     int rc = check_mlp_shape(E, d, n, M_cap, act);
     if (rc) return rc;
     const int64_t cap = capacity(T, k, E);
@@ -185,32 +185,60 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
             return MOE_ERR_INVALID_ARG;
         if (workspace_bytes < moe_mlp_bwd_workspace_bytes(n, M_cap)) return MOE_ERR_WORKSPACE;
     }
+    // with mx the last three GEMMs read only the MXFP8 copies
     if (stages & MOE_STAGE_WGRAD2) {
-        if (!a_w || !dy_u || !dw2 || !aligned16(a_w) || !aligned16(dy_u) || !aligned16(dw2))
-            return MOE_ERR_INVALID_ARG;
+        if (!dw2 || !aligned16(dw2)) return MOE_ERR_INVALID_ARG;
+        if (!mx && (!a_w || !dy_u || !aligned16(a_w) || !aligned16(dy_u))) return MOE_ERR_INVALID_ARG;
     }
     if (stages & MOE_STAGE_DGRAD1) {
-        if (!dh || !w1 || !dx_perm || !aligned16(dh) || !aligned16(w1) || !aligned16(dx_perm))
-            return MOE_ERR_INVALID_ARG;
+        if (!dx_perm || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
+        if (!mx && (!dh || !w1 || !aligned16(dh) || !aligned16(w1))) return MOE_ERR_INVALID_ARG;
     }
     if (stages & MOE_STAGE_WGRAD1) {
-        if (!x_perm || !dh || !dw1 || !aligned16(x_perm) || !aligned16(dh) || !aligned16(dw1))
+        if (!dw1 || !aligned16(dw1)) return MOE_ERR_INVALID_ARG;
+        if (!mx && (!x_perm || !dh || !aligned16(x_perm) || !aligned16(dh))) return MOE_ERR_INVALID_ARG;
+    }
+    if (mx) {
+        auto ok = [](const void* p, const void* q) { return p && q && aligned16(p); };
+        if ((stages & MOE_STAGE_DGRAD2) &&
+            (!ok(mx->dh_q, mx->dh_s) || !ok(mx->dht_q, mx->dht_s) || !ok(mx->awt_q, mx->awt_s)))
+            return MOE_ERR_INVALID_ARG;
+        if ((stages & MOE_STAGE_WGRAD2) && (!ok(mx->awt_q, mx->awt_s) || !ok(mx->dyt_q, mx->dyt_s)))
+            return MOE_ERR_INVALID_ARG;
+        if ((stages & MOE_STAGE_DGRAD1) && (!ok(mx->dh_q, mx->dh_s) || !ok(mx->w1_q, mx->w1_s)))
+            return MOE_ERR_INVALID_ARG;
+        if ((stages & MOE_STAGE_WGRAD1) && (!ok(mx->xt_q, mx->xt_s) || !ok(mx->dht_q, mx->dht_s)))
             return MOE_ERR_INVALID_ARG;
     }
     hipStream_t s = S(stream);
     float* part = static_cast<float*>(workspace);
     if (stages & MOE_STAGE_DGRAD2) {
-        if (moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap, act, gs, dh,
-                                    a_w, part, s))
-            return MOE_ERR_LAUNCH;
+        const int rc2 = mx ? moe::launch_dgrad2_dglu_mx(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap,
+                                                         act, gs, dh, a_w, part, mx->dh_q, mx->dh_s,
+                                                         mx->dht_q, mx->dht_s, mx->awt_q, mx->awt_s, s)
+                           : moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap,
+                                                      act, gs, dh, a_w, part, s);
+        if (rc2) return MOE_ERR_LAUNCH;
         if (moe::launch_ds_reduce(part, row_of, T, k, n, ds, s)) return MOE_ERR_LAUNCH;
     }
-    if (stages & MOE_STAGE_WGRAD2)
-        if (moe::launch_wgrad(a_w, n, dy_u, d, offsets, E, 2, gs, dw2, s)) return MOE_ERR_LAUNCH;
-    if (stages & MOE_STAGE_DGRAD1)
-        if (moe::launch_dgrad1(dh, w1, offsets, E, d, n, M_cap, dx_perm, s)) return MOE_ERR_LAUNCH;
-    if (stages & MOE_STAGE_WGRAD1)
-        if (moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, 1, gs, dw1, s)) return MOE_ERR_LAUNCH;
+    if (stages & MOE_STAGE_WGRAD2) {
+        const int rc2 = mx ? moe::launch_mx_wgrad(mx->awt_q, mx->awt_s, n, mx->dyt_q, mx->dyt_s, d, offsets,
+                                                   E, M_cap, dw2, s)
+                           : moe::launch_wgrad(a_w, n, dy_u, d, offsets, E, 2, gs, dw2, s);
+        if (rc2) return MOE_ERR_LAUNCH;
+    }
+    if (stages & MOE_STAGE_DGRAD1) {
+        const int rc1 = mx ? moe::launch_mx_ragged_m(mx->dh_q, mx->dh_s, mx->w1_q, mx->w1_s, offsets, E, d,
+                                                      2 * n, M_cap, dx_perm, s)
+                           : moe::launch_dgrad1(dh, w1, offsets, E, d, n, M_cap, dx_perm, s);
+        if (rc1) return MOE_ERR_LAUNCH;
+    }
+    if (stages & MOE_STAGE_WGRAD1) {
+        const int rc1 = mx ? moe::launch_mx_wgrad(mx->xt_q, mx->xt_s, d, mx->dht_q, mx->dht_s, 2 * n, offsets,
+                                                   E, M_cap, dw1, s)
+                           : moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, 1, gs, dw1, s);
+        if (rc1) return MOE_ERR_LAUNCH;
+    }
     return MOE_OK;
 }
 

@@ -44,7 +44,7 @@ namespace moe {
 constexpr int BK = 64;                    // K elements per LDS slab
 constexpr int kLoads = BM * BK * 2 / (kThreads * 16);  // 16-byte copies per thread per slab
 
-enum Epi { EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4 };
+enum Epi { EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4, EPI_DGLU_MX = 5 };
 
 struct GemmArgs {
     const uint16_t* A;  // activations (token rows)
@@ -76,6 +76,8 @@ struct GemmArgs {
     uint8_t* s_row;
     uint8_t* q_col;  // transposed: codes [n, M_cap], scales [n, M_cap/32] (nullable)
     uint8_t* s_col;
+    uint8_t* q2_col;  // dGLU MX: A' transposed codes [n, M_cap], scales [n, M_cap/32]
+    uint8_t* s2_col;
     int64_t M_cap;
 };
 
@@ -414,6 +416,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             __syncthreads();
             load_frags(0, buf0, 0);
             for (int kt = 0; kt < nk; ++kt) {
+                // No vector-memory load is in flight here in the steady state (the
+                // previous slab ended with a full wait), so this wait is free; it
+                // makes registers reloaded from scratch before the loop ready on
+                // entry, instead of the compiler waiting for them inside the loop,
+                // where the same counter also tracks the slab copies.
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 const int cur = (buf0 + kt) & 1;
                 const bool last = kt + 1 == nk;
                 if (!last) {
@@ -523,19 +531,17 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         const int ac = hc / 2;  // first A column of the 32-column block
                         const f32x16_t& G = acc[I][2 * U];
                         const f32x16_t& Up = acc[I][2 * U + 1];
-                        uint32_t ab[16];
-                        uint32_t amax = 0;
+                        uint32_t abp[8];  // bf16 A pairs: slots 2r, 2r + 1
+                        uint32_t am = 0;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float g = G[r];
-                            ab[r] = f32_to_bf16(glu_gate<ACT>(g) * Up[r]);
-                            amax = max(amax, ab[r] & 0x7fffu);
+                        for (int r = 0; r < 8; ++r) {
+                            abp[r] = pack_bf16x2(glu_gate<ACT>(G[2 * r]) * Up[2 * r],
+                                                 glu_gate<ACT>(G[2 * r + 1]) * Up[2 * r + 1]);
+                            am = max_u16x2(am, abp[r] & 0x7fff7fffu);
                         }
                         static_for<4>([&](auto Q) {
-                            uint2 v;
-                            v.x = ab[4 * Q] | (ab[4 * Q + 1] << 16);
-                            v.y = ab[4 * Q + 2] | (ab[4 * Q + 3] << 16);
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) = v;
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) =
+                                make_uint2(abp[2 * Q], abp[2 * Q + 1]);
                             if (p.out0) {
                                 uint2 g2, u2;
                                 g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
@@ -547,28 +553,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                                 *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * Q) = u2;
                             }
                         });
-                        // row-wise block
+                        // row-wise block (16 values here, 16 in lane l ^ 32)
+                        uint32_t amax = max(am & 0xffffu, am >> 16);
                         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
                         const int er = mx_block_exp(amax);
                         const float invr = mx_inv_scale(er);
                         static_for<4>([&](auto Q) {
-                            const uint32_t w = e4m3x4(bf16_to_f32(ab[4 * Q]) * invr, bf16_to_f32(ab[4 * Q + 1]) * invr,
-                                                      bf16_to_f32(ab[4 * Q + 2]) * invr, bf16_to_f32(ab[4 * Q + 3]) * invr);
-                            *(uint32_t*)(p.q_row + (int64_t)m * n + ac + 4 * h + 8 * Q) = w;
+                            *(uint32_t*)(p.q_row + (int64_t)m * n + ac + 4 * h + 8 * Q) =
+                                e4m3x4(bf16_lo(abp[2 * Q]) * invr, bf16_hi(abp[2 * Q]) * invr,
+                                       bf16_lo(abp[2 * Q + 1]) * invr, bf16_hi(abp[2 * Q + 1]) * invr);
                         });
-                        if (h == 0) p.s_row[(int64_t)m * (n / 32) + ac / 32] = (uint8_t)(er + 127);
+                        p.s_row[(int64_t)m * (n / 32) + ac / 32] = (uint8_t)(er + 127);  // same byte from both halves
                         // column-wise blocks, stored transposed
                         if (p.q_col) {
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                uint32_t cm = ab[r] & 0x7fffu;
-#pragma unroll
-                                for (int o = 1; o < 32; o <<= 1) cm = max(cm, (uint32_t)__shfl_xor((int)cm, o, 64));
-                                const int ec = mx_block_exp(cm);
-                                const int c = ac + 8 * (r >> 2) + 4 * h + (r & 3);
-                                p.q_col[(int64_t)c * p.M_cap + m] = (uint8_t)e4m3_hw(bf16_to_f32(ab[r]) * mx_inv_scale(ec));
-                                if ((lane & 31) == 0) p.s_col[(int64_t)c * (p.M_cap / 32) + mb / 32] = (uint8_t)(ec + 127);
-                            }
+                            const int64_t ls = p.M_cap / 32;
+                            mx_colq32(abp, lane, p.q_col + (int64_t)ac * p.M_cap + mb, p.M_cap,
+                                      p.s_col + (int64_t)ac * ls + mb / 32, ls);
                         }
                     }
                 });
@@ -609,6 +609,85 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         });
                     }
                 });
+            }
+        });
+    } else if constexpr (EPI == EPI_DGLU_MX) {
+        // The dGLU epilogue below, then MXFP8 copies of the bf16-rounded dH
+        // (row-wise: 32-column gate or up blocks, two lanes per row; column-wise:
+        // 32-row blocks, stored transposed [2n, M_cap]) and of A' (column-wise,
+        // transposed [n, M_cap]). A 32-row block lies wholly inside or wholly
+        // past an expert region (regions are 128-row multiples), so whole blocks
+        // are skipped together.
+        const int n2 = 2 * p.N;
+        const int64_t ls = p.M_cap / 32;
+        auto rowq = [&](const uint32_t* pk, int m, int col0) {  // 16 bf16 here, 16 in lane l ^ 32
+            uint32_t am = 0;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) am = max_u16x2(am, pk[r] & 0x7fff7fffu);
+            uint32_t amax = max(am & 0xffffu, am >> 16);
+            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+            const int er = mx_block_exp(amax);
+            const float inv = mx_inv_scale(er);
+            static_for<4>([&](auto Q) {
+                *(uint32_t*)(p.q_row + (int64_t)m * n2 + col0 + 8 * Q + 4 * h) =
+                    e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv, bf16_lo(pk[2 * Q + 1]) * inv,
+                           bf16_hi(pk[2 * Q + 1]) * inv);
+            });
+            p.s_row[(int64_t)m * (n2 / 32) + col0 / 32] = (uint8_t)(er + 127);  // same byte from both halves
+        };
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            const int mb = row0 + wm * 128 + 32 * I;  // first row of this 32-row block
+            if (mb < row_end) {
+                const int src = p.src_of[m];
+                const float w = src >= 0 ? p.topk_w[src] : 0.f;
+                float dsum = 0.f;
+                const int64_t hrow = (int64_t)m * p.ld_aux;
+                const int64_t drow = (int64_t)m * p.ld0;
+                static_for<TNW>([&](auto J) {
+                    const int ct = n0 + wn * WN + 32 * J;  // first activation column of the tile
+                    if (ct < p.N) {
+                        const int gcol = 2 * ct;
+                        uint32_t dgp[8], dup[8], awp[8];  // bf16 pairs: slots 2p, 2p + 1
+                        static_for<4>([&](auto Q) {
+                            const int cc = 8 * Q + 4 * h;
+                            float g[4], uu[4], dg[4], du[4], aw[4];
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                float fg, dfg;
+                                glu_gate_grad<ACT>(g[s], fg, dfg);
+                                const float a = fg * uu[s];
+                                const float dap = acc[I][J][4 * Q + s];
+                                dsum = fmaf(dap, a, dsum);
+                                const float da = w * dap;
+                                dg[s] = da * uu[s] * dfg;
+                                du[s] = da * fg;
+                                aw[s] = w * a;
+                            }
+                            dgp[2 * Q] = pack_bf16x2(dg[0], dg[1]);
+                            dgp[2 * Q + 1] = pack_bf16x2(dg[2], dg[3]);
+                            dup[2 * Q] = pack_bf16x2(du[0], du[1]);
+                            dup[2 * Q + 1] = pack_bf16x2(du[2], du[3]);
+                            awp[2 * Q] = pack_bf16x2(aw[0], aw[1]);
+                            awp[2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
+                            *(uint2*)(p.out0 + drow + gcol + cc) = make_uint2(dgp[2 * Q], dgp[2 * Q + 1]);
+                            *(uint2*)(p.out0 + drow + gcol + 32 + cc) = make_uint2(dup[2 * Q], dup[2 * Q + 1]);
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
+                        });
+                        rowq(dgp, m, gcol);
+                        rowq(dup, m, gcol + 32);
+                        mx_colq32(dgp, lane, p.q_col + (int64_t)gcol * p.M_cap + mb, p.M_cap,
+                                  p.s_col + (int64_t)gcol * ls + mb / 32, ls);
+                        mx_colq32(dup, lane, p.q_col + (int64_t)(gcol + 32) * p.M_cap + mb, p.M_cap,
+                                  p.s_col + (int64_t)(gcol + 32) * ls + mb / 32, ls);
+                        mx_colq32(awp, lane, p.q2_col + (int64_t)ct * p.M_cap + mb, p.M_cap,
+                                  p.s2_col + (int64_t)ct * ls + mb / 32, ls);
+                    }
+                });
+                dsum += __shfl_xor(dsum, 32, 64);
+                if (h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
             }
         });
     } else if constexpr (EPI == EPI_DGLU) {
@@ -775,6 +854,27 @@ int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t*
     g.topk_w = topk_w; g.src_of = src_of;
     set_gather(g, gdy);
     return run_glu<true, EPI_DGLU>(g, act, gdy.src_of != nullptr, ragged_m_grid(M_cap, E, n), s);
+}
+
+int launch_dgrad2_dglu_mx(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
+                          const float* topk_w, const int32_t* src_of, const int32_t* offsets, int E,
+                          int d, int n, int64_t M_cap, int act, const GatherSpec& gdy, uint16_t* dh,
+                          uint16_t* a_w, float* ds_part, uint8_t* dh_q, uint8_t* dh_s,
+                          uint8_t* dht_q, uint8_t* dht_s, uint8_t* awt_q, uint8_t* awt_s,
+                          hipStream_t s) {
+    GemmArgs g = zero_args();
+    g.A = dy_u; g.lda = d;
+    g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;
+    g.offsets = offsets; g.E = E; g.N = n; g.K = d;
+    g.out0 = dh; g.ld0 = 2 * n;
+    g.out1 = a_w; g.ld1 = n;
+    g.outf = ds_part; g.n_part = ds_partials_per_row(n);
+    g.aux = h; g.ld_aux = 2 * n;
+    g.topk_w = topk_w; g.src_of = src_of;
+    g.q_row = dh_q; g.s_row = dh_s; g.q_col = dht_q; g.s_col = dht_s;
+    g.q2_col = awt_q; g.s2_col = awt_s; g.M_cap = M_cap;
+    set_gather(g, gdy);
+    return run_glu<true, EPI_DGLU_MX>(g, act, gdy.src_of != nullptr, ragged_m_grid(M_cap, E, n), s);
 }
 
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,

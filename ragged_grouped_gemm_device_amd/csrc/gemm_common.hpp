@@ -74,6 +74,8 @@ __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t 
     // message instructions), so the value written here is simply dead after.
 }
 
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt fields left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr uint32_t kMasked = 0x80000000u;  // byte offset past every buffer: the load returns 0
 
 struct RaggedTile {

@@ -23,7 +23,6 @@ namespace moe {
 constexpr int QT = 128;  // tile edge
 
 // largest magnitude bit pattern (sign cleared) among 8 bf16 values
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
     const uint32_t m = 0x7fff7fffu;
     const u16x2_t a = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, v.x & m), __builtin_bit_cast(u16x2_t, v.y & m));
@@ -112,74 +111,134 @@ int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mod
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-// ------------------------------------------------------------------ MX FC2
-// Y[R_e] = MX(A[R_e]) x MX(W2_e) on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x
-// E4M3, one E8M0 scale per lane and 32-element K block). Same workgroup tile,
-// wavefront grid and ragged-M scheduling as the bf16 grouped GEMM; both
+// ------------------------------------------------------------------ MX GEMM
+// Grouped GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, one E8M0
+// scale per lane and 32-element K block), with the workgroup tile, wavefront
+// grid and persistent XCD-aware schedule of the bf16 grouped GEMM. Both
 // operands are K-major fp8 ([rows][K] bytes), streamed global -> LDS in
 // 128-byte K slabs (two MFMA K steps of 64).
+//  * ragged M (FC2 forward, FC1 dgrad): out[R_e] = A[R_e] x B_e^T, bf16,
+//    A [M_cap, K], B [E, N, K];
+//  * ragged K (both wgrads): out_e = A[:, R_e] x B[:, R_e]^T, fp32 [E, M, N],
+//    A [M, ld] and B [N, ld] the column-wise (transposed) copies, whose K
+//    runs over the expert's row region R_e (a 128-row multiple, so slabs
+//    never straddle two experts); an empty expert's output is written as 0.
 struct MxArgs {
-    const uint8_t* A;    // [M_cap, K] codes
-    const uint8_t* As;   // [M_cap, K/32] scales
-    const uint8_t* B;    // [E, N, K] codes (W2_e^T)
-    const uint8_t* Bs;   // [E, N, K/32] scales
+    const uint8_t* A;    // codes: [M_cap, K] (ragged M) or [M, ld] (ragged K)
+    const uint8_t* As;   // scales, one byte per 32 codes of a row
+    const uint8_t* B;    // codes: [E, N, K] (ragged M) or [N, ld] (ragged K)
+    const uint8_t* Bs;
     const int32_t* offsets;
-    int E, N, K;
-    uint16_t* out;       // [M_cap, N] bf16
+    int E, M, N, K;      // ragged K: M unused by ragged M; K unused by ragged K
+    int64_t ld;          // ragged K: bytes per code row (M_cap)
+    uint16_t* out;       // ragged M: [M_cap, N] bf16
+    float* outf;         // ragged K: [E, M, N] fp32
 };
 
 constexpr int MBK = 128;  // K bytes per LDS slab
 constexpr int kMxLoads = BM * MBK / (kThreads * 16);
 
-// Persistent like the bf16 grouped GEMM: one workgroup per compute unit walks
-// the XCD-aware tile order and fetches the next tile's first slab (codes and
-// scales) during the current tile's last one.
-__global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
+// Persistent: one workgroup per compute unit walks the tile order and fetches
+// the next tile's first slab (codes and scales) during the current tile's
+// last one. Ragged K takes the experts by descending row count, so the long
+// tiles start first.
+template <bool RAGGED_K>
+__global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][(BM + BN) * MBK];
     __shared__ int s_tiles[MOE_MAX_E + 1];
+    __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / (kWaves / 2), wn = wave % (kWaves / 2);  // 2 x (kWaves / 2) wavefront grid
     const int h = lane >> 5;
     const int ntn = (p.N + BN - 1) / BN;
-    const int KB = p.K / 32;  // scale blocks per row
-    const int nk = p.K / MBK;
-    const int mtiles = ragged_m_prefix(p.offsets, p.E, s_tiles);
-    const int total = mtiles * ntn;
+    const int ntm = RAGGED_K ? (p.M + BM - 1) / BM : 0;
+    const int64_t rowb = RAGGED_K ? p.ld : (int64_t)p.K;  // bytes per code row
+    const int KB = (int)(rowb / 32);                         // scale bytes per row
+    int total;
+    if constexpr (!RAGGED_K) {
+        total = ragged_m_prefix(p.offsets, p.E, s_tiles) * ntn;
+    } else {
+        for (int i = tid; i < p.E; i += kThreads) s_rows[i] = p.offsets[i + 1] - p.offsets[i];
+        __syncthreads();
+        for (int i = tid; i < p.E; i += kThreads) {
+            const int ri = s_rows[i];
+            int rank = 0;
+            for (int j = 0; j < p.E; ++j) {
+                const int rj = s_rows[j];
+                rank += (rj > ri) || (rj == ri && j < i);
+            }
+            s_tiles[rank] = i;
+        }
+        __syncthreads();
+        total = p.E * ntm * ntn;
+    }
     const int nb = gridDim.x;  // a multiple of 8
     auto logical = [&](int round) -> int {
         const int b = blockIdx.x;
         return round * nb + (b & 7) * (nb >> 3) + (b >> 3);
     };
-    auto get_tile = [&](int t) -> RaggedTile {
-        RaggedTile r = ragged_m_decode(p.offsets, p.E, ntn, mtiles, s_tiles, t);
-        r.e = __builtin_amdgcn_readfirstlane(r.e);
-        r.row0 = __builtin_amdgcn_readfirstlane(r.row0);
-        r.row_end = __builtin_amdgcn_readfirstlane(r.row_end);
-        r.n0 = __builtin_amdgcn_readfirstlane(r.n0);
-        return r;
+    struct Tile {
+        int e, row0, row_end, m0, n0, k_begin, nk;
     };
-    // operand regions of a tile: codes and scales, rows past the region read 0
+    auto get_tile = [&](int t) -> Tile {
+        Tile tl;
+        if constexpr (!RAGGED_K) {
+            const RaggedTile r = ragged_m_decode(p.offsets, p.E, ntn, total / ntn, s_tiles, t);
+            tl.e = __builtin_amdgcn_readfirstlane(r.e);
+            tl.row0 = __builtin_amdgcn_readfirstlane(r.row0);
+            tl.row_end = __builtin_amdgcn_readfirstlane(r.row_end);
+            tl.n0 = __builtin_amdgcn_readfirstlane(r.n0);
+            tl.m0 = 0;
+            tl.k_begin = 0;
+            tl.nk = p.K / MBK;
+        } else {
+            const int per = ntm * ntn;
+            const int slot = t / per;
+            const int r = t - slot * per;
+            tl.e = __builtin_amdgcn_readfirstlane(s_tiles[slot]);
+            tl.m0 = (r / ntn) * BM;
+            tl.n0 = (r % ntn) * BN;
+            tl.row0 = tl.row_end = 0;
+            tl.k_begin = __builtin_amdgcn_readfirstlane(p.offsets[tl.e]);
+            tl.nk = (__builtin_amdgcn_readfirstlane(p.offsets[tl.e + 1]) - tl.k_begin) / MBK;
+        }
+        return tl;
+    };
+    // operand regions of a tile: codes and scales; rows past the region (ragged
+    // M) or past M and N read as 0
     struct MxSrc {
         const uint8_t *a, *b, *as, *bs;
         uint32_t a_bytes, b_bytes, as_bytes, bs_bytes;
     };
-    auto make_src = [&](const RaggedTile& t) -> MxSrc {
+    auto make_src = [&](const Tile& t) -> MxSrc {
         MxSrc s;
-        s.a = p.A + (int64_t)t.row0 * p.K;
-        s.a_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * p.K);
-        s.b = p.B + ((int64_t)t.e * p.N + t.n0) * p.K;
-        s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * p.K);
-        s.as = p.As + (int64_t)t.row0 * KB;
-        s.as_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * KB);
-        s.bs = p.Bs + ((int64_t)t.e * p.N + t.n0) * KB;
-        s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB);
+        if constexpr (!RAGGED_K) {
+            s.a = p.A + (int64_t)t.row0 * p.K;
+            s.a_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * p.K);
+            s.b = p.B + ((int64_t)t.e * p.N + t.n0) * p.K;
+            s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * p.K);
+            s.as = p.As + (int64_t)t.row0 * KB;
+            s.as_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * KB);
+            s.bs = p.Bs + ((int64_t)t.e * p.N + t.n0) * KB;
+            s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB);
+        } else {
+            const int kb = t.k_begin / 32;
+            s.a = p.A + (int64_t)t.m0 * rowb + t.k_begin;
+            s.a_bytes = (uint32_t)((int64_t)(p.M - t.m0) * rowb - t.k_begin);
+            s.b = p.B + (int64_t)t.n0 * rowb + t.k_begin;
+            s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * rowb - t.k_begin);
+            s.as = p.As + (int64_t)t.m0 * KB + kb;
+            s.as_bytes = (uint32_t)((int64_t)(p.M - t.m0) * KB - kb);
+            s.bs = p.Bs + (int64_t)t.n0 * KB + kb;
+            s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB - kb);
+        }
         return s;
     };
     // this lane's source offset for copy 0 of a slab; copy i adds 64 rows
     const int q0 = wave * 64 + lane;
-    const uint32_t off0 = (uint32_t)((q0 >> 3) * p.K + (((q0 & 7) ^ kmaj_swz(q0 >> 3)) * 16));
-    const uint32_t istep = (uint32_t)(kThreads / 8 * p.K);
+    const uint32_t off0 = (uint32_t)((q0 >> 3) * rowb + (((q0 & 7) ^ kmaj_swz(q0 >> 3)) * 16));
+    const uint32_t istep = (uint32_t)(kThreads / 8 * rowb);
     auto issue = [&](const MxSrc& s, int kt, int buf) {
         const uint32_t l0 = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_ab[buf][0]) + wave * 1024;
         const uint32_t o = off0 + (uint32_t)kt * MBK;
@@ -220,12 +279,14 @@ __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
     int round = 0;
     int t = logical(0);
     if (t >= total) return;
-    RaggedTile tl = get_tile(t);
+    Tile tl = get_tile(t);
     MxSrc src = make_src(tl);
     uint32_t sa[4], sb[TNW], na[4], nb_[TNW];
-    issue(src, 0, 0);
-    load_scales(src, 0, na, nb_);
-    int buf0 = 0;
+    if (tl.nk > 0) {
+        issue(src, 0, 0);
+        load_scales(src, 0, na, nb_);
+    }
+    int buf0 = 0;  // LDS buffer holding slab 0 of the current tile
     f32x16_t acc[4][TNW];
     for (;;) {
 #pragma unroll
@@ -234,89 +295,127 @@ __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
             for (int j = 0; j < TNW; ++j) acc[i][j] = (f32x16_t){};
         const int tn = logical(round + 1);
         const bool have_next = tn < total;
-        RaggedTile tl_next = tl;
+        Tile tl_next = tl;
         MxSrc src_next = src;
+        int nk_next = 0;
         if (have_next) {
             tl_next = get_tile(tn);
             src_next = make_src(tl_next);
+            nk_next = tl_next.nk;
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        // shifted by this half-wave's block: K step ks then finds its scale
-        // in byte 0 after a further shift by 16 ks
+        const int nk = tl.nk;
+        int next_buf0 = buf0;
+        if (nk > 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            // shifted by this half-wave's block: K step ks then finds its scale
+            // in byte 0 after a further shift by 16 ks
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
+            for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = (buf0 + kt) & 1;
-            // scale loads first: any wait the compiler places on their
-            // registers then precedes (and cannot stall on) the slab copies
-            if (kt + 1 < nk) {
-                load_scales(src, kt + 1, na, nb_);
-                issue(src, kt + 1, cur ^ 1);
-            } else if (have_next) {
-                load_scales(src_next, 0, na, nb_);
-                issue(src_next, 0, cur ^ 1);
-            }
-            const uint8_t* sA = s_ab[cur];
-            const uint8_t* sB = s_ab[cur] + BM * MBK;
-            static_for<MBK / 64>([&](auto KS) {
-                constexpr int ks = KS;
-                i32x8_t fa[4], fb[TNW];
+            for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
+            for (int kt = 0; kt < nk; ++kt) {
+                // No vector-memory load is in flight here in the steady state (the
+                // previous slab ended with a full wait), so this wait is free; it
+                // makes registers reloaded from scratch before the loop ready on
+                // entry, instead of the compiler waiting for them inside the loop,
+                // where the same counter also tracks the slab copies.
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                const int cur = (buf0 + kt) & 1;
+                // scale loads first: any wait the compiler places on their
+                // registers then precedes (and cannot stall on) the slab copies
+                if (kt + 1 < nk) {
+                    load_scales(src, kt + 1, na, nb_);
+                    issue(src, kt + 1, cur ^ 1);
+                } else if (nk_next > 0) {
+                    load_scales(src_next, 0, na, nb_);
+                    issue(src_next, 0, cur ^ 1);
+                }
+                const uint8_t* sA = s_ab[cur];
+                const uint8_t* sB = s_ab[cur] + BM * MBK;
+                static_for<MBK / 64>([&](auto KS) {
+                    constexpr int ks = KS;
+                    i32x8_t fa[4], fb[TNW];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fa[i] = frag(sA, wm * 128 + 32 * i, ks);
+                    for (int i = 0; i < 4; ++i) fa[i] = frag(sA, wm * 128 + 32 * i, ks);
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks);
-                __builtin_amdgcn_s_setprio(1);
-                static_for<4>([&](auto I) {
-                    static_for<TNW>([&](auto J) {
-                        // the instruction reads byte 0 of each scale register, so the
-                        // block of this K step is shifted there (OPSEL stays 0)
-                        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
-                            (int)(sa[I] >> (16 * ks)));
+                    for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks);
+                    __builtin_amdgcn_s_setprio(1);
+                    static_for<4>([&](auto I) {
+                        static_for<TNW>([&](auto J) {
+                            // the instruction reads byte 0 of each scale register, so the
+                            // block of this K step is shifted there (OPSEL stays 0)
+                            acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
+                                (int)(sa[I] >> (16 * ks)));
+                        });
                     });
+                    __builtin_amdgcn_s_setprio(0);
                 });
-                __builtin_amdgcn_s_setprio(0);
-            });
-            // Pin the MFMAs here: left alone, the compiler sinks them below the
-            // barrier that waits for the next slab's copies (they touch no
-            // memory), which serialises that wait with the multiply.
+                // Pin the MFMAs here: left alone, the compiler sinks them below the
+                // barrier that waits for the next slab's copies (they touch no
+                // memory), which serialises that wait with the multiply.
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) asm volatile("" : "+v"(acc[i][j]));
-            if (kt + 1 < nk) {
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
+                    for (int j = 0; j < TNW; ++j) asm volatile("" : "+v"(acc[i][j]));
+                if (kt + 1 < nk) {
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
+                    for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * h);
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
+                    for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * h);
+                } else {
+                    next_buf0 = cur ^ 1;
+                }
             }
+        } else if (nk_next > 0) {
+            // nothing to multiply (an empty expert): the buffer this tile would
+            // have used takes the next tile's first slab
+            load_scales(src_next, 0, na, nb_);
+            issue(src_next, 0, buf0);
         }
-        // epilogue: bf16 Y, lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
-        const int rbase = tl.row0 + wm * 128 + (lane & 31);
-        static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
-            if (m < tl.row_end) {
-                static_for<TNW>([&](auto J) {
-                    if (tl.n0 + wn * WN + 32 * J < p.N) {
+        // epilogue: lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
+        if constexpr (!RAGGED_K) {
+            const int rbase = tl.row0 + wm * 128 + (lane & 31);
+            static_for<4>([&](auto I) {
+                const int m = rbase + 32 * I;
+                if (m < tl.row_end) {
+                    static_for<TNW>([&](auto J) {
+                        if (tl.n0 + wn * WN + 32 * J < p.N) {
+                            static_for<4>([&](auto Q) {
+                                const int c = tl.n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
+                                uint2 v;
+                                v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                                v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                                *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
+                            });
+                        }
+                    });
+                }
+            });
+        } else {
+            float* o = p.outf + (int64_t)tl.e * p.M * p.N;
+            const int rbase = tl.m0 + wm * 128 + (lane & 31);
+            static_for<4>([&](auto I) {
+                const int m = rbase + 32 * I;
+                if (m < p.M) {
+                    static_for<TNW>([&](auto J) {
                         static_for<4>([&](auto Q) {
                             const int c = tl.n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
-                            uint2 v;
-                            v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
-                            v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
-                            *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
+                            if (c < p.N)
+                                *(float4*)(o + (int64_t)m * p.N + c) =
+                                    make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
+                                                acc[I][J][4 * Q + 3]);
                         });
-                    }
-                });
-            }
-        });
+                    });
+                }
+            });
+        }
         if (!have_next) break;
         ++round;
-        buf0 = (buf0 + nk) & 1;
+        buf0 = next_buf0;
         tl = tl_next;
         src = src_next;
     }
@@ -325,11 +424,34 @@ __global__ void __launch_bounds__(kThreads, 1) mx_fc2_kernel(MxArgs p) {
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
                   const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
                   hipStream_t s) {
+    return launch_mx_ragged_m(a_q, a_s, w2t_q, w2t_s, offsets, E, d, n, M_cap, y, s);
+}
+
+int launch_mx_ragged_m(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                       const int32_t* offsets, int E, int N, int K, int64_t M_cap, uint16_t* out,
+                       hipStream_t s) {
     MxArgs a;
-    a.A = a_q; a.As = a_s; a.B = w2t_q; a.Bs = w2t_s;
-    a.offsets = offsets; a.E = E; a.N = d; a.K = n;
-    a.out = y;
-    mx_fc2_kernel<<<persistent_grid(ragged_m_grid(M_cap, E, d)), kThreads, 0, s>>>(a);
+    __builtin_memset(&a, 0, sizeof(a));
+    a.A = a_q; a.As = a_s; a.B = b_q; a.Bs = b_s;
+    a.offsets = offsets; a.E = E; a.N = N; a.K = K; a.ld = K;
+    a.out = out;
+    const int64_t tb = ragged_m_grid(M_cap, E, N);
+    if (tb <= 0) return 0;
+    mx_gemm_kernel<false><<<persistent_grid(tb), kThreads, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_mx_wgrad(const uint8_t* at_q, const uint8_t* at_s, int M, const uint8_t* bt_q,
+                    const uint8_t* bt_s, int N, const int32_t* offsets, int E, int64_t M_cap,
+                    float* out, hipStream_t s) {
+    MxArgs a;
+    __builtin_memset(&a, 0, sizeof(a));
+    a.A = at_q; a.As = at_s; a.B = bt_q; a.Bs = bt_s;
+    a.offsets = offsets; a.E = E; a.M = M; a.N = N; a.ld = M_cap;
+    a.outf = out;
+    const int64_t tb = (int64_t)E * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tb <= 0) return 0;
+    mx_gemm_kernel<true><<<persistent_grid(tb), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -77,4 +77,81 @@ __device__ __forceinline__ uint32_t e4m3_hw(float y) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xffu;
 }
 
+// two bf16 magnitudes (or other 16-bit fields) per register
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
+}
+
+// The value of lane l ^ M inside each 32-lane half (M = 1, 2, 4, 8, 16): DPP
+// quad permutes for 1 and 2, a rotation of the 16-lane row by 8 for 8, and a
+// bit-mask ds_swizzle (and 0x1f, xor M) for 4 and 16.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+    else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+    else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
+    else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (M << 10));
+}
+
+// Column-wise MXFP8 blocks of one 32 x 32 block held the MFMA way: lane l has
+// row l & 31 and, in 16-bit slot j of pk[j / 2] (bf16 bits), column
+// 8 (j / 4) + 4 h + j % 4 with h = l / 32. The 32-row maxima come from a
+// transposing butterfly inside each half: every exchange pairs lanes whose
+// rows differ in one bit and halves the slots a lane carries (it keeps the
+// half its partner sends), so after the exchanges across row bits 4..1 lane
+// pair (2i, 2i + 1) carries slot i, and one more exchange finishes its
+// maximum (9 exchanges for 16 columns instead of 5 per column). The E8M0
+// codes travel back the same way. Codes go to q[c * ldq + row], the scale of
+// column c to sc[c * lds] (each lane of a pair stores the same byte).
+__device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_t* q, int64_t ldq,
+                                          uint8_t* sc, int64_t lds) {
+    const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+    const int h = (lane >> 5) & 1;
+    uint32_t t1[4], t2[2];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {  // rows r, r ^ 16: slots 2p, 2p + 1 (+ 8 b4)
+        const uint32_t lo = pk[p] & 0x7fff7fffu, hi = pk[p + 4] & 0x7fff7fffu;
+        t1[p] = max_u16x2(b4 ? hi : lo, xor_lane<16>(b4 ? lo : hi));
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)  // slots 2p, 2p + 1 (+ 4 b3 + 8 b4)
+        t2[p] = max_u16x2(b3 ? t1[p + 2] : t1[p], xor_lane<8>(b3 ? t1[p] : t1[p + 2]));
+    // slots 0, 1 (+ 2 b2 + 4 b3 + 8 b4)
+    const uint32_t t3 = max_u16x2(b2 ? t2[1] : t2[0], xor_lane<4>(b2 ? t2[0] : t2[1]));
+    // slot i = b1 + 2 b2 + 4 b3 + 8 b4
+    uint32_t t4 = max(b1 ? t3 >> 16 : t3 & 0xffffu, xor_lane<2>(b1 ? t3 & 0xffffu : t3 >> 16));
+    t4 = max(t4, xor_lane<1>(t4));
+    const uint32_t ec = (uint32_t)(mx_block_exp(t4) + 127);
+    const int i = (lane >> 1) & 15;
+    sc[(int64_t)(8 * (i >> 2) + 4 * h + (i & 3)) * lds] = (uint8_t)ec;
+    // codes back to every slot: w0[p] holds slots 2p, 2p + 1
+    uint32_t o = xor_lane<2>(ec);
+    const uint32_t w3 = b1 ? (o | (ec << 16)) : (ec | (o << 16));
+    o = xor_lane<4>(w3);
+    const uint32_t w2[2] = {b2 ? o : w3, b2 ? w3 : o};
+    uint32_t w1[4], w0[8];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        o = xor_lane<8>(w2[p]);
+        w1[p] = b3 ? o : w2[p];
+        w1[p + 2] = b3 ? w2[p] : o;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        o = xor_lane<16>(w1[p]);
+        w0[p] = b4 ? o : w1[p];
+        w0[p + 4] = b4 ? w1[p] : o;
+    }
+    const int row = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t ecj = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        const float inv = __uint_as_float((254u - ecj) << 23);  // 2^-(ecj - 127)
+        const float x = (j & 1) ? bf16_hi(pk[j >> 1]) : bf16_lo(pk[j >> 1]);
+        q[(int64_t)(8 * (j >> 2) + 4 * h + (j & 3)) * ldq + row] = (uint8_t)e4m3_hw(x * inv);
+    }
+}
+
 }  // namespace moe

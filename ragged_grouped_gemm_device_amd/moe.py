@@ -56,7 +56,7 @@ SIGNATURES = {
     "moe_grouped_mlp_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I, C.c_uint, _P, _P, _P,
                                  _P, _P]),
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I,
-                                 C.c_uint, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                 C.c_uint, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quant_mxfp8": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _P]),
 }
 
@@ -69,6 +69,14 @@ class MoEError(RuntimeError):
 
 class moe_mx_fwd(C.Structure):
     _fields_ = [("a_q", _P), ("a_s", _P), ("at_q", _P), ("at_s", _P), ("w2t_q", _P), ("w2t_s", _P)]
+
+
+MX_BWD_FIELDS = ("dh_q", "dh_s", "dht_q", "dht_s", "awt_q", "awt_s", "dyt_q", "dyt_s", "xt_q", "xt_s",
+                 "w1_q", "w1_s")
+
+
+class moe_mx_bwd(C.Structure):
+    _fields_ = [(name, _P) for name in MX_BWD_FIELDS]
 
 
 _LIB = None
@@ -173,8 +181,14 @@ def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD,
 
 
 def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets, dh, a_w, ds,
-                        dx_perm, dw1, dw2, workspace, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU):
-    E, d, n2 = w1.shape
+                        dx_perm, dw1, dw2, workspace, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU,
+                        mx=None, shape=None):
+    """mx: dict of the moe_mx_bwd fields (missing ones pass NULL). shape = (E, d, n) when w1
+    is not given (an MX call that reads only the quantized copies)."""
+    E, d, n2 = w1.shape if w1 is not None else (shape[0], shape[1], 2 * shape[2])
+    mxp = None
+    if mx is not None:
+        mxp = C.byref(moe_mx_bwd(*[_ptr(mx.get(key)) for key in MX_BWD_FIELDS]))
     T, k = topk_w.shape
     M_cap = src_of.shape[0]
     rc = _lib().moe_grouped_mlp_bwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(h), _ptr(dy_u),
@@ -182,7 +196,7 @@ def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets
                                     E, d, n2 // 2, M_cap, act, stages, _ptr(dh), _ptr(a_w), _ptr(ds),
                                     _ptr(dx_perm), _ptr(dw1), _ptr(dw2), _ptr(workspace),
                                     0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                    _stream())
+                                    mxp, _stream())
     _check("moe_grouped_mlp_bwd", rc)
 
 
@@ -235,6 +249,31 @@ class Buffers:
             self.at_s = torch.empty(n, M // 32, dtype=u8, device=dev)
             self.w2t_q = torch.empty(E, d, n, dtype=u8, device=dev)
             self.w2t_s = torch.empty(E, d, n // 32, dtype=u8, device=dev)
+            self.dh_q = torch.empty(M, 2 * n, dtype=u8, device=dev)
+            self.dh_s = torch.empty(M, 2 * n // 32, dtype=u8, device=dev)
+            self.dht_q = torch.empty(2 * n, M, dtype=u8, device=dev)
+            self.dht_s = torch.empty(2 * n, M // 32, dtype=u8, device=dev)
+            self.awt_q = torch.empty(n, M, dtype=u8, device=dev)
+            self.awt_s = torch.empty(n, M // 32, dtype=u8, device=dev)
+            self.dyt_q = torch.empty(d, M, dtype=u8, device=dev)
+            self.dyt_s = torch.empty(d, M // 32, dtype=u8, device=dev)
+            self.xt_q = torch.empty(d, M, dtype=u8, device=dev)
+            self.xt_s = torch.empty(d, M // 32, dtype=u8, device=dev)
+            self.w1_q = torch.empty(E, d, 2 * n, dtype=u8, device=dev)
+            self.w1_s = torch.empty(E, d, 2 * n // 32, dtype=u8, device=dev)
+
+    def quantize_weights(self, w1, w2):
+        """MXFP8 weight copies: W2_e along n, transposed [E, d, n] (FC2), and W1_e along 2n
+        [E, d, 2n] (FC1 dgrad)."""
+        moe_quant_mxfp8(w2, MOE_QUANT_COLWISE, None, None, self.w2t_q, self.w2t_s)
+        moe_quant_mxfp8(w1, MOE_QUANT_ROWWISE, self.w1_q, self.w1_s)
+
+    def mx_fwd(self):
+        return dict(a_q=self.a_q, a_s=self.a_s, at_q=self.at_q, at_s=self.at_s, w2t_q=self.w2t_q,
+                    w2t_s=self.w2t_s)
+
+    def mx_bwd(self):
+        return {key: getattr(self, key) for key in MX_BWD_FIELDS}
 
 
 def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True,
@@ -254,11 +293,22 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
 
 
 def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU, logits=None,
-             renorm=False, x=None):
+             renorm=False, x=None, mx=False):
     """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum, and with
     the forward's logits also the router backward dS -> dlogits. With x given (the un-permuted
-    input), the GEMMs read x and dO through src_of instead of permuted copies."""
-    if x is not None:
+    input), the GEMMs read x and dO through src_of instead of permuted copies. With mx (buffers
+    made with mx=True and quantize_weights done), dY_u and X_perm are quantized column-wise and
+    the last three GEMMs run on MXFP8."""
+    if mx:
+        if x is not None:
+            raise ValueError("the MXFP8 backward quantizes the permuted copies: no row gather")
+        moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
+        moe_quant_mxfp8(buf.dy_u, MOE_QUANT_COLWISE, None, None, buf.dyt_q, buf.dyt_s)
+        moe_quant_mxfp8(buf.x_perm, MOE_QUANT_COLWISE, None, None, buf.xt_q, buf.xt_s)
+        moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
+                            buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                            buf.bwd_ws, stages, act=act, mx=buf.mx_bwd())
+    elif x is not None:
         moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
                             buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
                             buf.bwd_ws, stages | MOE_GATHER_ROWS, act=act)

@@ -113,11 +113,24 @@ def test_host_validation_returns_before_launch():
     assert rc == M.MOE_ERR_INVALID_ARG              # k > E
     # mlp bwd: workspace too small for the dS partials
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x04,
-                                 f, f, f, f, f, f, f, 0, None)
+                                 f, f, f, f, f, f, f, 0, None, None)
     assert rc == M.MOE_ERR_WORKSPACE
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 256, 0, 0x04,
-                                 f, f, f, f, f, f, f, 1 << 20, None)
+                                 f, f, f, f, f, f, f, 1 << 20, None, None)
     assert rc == M.MOE_ERR_WORKSPACE               # M_cap below capacity
+    # MXFP8 backward: every copy a requested stage reads or writes must be given
+    full = {key: f for key in M.MX_BWD_FIELDS}
+    for stage, needed in ((0x04, ("dh_q", "dht_s", "awt_q")), (0x08, ("awt_s", "dyt_q")),
+                          (0x10, ("dh_s", "w1_q")), (0x20, ("xt_q", "dht_q"))):
+        for key in needed:
+            mx = M.moe_mx_bwd(*[None if k2 == key else full[k2] for k2 in M.MX_BWD_FIELDS])
+            rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, stage,
+                                         f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)
+            assert rc == M.MOE_ERR_INVALID_ARG, (stage, key)
+    mx = M.moe_mx_bwd(*[_fake(0x1001) if k2 == "w1_q" else full[k2] for k2 in M.MX_BWD_FIELDS])
+    rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x10,
+                                 f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)
+    assert rc == M.MOE_ERR_INVALID_ARG             # misaligned codes
     # quant: bad mode / shape
     rc = lib.moe_quant_mxfp8(f, 1, 64, 64, 0, f, f, f, f, None)
     assert rc == M.MOE_ERR_INVALID_ARG

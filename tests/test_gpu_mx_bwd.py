@@ -1,0 +1,163 @@
+"""GPU parity of the MXFP8 backward: the dGLU epilogue's fused quantization,
+the MX-scaled FC1 dgrad and the two MX-scaled ragged wgrads.
+
+* DGRAD2 stays bf16: dH, A' and dS within 2e-2 of the oracle (as the bf16 path).
+* Its fused MXFP8 copies equal the standalone quantization kernel's codes of
+  the same bf16 dH and A' (bit-exact; that kernel is pinned to the oracle),
+  and the column-wise dY_u / X_perm copies and row-wise W1 copy equal the
+  oracle's quantization of the (bit-exact) permuted inputs.
+* The three MX GEMMs on the GPU's own codes: dW1 and dW2 within 1e-3 of the
+  fp64 block-scaled product of those codes, dX_perm within 1e-2 (one bf16
+  rounding). The scaled MFMA is not exact-products-plus-fp32-sum: on random
+  codes it lands about 7e-5 (max-abs-normalised) from the fp64 product, far
+  above fp32 summation error, so the bound leaves a 10x margin over that.
+* End to end against the oracle's MXFP8 backward from the same seeded inputs:
+  within 6e-2 (the codes on the two sides may differ where dH rounds
+  differently in bf16). Empty experts: dW exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from ragged_grouped_gemm_device_amd import workloads as W
+
+from ._util import bf16_bits, bf16_tensor, bf16_values, f32_tensor, rel_err
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    W.small("mxb-small", T=600, k=2, E=4, d=256, n=256, seed=41, routing="zipf"),
+    W.small("mxb-ragged", T=700, k=3, E=6, d=192, n=320, seed=21, routing="zipf"),
+    W.small("mxb-empty", T=300, k=2, E=16, d=256, n=128, seed=22, routing="zipf"),
+    W.small("mxb-wide", T=1200, k=2, E=4, d=640, n=384, seed=23),
+]
+
+
+@pytest.fixture(scope="module")
+def M():
+    from ragged_grouped_gemm_device_amd import moe
+    moe.load()
+    return moe
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _run_gpu(M, wl, inp, act):
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
+    for name in ("dh", "a_w", "ds", "dx_perm", "dx", "dw1", "dw2"):
+        getattr(buf, name).fill_(float("nan"))
+    for name in M.MX_BWD_FIELDS:
+        getattr(buf, name).fill_(0xAB)
+    x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
+    logits, dout = f32_tensor(inp["logits"]), bf16_tensor(inp["dout"])
+    buf.quantize_weights(w1, w2)
+    M.forward(buf, x, logits, w1, w2, act=act)
+    M.backward(buf, dout, w1, w2, act=act, mx=True)
+    torch.cuda.synchronize()
+    return buf
+
+
+def _gpu_quant(M, t, mode):
+    """Standalone quantization kernel on a bf16 device matrix [R, C]."""
+    R, C = t.shape
+    U8 = torch.uint8
+    q_row = torch.empty(R, C, dtype=U8, device="cuda") if mode & 1 else None
+    s_row = torch.empty(R, C // 32, dtype=U8, device="cuda") if mode & 1 else None
+    q_col = torch.empty(C, R, dtype=U8, device="cuda") if mode & 2 else None
+    s_col = torch.empty(C, R // 32, dtype=U8, device="cuda") if mode & 2 else None
+    M.moe_quant_mxfp8(t.contiguous(), mode, q_row, s_row, q_col, s_col)
+    torch.cuda.synchronize()
+    return [None if v is None else _np(v) for v in (q_row, s_row, q_col, s_col)]
+
+
+def _check(name, got, ref, tol):
+    assert np.isfinite(got).all(), f"{name}: unwritten (NaN) or non-finite elements"
+    err = rel_err(got, ref)
+    print(f"  {name}: max-abs-normalised error {err:.3e}", flush=True)
+    assert err <= tol, f"{name}: {err}"
+
+
+@pytest.mark.parametrize("wl,act", [(c, "swiglu") for c in CASES] + [(CASES[1], "geglu")],
+                         ids=[c.name for c in CASES] + [CASES[1].name + "-geglu"])
+def test_mx_backward_parity(M, wl, act):
+    print(f"mx backward case {wl} act={act}", flush=True)
+    inp = W.make_inputs(wl)
+    buf = _run_gpu(M, wl, inp, M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
+    x, w1, w2 = O.from_bf16(inp["x"]), O.from_bf16(inp["w1"]), O.from_bf16(inp["w2"])
+    f = O.forward(x, inp["logits"], w1, w2, wl.k, act=act)
+    b = O.mlp_backward_mx(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"]), f["topk_w"],
+                          f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k, act=act)
+    offsets = f["offsets"]
+    end = int(offsets[-1])
+    assert np.array_equal(_np(buf.offsets), offsets)
+
+    # DGRAD2 (bf16) as in the bf16 path
+    _check("dS", _np(buf.ds), b["dS"], 2e-2)
+    _check("dH", bf16_values(buf.dh)[:end], b["dH"][:end], 2e-2)
+    _check("A'", bf16_values(buf.a_w)[:end], b["a_w"][:end], 2e-2)
+
+    # fused copies == standalone quantization of the same bf16 tensors
+    g = _gpu_quant(M, buf.dh[:end], 3)
+    assert np.array_equal(_np(buf.dh_q)[:end], g[0]), "dH row codes"
+    assert np.array_equal(_np(buf.dh_s)[:end], g[1]), "dH row scales"
+    assert np.array_equal(_np(buf.dht_q)[:, :end], g[2]), "dH column codes"
+    assert np.array_equal(_np(buf.dht_s)[:, :end // 32], g[3]), "dH column scales"
+    g = _gpu_quant(M, buf.a_w[:end], 2)
+    assert np.array_equal(_np(buf.awt_q)[:, :end], g[2]), "A' column codes"
+    assert np.array_equal(_np(buf.awt_s)[:, :end // 32], g[3]), "A' column scales"
+    # quantized inputs == the oracle's quantization of the same bf16 values
+    assert np.array_equal(_np(buf.dyt_q)[:, :end], b["dyt_q"]) and np.array_equal(
+        _np(buf.dyt_s)[:, :end // 32], b["dyt_s"]), "dY_u column copy"
+    assert np.array_equal(_np(buf.xt_q)[:, :end], b["xt_q"]) and np.array_equal(
+        _np(buf.xt_s)[:, :end // 32], b["xt_s"]), "X_perm column copy"
+    assert np.array_equal(_np(buf.w1_q), b["w1q"]) and np.array_equal(_np(buf.w1_s), b["w1s"]), "W1 copy"
+
+    # the MX GEMMs on the GPU's own codes
+    dht_d = O.mx_dequant(_np(buf.dht_q)[:, :end], _np(buf.dht_s)[:, :end // 32])
+    awt_d = O.mx_dequant(_np(buf.awt_q)[:, :end], _np(buf.awt_s)[:, :end // 32])
+    xt_d = O.mx_dequant(b["xt_q"], b["xt_s"])
+    dyt_d = O.mx_dequant(b["dyt_q"], b["dyt_s"])
+    dW1 = np.zeros(w1.shape)
+    dW2 = np.zeros(w2.shape)
+    dxp = np.zeros((end, wl.d))
+    for e in range(wl.E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            dW1[e] = xt_d[:, r0:r1] @ dht_d[:, r0:r1].T
+            dW2[e] = awt_d[:, r0:r1] @ dyt_d[:, r0:r1].T
+            dxp[r0:r1] = O.mx_gemm_rows(_np(buf.dh_q)[r0:r1], _np(buf.dh_s)[r0:r1], b["w1q"][e], b["w1s"][e])
+    _check("dW1 (own codes)", _np(buf.dw1), dW1, 1e-3)
+    _check("dW2 (own codes)", _np(buf.dw2), dW2, 1e-3)
+    _check("dX_perm (own codes)", bf16_values(buf.dx_perm)[:end], dxp, 1e-2)
+
+    # end to end against the oracle's MXFP8 backward
+    _check("dX_perm", bf16_values(buf.dx_perm)[:end], b["dx_perm"][:end], 6e-2)
+    _check("dX", bf16_values(buf.dx), b["dx"], 6e-2)
+    _check("dW1", _np(buf.dw1), b["dW1"], 6e-2)
+    _check("dW2", _np(buf.dw2), b["dW2"], 6e-2)
+    pad = f["src_of"][:end] < 0
+    v = bf16_bits(buf.dx_perm)[:end][pad]
+    assert np.all((v == 0) | (v == 0x8000)), "padding rows of dX_perm"
+    for e in np.nonzero(f["counts"] == 0)[0]:
+        assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
+
+
+def test_mx_wgrad_all_tokens_to_one_expert(M):
+    """One expert takes every row, the rest are empty: the longest ragged-K
+    tiles and many zero-K tiles in one launch."""
+    wl = W.small("mxb-one", T=520, k=1, E=8, d=128, n=128, seed=31)
+    inp = W.make_inputs(wl)
+    inp["logits"][:] = 0.0                     # ties everywhere -> expert 0
+    buf = _run_gpu(M, wl, inp, M.MOE_ACT_SWIGLU)
+    x, w1, w2 = O.from_bf16(inp["x"]), O.from_bf16(inp["w1"]), O.from_bf16(inp["w2"])
+    f = O.forward(x, inp["logits"], w1, w2, wl.k)
+    b = O.mlp_backward_mx(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"]), f["topk_w"],
+                          f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k)
+    assert list(_np(buf.counts)) == [520, 0, 0, 0, 0, 0, 0, 0]
+    _check("dX", bf16_values(buf.dx), b["dx"], 6e-2)
+    _check("dW1", _np(buf.dw1), b["dW1"], 6e-2)
+    _check("dW2", _np(buf.dw2), b["dW2"], 6e-2)
+    assert torch.all(buf.dw1[1:] == 0) and torch.all(buf.dw2[1:] == 0)
