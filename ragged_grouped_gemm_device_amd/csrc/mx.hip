@@ -145,6 +145,9 @@ constexpr int kMxLoads = BM * MBK / (kThreads * 16);
 template <bool RAGGED_K>
 __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_ab[2][(BM + BN) * MBK];
+    // block scales of 4 consecutive slabs (a group): 16 bytes for each of the
+    // BM A rows then the BN B rows, double-buffered by group
+    __shared__ __attribute__((aligned(1024))) uint8_t s_sc[2][(BM + BN) * 16];
     __shared__ int s_tiles[MOE_MAX_E + 1];
     __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -248,21 +251,28 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
 #pragma unroll
         for (int i = 0; i < kMxLoads; ++i) lds_copy16(rb, l0 + BM * MBK + i * kWaves * 1024, o + i * istep);
     };
-    // per-lane scale words: the 4 K blocks of one slab for this lane's rows
-    // and columns (raw: they are consumed only after the slab barrier, so the
-    // loads wait no earlier than the slab copies issued before them)
-    auto load_scales = [&](const MxSrc& s, int kt, uint32_t* sa, uint32_t* sb) {
-        const __amdgpu_buffer_rsrc_t ras = make_rsrc(s.as, s.as_bytes), rbs = make_rsrc(s.bs, s.bs_bytes);
+    // Block scales travel by group of 4 slabs: one 16-byte copy per A row and
+    // per B row (wavefronts 0-3 the A rows, 4-7 the B rows) straight into LDS.
+    // Loading each lane's slab word from global memory instead touched one
+    // cache line per row, per slab and per wavefront, and cost a third of the
+    // kernel's time. Bytes past a row's valid K read whatever follows (or 0
+    // past the region) and are never used.
+    auto issue_scales = [&](const MxSrc& s, int g, int sbuf) {
+        const bool a_side = wave < kWaves / 2;
+        const int row = (wave % (kWaves / 2)) * 64 + lane;
+        const i32x4_t r = a_side ? rsrc_words(s.as, s.as_bytes) : rsrc_words(s.bs, s.bs_bytes);
+        const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_sc[sbuf][0]) + wave * 1024;
+        lds_copy16(r, l, (uint32_t)(row * KB + g * 16));
+    };
+    // this lane's scale words of slab kt4 (0..3) of the group in buffer sbuf:
+    // the 4 K blocks of the slab for its rows (A) and columns (B)
+    auto read_scales = [&](int sbuf, int kt4, uint32_t* sa, uint32_t* sb) {
+        const uint8_t* base = s_sc[sbuf] + kt4 * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 128 + 32 * i + (lane & 31);
-            sa[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ras, (uint32_t)(r * KB + kt * 4), 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(base + (wm * 128 + 32 * i + (lane & 31)) * 16);
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) {
-            const int c = wn * WN + 32 * j + (lane & 31);
-            sb[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbs, (uint32_t)(c * KB + kt * 4), 0, 0);
-        }
+        for (int j = 0; j < TNW; ++j)
+            sb[j] = *(const uint32_t*)(base + (BM + wn * WN + 32 * j + (lane & 31)) * 16);
     };
     // Operand fragment of row `base + (lane & 31)` for K step ks (64 bytes = K
     // blocks 2ks and 2ks+1): the instruction reads a lane's first 16 bytes as
@@ -284,9 +294,10 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     uint32_t sa[4], sb[TNW], na[4], nb_[TNW];
     if (tl.nk > 0) {
         issue(src, 0, 0);
-        load_scales(src, 0, na, nb_);
+        issue_scales(src, 0, 0);
     }
     int buf0 = 0;  // LDS buffer holding slab 0 of the current tile
+    int sg0 = 0;   // scale buffer holding group 0 of the current tile
     f32x16_t acc[4][TNW];
     for (;;) {
 #pragma unroll
@@ -304,10 +315,12 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
             nk_next = tl_next.nk;
         }
         const int nk = tl.nk;
+        const int ng = (nk + 3) / 4;  // scale groups of this tile
         int next_buf0 = buf0;
         if (nk > 0) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+            read_scales(sg0, 0, na, nb_);
             // shifted by this half-wave's block: K step ks then finds its scale
             // in byte 0 after a further shift by 16 ks
 #pragma unroll
@@ -322,15 +335,18 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                 // where the same counter also tracks the slab copies.
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 const int cur = (buf0 + kt) & 1;
-                // scale loads first: any wait the compiler places on their
-                // registers then precedes (and cannot stall on) the slab copies
                 if (kt + 1 < nk) {
-                    load_scales(src, kt + 1, na, nb_);
                     issue(src, kt + 1, cur ^ 1);
                 } else if (nk_next > 0) {
-                    load_scales(src_next, 0, na, nb_);
                     issue(src_next, 0, cur ^ 1);
+                    issue_scales(src_next, 0, (sg0 + ng) & 1);
                 }
+                // the next group's scales, into the buffer the previous group
+                // left (its last reads ended before the previous slab barrier)
+                if ((kt & 3) == 0 && kt + 4 < nk) issue_scales(src, kt / 4 + 1, (sg0 + kt / 4 + 1) & 1);
+                // the next slab's scale words: its group landed at least one
+                // slab barrier ago
+                if (kt + 1 < nk) read_scales((sg0 + (kt + 1) / 4) & 1, (kt + 1) & 3, na, nb_);
                 const uint8_t* sA = s_ab[cur];
                 const uint8_t* sB = s_ab[cur] + BM * MBK;
                 static_for<MBK / 64>([&](auto KS) {
@@ -371,10 +387,10 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                 }
             }
         } else if (nk_next > 0) {
-            // nothing to multiply (an empty expert): the buffer this tile would
-            // have used takes the next tile's first slab
-            load_scales(src_next, 0, na, nb_);
+            // nothing to multiply (an empty expert): the buffers this tile would
+            // have used take the next tile's first slab and scale group
             issue(src_next, 0, buf0);
+            issue_scales(src_next, 0, sg0);
         }
         // epilogue: lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
         if constexpr (!RAGGED_K) {
@@ -416,6 +432,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
         if (!have_next) break;
         ++round;
         buf0 = next_buf0;
+        sg0 = (sg0 + ng) & 1;
         tl = tl_next;
         src = src_next;
     }
