@@ -328,13 +328,18 @@ def forward(x, logits, w1, w2, k: int, renorm: bool = False, rounding: bool = Tr
 # evidence section: dSwiGLU fused into the dgrad GEMM]
 # --------------------------------------------------------------------------
 def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k: int,
-                 g: int = GLU_INTERLEAVE, rounding: bool = True, act: str = "swiglu"):
+                 g: int = GLU_INTERLEAVE, rounding: bool = True, act: str = "swiglu", dap=None):
     """Manual backward of the MLP for fixed routing weights.
 
     The routing weights w are treated as inputs: dS[t,j] = dL/dw[t,j] is the
     router-weight gradient, computed on the plain side <dO_t, Y_row>. Gradients
     of x, W1 and W2 follow the chain rule with the gate/up activation taken
     from the stored H. Returns dict(dy_u, dS, dH, a_w, dx_perm, dx, dW1, dW2).
+
+    dap [M_cap, n], when given, replaces the FC2 dgrad dY_u W2_e^T (the
+    unweighted dA' of each row, e.g. from an MXFP8 GEMM); dS is then taken on
+    the rewritten side, <dA'_row, a_row> [P2 backward-rewrite section], since
+    that product is what such a dA' feeds.
     """
     x_perm = np.asarray(x_perm, dtype=np.float64)
     M_cap, d = x_perm.shape
@@ -352,6 +357,7 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
     w_row[valid] = w[src[valid]]
 
     dS = np.einsum("pd,pd->p", dout[np.arange(T * k) // k], Y[rows]).reshape(T, k)
+    ds_row = np.zeros(M_cap)
 
     dH = np.zeros((M_cap, n2))
     a_w = np.zeros((M_cap, n))
@@ -361,11 +367,12 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
     for e, r0, r1 in expert_segments(counts, offsets):
         if r1 == r0:
             continue
-        da_u = dy_u[r0:r1] @ w2[e].T                     # dA' (unweighted)
+        da_u = dy_u[r0:r1] @ w2[e].T if dap is None else dap[r0:r1]   # dA' (unweighted)
         hg, hu = deinterleave(H[r0:r1], g)
         f, f_grad = GLU_ACTS[act]
         fg = f(hg)
         a = fg * hu
+        ds_row[r0:r1] = np.einsum("rc,rc->r", da_u, a)
         da = w_row[r0:r1, None] * da_u
         dg = da * hu * f_grad(hg)
         du = da * fg
@@ -377,6 +384,8 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
         dx_perm[r0:r1] = _maybe_round(dh @ w1[e].T, rounding)
         dW1[e] = x_perm[r0:r1].T @ dh
     dx = combine(dx_perm, rows, k, None, rounding)
+    if dap is not None:
+        dS = ds_row[rows].reshape(T, k)
     return dict(dy_u=dy_u, dS=dS, dH=dH, a_w=a_w, dx_perm=dx_perm, dx=dx, dW1=dW1, dW2=dW2)
 
 
@@ -495,6 +504,63 @@ def mx_gemm_rows(a_q, a_s, bt_q, bt_s):
     return np.einsum("rcb,rb,cb->rc", partial, sa, sb)
 
 
+def mx_fc1(x_q, x_s, w1t_q, w1t_s, counts, offsets, g: int = GLU_INTERLEAVE, rounding: bool = True,
+           act: str = "swiglu"):
+    """Grouped MXFP8 FC1 with the GLU epilogue: H[R_e] = MX(X_perm[R_e]) x MX(W1_e).
+
+    x_q [M_cap, d], x_s [M_cap, d/32] (X_perm row-wise, blocks along d);
+    w1t_q [E, 2n, d], w1t_s [E, 2n, d/32] (W1_e quantized in blocks of 32
+    along d and stored transposed). As in mlp_forward, A = act(gate) * up is
+    taken from the unrounded product and H is stored rounded. Returns H, A.
+    """
+    act_fn = GLU_ACTS[act][0]
+    M_cap = x_q.shape[0]
+    E, n2, _ = w1t_q.shape
+    H = np.zeros((M_cap, n2))
+    A = np.zeros((M_cap, n2 // 2))
+    for e, r0, r1 in expert_segments(counts, offsets):
+        if r1 > r0:
+            h = mx_gemm_rows(x_q[r0:r1], x_s[r0:r1], w1t_q[e], w1t_s[e])
+            hg, hu = deinterleave(h, g)
+            A[r0:r1] = _maybe_round(act_fn(hg) * hu, rounding)
+            H[r0:r1] = _maybe_round(h, rounding)
+    return H, A
+
+
+def mlp_forward_mx(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, act: str = "swiglu",
+                   fc1_mx: bool = True):
+    """MXFP8 forward of the expert MLP [P1 core-idea section: MXFP8 output of the
+    FC1 epilogue; P3 three-components section: MXFP8 grouped GEMM].
+
+    With fc1_mx, FC1 runs on X_perm quantized row-wise (blocks along d) and W1_e
+    quantized along d (mx_fc1); otherwise FC1 is the bf16 product of
+    mlp_forward. The bf16 A is quantized row-wise and FC2 runs on it and on W2_e
+    quantized along n (mx_fc2). Returns dict(H, A, Y) and the quantized copies.
+    """
+    x_perm = np.asarray(x_perm, dtype=np.float64)
+    E = w1.shape[0]
+    end = int(offsets[-1])
+    out = {}
+    if fc1_mx:
+        x_q, x_s, _, _ = quant_mxfp8(x_perm[:end], rowwise=True, colwise=False)
+        w1t = [quant_mxfp8(w1[e], rowwise=False, colwise=True)[2:] for e in range(E)]
+        w1t_q, w1t_s = np.stack([q for q, _ in w1t]), np.stack([sc for _, sc in w1t])
+        Hm, Am = mx_fc1(x_q, x_s, w1t_q, w1t_s, counts, offsets, g, True, act)   # rows [0, end)
+        H = np.zeros((x_perm.shape[0], Hm.shape[1]))
+        A = np.zeros((x_perm.shape[0], Am.shape[1]))
+        H[:end], A[:end] = Hm, Am
+        out.update(x_q=x_q, x_s=x_s, w1t_q=w1t_q, w1t_s=w1t_s)
+    else:
+        H, A, _ = mlp_forward(x_perm, w1, w2, counts, offsets, g, True, act)
+    a_q, a_s, _, _ = quant_mxfp8(A[:end], rowwise=True, colwise=False)
+    w2t = [quant_mxfp8(w2[e], rowwise=False, colwise=True)[2:] for e in range(E)]
+    w2t_q, w2t_s = np.stack([q for q, _ in w2t]), np.stack([sc for _, sc in w2t])
+    Y = np.zeros((x_perm.shape[0], w2.shape[2]))
+    Y[:end] = mx_fc2(a_q, a_s, w2t_q, w2t_s, counts, offsets)
+    out.update(H=H, A=A, Y=Y, a_q=a_q, a_s=a_s, w2t_q=w2t_q, w2t_s=w2t_s)
+    return out
+
+
 def mx_fc2(a_q, a_s, w2t_q, w2t_s, counts, offsets, rounding: bool = True):
     """Grouped MXFP8 FC2: Y[R_e] = MX(A[R_e]) x MX(W2_e) for each expert.
 
@@ -515,13 +581,16 @@ def mx_fc2(a_q, a_s, w2t_q, w2t_s, counts, offsets, rounding: bool = True):
 # O11: tolerance metric
 # --------------------------------------------------------------------------
 def mlp_backward_mx(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k: int,
-                    g: int = GLU_INTERLEAVE, act: str = "swiglu"):
+                    g: int = GLU_INTERLEAVE, act: str = "swiglu", dgrad2_mx: bool = False):
     """MXFP8 backward of the expert MLP  [P1 core-idea and published-evidence
     sections: GroupGemm + dActivation + Quantize/Transpose; P3 three-components
     section: MXFP8 grouped GEMM].
 
-    FC2 dgrad with the dGLU epilogue stays bf16 (dH, A', dS exactly as in
-    mlp_backward). Its outputs are quantized to MXFP8: dH row-wise (32-column
+    FC2 dgrad with the dGLU epilogue is bf16 (dH, A', dS exactly as in
+    mlp_backward), or with dgrad2_mx runs on dY_u quantized row-wise (blocks
+    along d) and W2_e quantized along d, the dGLU epilogue then taking that
+    product as dA' (and dS on the rewritten side). Its outputs are quantized
+    to MXFP8: dH row-wise (32-column
     blocks: the K of the FC1 dgrad) and column-wise (32-row blocks: the K of
     the FC1 wgrad), A' column-wise (the K of the FC2 wgrad). dY_u and X_perm
     are quantized column-wise and W1_e row-wise along 2n. Then
@@ -531,10 +600,23 @@ def mlp_backward_mx(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of,
     over each expert's 128-aligned row region R_e (padding rows are zero), and
     dx = the unweighted combine of dX_perm.
     """
-    b = mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k, g,
-                     True, act)
     E = w1.shape[0]
     end = int(offsets[-1])
+    extra = {}
+    dap = None
+    if dgrad2_mx:
+        M_cap = np.asarray(x_perm).shape[0]
+        dy_u = permute(np.asarray(dout, dtype=np.float64), np.asarray(row_of, dtype=np.int64), k, M_cap)
+        dy_q, dy_s, _, _ = quant_mxfp8(dy_u[:end], rowwise=True, colwise=False)
+        w2r = [quant_mxfp8(w2[e], rowwise=True, colwise=False)[:2] for e in range(E)]
+        dap = np.zeros((M_cap, w2.shape[1]))
+        for e, r0, r1 in expert_segments(counts, offsets):
+            if r1 > r0:
+                dap[r0:r1] = mx_gemm_rows(dy_q[r0:r1], dy_s[r0:r1], w2r[e][0], w2r[e][1])
+        extra = dict(dy_q=dy_q, dy_s=dy_s, w2q=np.stack([q for q, _ in w2r]),
+                     w2s=np.stack([sc for _, sc in w2r]))
+    b = mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, src_of, k, g,
+                     True, act, dap)
     dh_q, dh_s, dht_q, dht_s = quant_mxfp8(b["dH"][:end], rowwise=True, colwise=True)
     _, _, awt_q, awt_s = quant_mxfp8(b["a_w"][:end], rowwise=False, colwise=True)
     _, _, dyt_q, dyt_s = quant_mxfp8(b["dy_u"][:end], rowwise=False, colwise=True)
@@ -560,6 +642,7 @@ def mlp_backward_mx(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of,
     out.update(dx_perm=dx_perm, dx=dx, dW1=dW1, dW2=dW2, dh_q=dh_q, dh_s=dh_s, dht_q=dht_q,
                dht_s=dht_s, awt_q=awt_q, awt_s=awt_s, dyt_q=dyt_q, dyt_s=dyt_s, xt_q=xt_q,
                xt_s=xt_s, w1q=np.stack([q for q, _ in w1q]), w1s=np.stack([s for _, s in w1q]))
+    out.update(extra)
     return out
 
 

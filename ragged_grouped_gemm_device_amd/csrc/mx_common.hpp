@@ -144,13 +144,29 @@ __device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_
         w0[p] = b4 ? o : w1[p];
         w0[p + 4] = b4 ? w1[p] : o;
     }
-    const int row = lane & 31;
+    // Codes: the 4 slots 4Q + s of a lane become one word, and a 4 x 4 byte
+    // transpose across the lanes of a row quad (two exchanges, each followed
+    // by a byte permute) leaves lane t of the quad with slot 4Q + t for the
+    // quad's 4 rows: one 4-byte store per column and quad instead of four
+    // 1-byte stores.
+    const int row = lane & 31, t = row & 3;
+    const uint32_t sel1 = (t & 1) ? 0x03070105u : 0x06020400u;  // bytes 0-3: own word, 4-7: partner's
+    const uint32_t sel2 = (t & 2) ? 0x03020706u : 0x05040100u;
+    uint8_t* qr = q + (row & ~3);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t ecj = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-        const float inv = __uint_as_float((254u - ecj) << 23);  // 2^-(ecj - 127)
-        const float x = (j & 1) ? bf16_hi(pk[j >> 1]) : bf16_lo(pk[j >> 1]);
-        q[(int64_t)(8 * (j >> 2) + 4 * h + (j & 3)) * ldq + row] = (uint8_t)e4m3_hw(x * inv);
+    for (int Q = 0; Q < 4; ++Q) {
+        float y[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int j = 4 * Q + s;
+            const uint32_t ecj = (w0[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+            const float inv = __uint_as_float((254u - ecj) << 23);  // 2^-(ecj - 127)
+            y[s] = ((j & 1) ? bf16_hi(pk[j >> 1]) : bf16_lo(pk[j >> 1])) * inv;
+        }
+        uint32_t w = e4m3x4(y[0], y[1], y[2], y[3]);
+        w = __builtin_amdgcn_perm(xor_lane<1>(w), w, sel1);  // 16-bit pairs: rows (2i, 2i + 1)
+        w = __builtin_amdgcn_perm(xor_lane<2>(w), w, sel2);  // words: rows 4i .. 4i + 3
+        *(uint32_t*)(qr + (int64_t)(8 * Q + 4 * h + t) * ldq) = w;
     }
 }
 

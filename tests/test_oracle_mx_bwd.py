@@ -15,6 +15,9 @@ import pytest
 from oracle import moe_oracle as O
 
 TOL_MX = 6e-2
+# outputs behind two quantized GEMMs (Y after an MX FC1 and an MX FC2): the
+# E4M3 rounding of both products adds, so twice the one-GEMM bound
+TOL_MX_CHAIN = 1.2e-1
 
 
 def _run(T=64, E=3, k=2, d=64, n=64, seed=0, wstd=0.2, scale=1.0):
@@ -78,3 +81,93 @@ def test_mx_backward_zero_upstream_gradient():
     m = O.mlp_backward_mx(*args)
     for key in ("dx", "dW1", "dW2", "dH"):
         assert np.all(m[key] == 0), key
+
+
+def _exact_case(seed=5, T=80, E=3, k=2, d=64, n=64):
+    """Small-integer data: every MXFP8 copy is exact, so every MX product equals
+    the plain product of the same values."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-3, 4, (T, d)).astype(np.float64)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w1 = rng.integers(-2, 3, (E, d, 2 * n)).astype(np.float64) / 64.0
+    w2 = rng.integers(-2, 3, (E, n, d)).astype(np.float64) / 64.0
+    dout = rng.integers(-3, 4, (T, d)).astype(np.float64)
+    return x, logits, w1, w2, dout
+
+
+def test_mx_fc1_exact_data_equals_bf16_forward():
+    x, logits, w1, w2, _ = _exact_case()
+    f = O.forward(x, logits, w1, w2, 2)
+    m = O.mlp_forward_mx(f["x_perm"], w1, w2, f["counts"], f["offsets"])
+    end = int(f["offsets"][-1])
+    assert np.array_equal(O.mx_dequant(m["x_q"], m["x_s"]), f["x_perm"][:end])
+    np.testing.assert_array_equal(m["H"], f["H"])
+    np.testing.assert_array_equal(m["A"], f["A"])
+
+
+def test_mx_forward_within_tolerance_of_bf16():
+    rng = np.random.default_rng(6)
+    T, E, k, d, n = 96, 4, 2, 128, 64
+    x = O.round_bf16(rng.standard_normal((T, d)))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w1 = O.round_bf16(0.2 * rng.standard_normal((E, d, 2 * n)))
+    w2 = O.round_bf16(0.2 * rng.standard_normal((E, n, d)))
+    f = O.forward(x, logits, w1, w2, k)
+    for fc1_mx in (True, False):
+        m = O.mlp_forward_mx(f["x_perm"], w1, w2, f["counts"], f["offsets"], fc1_mx=fc1_mx)
+        for key in ("H", "A", "Y"):
+            err = O.max_abs_normalised_error(m[key], f[key])
+            assert err <= (TOL_MX_CHAIN if key == "Y" and fc1_mx else TOL_MX), (fc1_mx, key, err)
+            if key in ("H", "A"):
+                assert (err > 0) == fc1_mx, (fc1_mx, key, err)
+
+
+def test_mx_fc1_equals_block_scaled_definition_per_expert():
+    """mx_fc1 = the block-scaled sum written out per block, then the GLU."""
+    f, _, _, args = _run(seed=7)
+    w1 = args[1]
+    m = O.mlp_forward_mx(f["x_perm"], w1, args[2], f["counts"], f["offsets"])
+    xv = O.mx_dequant(m["x_q"], m["x_s"])
+    for e, r0, r1 in O.expert_segments(f["counts"], f["offsets"]):
+        if r1 == r0:
+            continue
+        wv = O.mx_dequant(m["w1t_q"][e], m["w1t_s"][e])            # [2n, d]
+        h = xv[r0:r1] @ wv.T
+        np.testing.assert_array_equal(m["H"][r0:r1], O.round_bf16(h))
+        hg, hu = O.deinterleave(h)
+        np.testing.assert_array_equal(m["A"][r0:r1], O.round_bf16(O.silu(hg) * hu))
+
+
+def test_mx_dgrad2_exact_data_equals_bf16_backward():
+    x, logits, w1, w2, dout = _exact_case(seed=8)
+    f = O.forward(x, logits, w1, w2, 2)
+    args = (f["x_perm"], w1, w2, f["H"], f["Y"], dout, f["topk_w"], f["counts"], f["offsets"],
+            f["row_of"], f["src_of"], 2)
+    b = O.mlp_backward(*args)
+    m = O.mlp_backward_mx(*args, dgrad2_mx=True)
+    for key in ("dH", "a_w"):
+        np.testing.assert_array_equal(m[key], b[key])
+    # dS on the rewritten side equals the plain side up to the bf16 rounding of Y
+    assert O.max_abs_normalised_error(m["dS"], b["dS"]) <= 1e-2
+
+
+def test_mx_dgrad2_within_tolerance_and_rewritten_ds():
+    f, b, _, args = _run(T=96, E=4, k=2, d=128, n=64, seed=9)
+    m = O.mlp_backward_mx(*args, dgrad2_mx=True)
+    assert np.array_equal(m["a_w"], b["a_w"])   # A' = w a does not depend on dA'
+    for key in ("dH", "dS", "dx", "dW1", "dW2"):
+        err = O.max_abs_normalised_error(m[key], b[key])
+        assert 0 < err <= TOL_MX, (key, err)
+    # dS = <dA'_mx, a> per row, the dA' from the block-scaled product of the copies
+    dyv = O.mx_dequant(m["dy_q"], m["dy_s"])
+    end = int(f["offsets"][-1])
+    rows = np.asarray(f["row_of"], dtype=np.int64)
+    H = f["H"]
+    dsr = np.zeros(H.shape[0])
+    for e, r0, r1 in O.expert_segments(f["counts"], f["offsets"]):
+        if r1 > r0:
+            dap = dyv[r0:r1] @ O.mx_dequant(m["w2q"][e], m["w2s"][e]).T
+            hg, hu = O.deinterleave(H[r0:r1])
+            dsr[r0:r1] = (dap * O.silu(hg) * hu).sum(axis=1)
+    np.testing.assert_allclose(m["dS"].reshape(-1), dsr[rows], rtol=1e-10, atol=1e-12)
+    assert end > 0
