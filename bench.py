@@ -149,7 +149,7 @@ def main():
     if mx_mode:
         # W2 (for FC2) and W1 (for the FC1 dgrad) quantized once (weights), outside the timed step
         buf.quantize_weights(w1, w2)
-        mx = buf.mx_fwd()
+        mx = buf.mx_fwd()   # FC1 on x_q / w1t_q, FC2 on a_q / w2t_q
 
     ev = []  # (start, end) of the FC1 launch in each timed step
 
@@ -158,6 +158,10 @@ def main():
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
         if not args.gather:
             M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+        if mx_mode:   # FC1 operand (row-wise) and FC1 wgrad operand (column-wise) in one pass
+            M.moe_quant_mxfp8(buf.x_perm, M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE, buf.x_q, buf.x_s,
+                              buf.xt_q, buf.xt_s)
+            buf.xt_from_forward = True
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -222,16 +226,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16+mxfp8" if mx_mode else "bf16",
+        "dtype": "mxfp8" if mx_mode else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: T={wl.T} tokens top-{wl.k} over E={wl.E} experts, d={wl.d}, "
                         f"n={wl.n} (FC1 N=2n={2 * wl.n}); route->permute->FC1+{glu}"
-                        + ("+MXFP8 quant epilogue->MXFP8 FC2" if mx_mode else "->FC2")
+                        + ("+MXFP8 quant epilogue->MXFP8 FC2 (FC1 on MXFP8 X_perm and W1)" if mx_mode
+                           else "->FC2")
                         + f"->combine + full backward with d{glu}, dS, ragged wgrads and the router "
                         "softmax backward"
-                        + (" (dgrad2+dGLU bf16 with fused MXFP8 quantization of dH and A'; column-wise "
-                           "MXFP8 dY_u and X_perm; FC1 dgrad and both wgrads MXFP8)" if mx_mode else " (bf16)")
+                        + (" (every GEMM on MXFP8: dgrad2+dGLU with fused MXFP8 quantization of dH "
+                           "and A', FC1 dgrad, both wgrads; element-wise and router work in bf16/fp32)"
+                           if mx_mode else " (bf16)")
                         + ("; x and dO rows gathered inside the GEMMs (no permute)" if args.gather else ""),
             "T": wl.T, "k": wl.k, "E": wl.E, "d": wl.d, "n": wl.n,
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -286,9 +292,16 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
         sc = torch.empty(n, end // 32, dtype=torch.uint8, device="cuda")
         rows += [
             (f"FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
-                                                             buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx,
-                                                             act=act),
+                                                             buf.a, buf.y, M.MOE_STAGE_FC1,
+                                                             mx=buf.mx_fwd(fc1=False), act=act),
              4.0 * Mr * d * n, None),
+            (f"MX FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
+                                                                buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx,
+                                                                act=act),
+             4.0 * Mr * d * n, None, PEAK_MXFP8_TFLOPS),
+            ("quant X row+col", lambda: M.moe_quant_mxfp8(buf.x_perm, 3, buf.x_q, buf.x_s, buf.xt_q,
+                                                          buf.xt_s),
+             None, 2.0 * buf.M_cap * d + 2.0 * buf.M_cap * d * 33 / 32),
             ("FC2 MXFP8", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a,
                                                         buf.y, M.MOE_STAGE_FC2, mx=mx),
              2.0 * Mr * d * n, None, PEAK_MXFP8_TFLOPS),
@@ -307,10 +320,14 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
             fl, None))
     if mx is not None:
         mxb = buf.mx_bwd()
-        rows.append(("quant dY_u col", lambda: M.moe_quant_mxfp8(buf.dy_u, M.MOE_QUANT_COLWISE, None, None,
-                                                                 buf.dyt_q, buf.dyt_s),
-                     None, 2.0 * buf.M_cap * d + buf.M_cap * d * 33 / 32))
-        for st, fl, pk in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n, PEAK_BF16_TFLOPS),
+        rows.append(("quant dY_u row+col", lambda: M.moe_quant_mxfp8(buf.dy_u, 3, buf.dy_q, buf.dy_s,
+                                                                     buf.dyt_q, buf.dyt_s),
+                     None, 2.0 * buf.M_cap * d + 2.0 * buf.M_cap * d * 33 / 32))
+        rows.append(("MX bwd 0x04 bf16", (lambda: M.moe_grouped_mlp_bwd(
+            buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+            buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, M.MOE_STAGE_DGRAD2,
+            act=act, mx=buf.mx_bwd(dgrad2=False))), 2.0 * Mr * d * n, None))
+        for st, fl, pk in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n, PEAK_MXFP8_TFLOPS),
                            (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n, PEAK_MXFP8_TFLOPS),
                            (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n, PEAK_MXFP8_TFLOPS),
                            (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n, PEAK_MXFP8_TFLOPS)):

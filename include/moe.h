@@ -198,6 +198,10 @@ typedef struct moe_mx_fwd {
     uint8_t* at_s;         /* [n, M_cap/32] transposed scales, or NULL           */
     const uint8_t* w2t_q;  /* [E, d, n]     W2_e quantized along n, transposed (in) */
     const uint8_t* w2t_s;  /* [E, d, n/32]  its scales (in)                      */
+    const uint8_t* x_q;    /* [M_cap, d]    X_perm row-wise codes (in), or NULL: FC1 in bf16 */
+    const uint8_t* x_s;    /* [M_cap, d/32] its scales (in)                      */
+    const uint8_t* w1t_q;  /* [E, 2n, d]    W1_e quantized along d, transposed (in) */
+    const uint8_t* w1t_s;  /* [E, 2n, d/32] its scales (in)                      */
 } moe_mx_fwd;
 
 /*
@@ -216,7 +220,9 @@ typedef struct moe_mx_fwd {
  *        bf16 A [P1, core-idea section: MXFP8 and transposed output fused in
  *        the GEMM], and FC2 runs on MX-scaled MFMA from a_q/a_s and
  *        w2t_q/w2t_s instead of w2 [P3, three-components section: MXFP8
- *        grouped GEMM].
+ *        grouped GEMM]. With mx->x_q != NULL FC1 also runs on MX-scaled MFMA,
+ *        from x_q/x_s and w1t_q/w1t_s instead of x_perm and w1 (then
+ *        d % 128 == 0 and no MOE_GATHER_ROWS).
  *   x_perm [M_cap, d], w1 [E, d, 2n], w2 [E, n, d] (bf16, in);
  *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out),
  *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
@@ -250,6 +256,10 @@ typedef struct moe_mx_bwd {
     const uint8_t* xt_s;   /* [d, M_cap/32]                                     */
     const uint8_t* w1_q;   /* [E, d, 2n]      W1_e row-wise along 2n (DGRAD1 in) */
     const uint8_t* w1_s;   /* [E, d, 2n/32]                                     */
+    const uint8_t* dy_q;   /* [M_cap, d]      dY_u row-wise codes (DGRAD2 in), or NULL: DGRAD2 in bf16 */
+    const uint8_t* dy_s;   /* [M_cap, d/32]                                     */
+    const uint8_t* w2_q;   /* [E, n, d]       W2_e row-wise along d (DGRAD2 in) */
+    const uint8_t* w2_s;   /* [E, n, d/32]                                      */
 } moe_mx_bwd;
 
 /*
@@ -285,7 +295,10 @@ typedef struct moe_mx_bwd {
  *   transposed) and of A' (column-wise transposed); the other three GEMMs
  *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q, WGRAD2 from awt_q x
  *   dyt_q, WGRAD1 from xt_q x dht_q (K = the expert's row region). Only the
- *   rows of expert regions are written in the transposed copies.
+ *   rows of expert regions are written in the transposed copies. With
+ *   dy_q != NULL DGRAD2 also runs on MX-scaled MFMA (dy_q x w2_q, then d %
+ *   128 == 0 and no MOE_GATHER_ROWS), its dGLU epilogue taking that product
+ *   as dA' and dS on the rewritten side as always.
  * Requires the shape constraints of moe_grouped_mlp_fwd.
  */
 int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,

@@ -135,10 +135,16 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
             (!mx->w2t_q || !mx->w2t_s || !aligned16(mx->w2t_q) || !aligned16(mx->w2t_s)))
             return MOE_ERR_INVALID_ARG;
     }
-    if (stages & MOE_STAGE_FC1) {
-        if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
-        if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
+    const bool fc1_mx = mx && mx->x_q;  // FC1 on MXFP8 operands
+    if (fc1_mx && (stages & MOE_STAGE_FC1)) {
+        if (d % 128 || (stages & MOE_GATHER_ROWS)) return MOE_ERR_UNSUPPORTED;
+        if (!mx->x_s || !mx->w1t_q || !mx->w1t_s || !aligned16(mx->x_q) || !aligned16(mx->w1t_q))
+            return MOE_ERR_INVALID_ARG;
     }
+    if ((stages & MOE_STAGE_FC1) && !fc1_mx) {
+        if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
+    }
+    if ((stages & MOE_STAGE_FC1) && h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(a)) return MOE_ERR_INVALID_ARG;
     if (stages & MOE_STAGE_FC2) {
         if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
@@ -146,9 +152,12 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     }
     hipStream_t s = S(stream);
     if (stages & MOE_STAGE_FC1) {
-        const int rc1 = mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a,
-                                                     mx->a_q, mx->a_s, mx->at_q, mx->at_s, s)
-                           : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, s);
+        const int rc1 = fc1_mx ? moe::launch_fc1_glu_mxin(mx->x_q, mx->x_s, mx->w1t_q, mx->w1t_s, offsets, E,
+                                                          d, n, M_cap, act, h, a, mx->a_q, mx->a_s, mx->at_q,
+                                                          mx->at_s, s)
+                        : mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a,
+                                                      mx->a_q, mx->a_s, mx->at_q, mx->at_s, s)
+                             : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_FC2) {
@@ -177,12 +186,19 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     if (!offsets) return MOE_ERR_INVALID_ARG;
     moe::GatherSpec gs;
     if ((rc = gather_spec(stages, src_of, T, k, E, d, gs))) return rc;
+    const bool dgrad2_mx = mx && mx->dy_q;  // FC2 dgrad on MXFP8 operands
     if (stages & MOE_STAGE_DGRAD2) {
-        if (!dy_u || !w2 || !h || !topk_w || !src_of || !row_of || !dh || !a_w || !ds || !workspace)
+        if (!h || !topk_w || !src_of || !row_of || !dh || !a_w || !ds || !workspace)
             return MOE_ERR_INVALID_ARG;
-        if (!aligned16(dy_u) || !aligned16(w2) || !aligned16(h) || !aligned16(dh) ||
-            !aligned16(a_w) || !aligned16(workspace))
+        if (!aligned16(h) || !aligned16(dh) || !aligned16(a_w) || !aligned16(workspace))
             return MOE_ERR_INVALID_ARG;
+        if (dgrad2_mx) {
+            if (d % 128 || (stages & MOE_GATHER_ROWS)) return MOE_ERR_UNSUPPORTED;
+            if (!mx->dy_s || !mx->w2_q || !mx->w2_s || !aligned16(mx->dy_q) || !aligned16(mx->w2_q))
+                return MOE_ERR_INVALID_ARG;
+        } else if (!dy_u || !w2 || !aligned16(dy_u) || !aligned16(w2)) {
+            return MOE_ERR_INVALID_ARG;
+        }
         if (workspace_bytes < moe_mlp_bwd_workspace_bytes(n, M_cap)) return MOE_ERR_WORKSPACE;
     }
     // with mx the last three GEMMs read only the MXFP8 copies
@@ -213,7 +229,11 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     hipStream_t s = S(stream);
     float* part = static_cast<float*>(workspace);
     if (stages & MOE_STAGE_DGRAD2) {
-        const int rc2 = mx ? moe::launch_dgrad2_dglu_mx(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap,
+        const int rc2 = dgrad2_mx
+                            ? moe::launch_dgrad2_dglu_mxin(mx->dy_q, mx->dy_s, mx->w2_q, mx->w2_s, h, topk_w, src_of,
+                                                           offsets, E, d, n, M_cap, act, dh, a_w, part, mx->dh_q,
+                                                           mx->dh_s, mx->dht_q, mx->dht_s, mx->awt_q, mx->awt_s, s)
+                        : mx ? moe::launch_dgrad2_dglu_mx(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap,
                                                          act, gs, dh, a_w, part, mx->dh_q, mx->dh_s,
                                                          mx->dht_q, mx->dht_s, mx->awt_q, mx->awt_s, s)
                            : moe::launch_dgrad2_dglu(dy_u, w2, h, topk_w, src_of, offsets, E, d, n, M_cap,

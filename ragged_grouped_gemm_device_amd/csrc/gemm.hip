@@ -79,6 +79,12 @@ struct GemmArgs {
     uint8_t* q2_col;  // dGLU MX: A' transposed codes [n, M_cap], scales [n, M_cap/32]
     uint8_t* s2_col;
     int64_t M_cap;
+    // MXFP8 operands (MX kernels): A and B hold E4M3 codes, addressed as pairs
+    // of bytes (lda, ldb, b_estride and K count 2-byte units); as and bs hold
+    // their block scales, kb bytes per row: A [M_cap, kb], B [E, N, kb]
+    const uint8_t* as;
+    const uint8_t* bs;
+    int kb;
 };
 
 // Token of a pair index src = t*k + j without an integer division: with
@@ -106,6 +112,13 @@ struct SlabSrc {
     int g_col0;              // ragged-K gathered operand: first column of the tile
 };
 
+// MX: block scales of a tile's A rows and B rows
+struct ScaleSrc {
+    const uint8_t* as_base;
+    const uint8_t* bs_base;
+    uint32_t as_bytes, bs_bytes;
+};
+
 // Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
 // into the LDS stage at `lds`. Copy i of wavefront w fills LDS block i * 8 + w
 // (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the
@@ -131,12 +144,18 @@ __device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS cha
 // instead of from an expert-major copy. Ragged M gathers the K-major A rows
 // of a tile once per tile; ragged K gathers the K rows of every slab, with
 // the token indices of the next slab loaded one copy-issue ahead.
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT, int GATHER>
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT, int GATHER, bool MX>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
+    // MX: both operands are K-major E4M3 codes on v_mfma_scale_f32_32x32x64_f8f6f4;
+    // a 128-byte slab then holds 128 K values (2 MFMA steps of 64)
+    static_assert(!MX || (A_KMAJ && B_KMAJ && !RAGGED_K && GATHER == 0), "MX: K-major, ragged M");
     // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
     __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
     __shared__ int s_tiles[MOE_MAX_E + 1];  // ragged M: tile prefix; ragged K: experts by work
     __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
+    // MX: block scales of 4 consecutive slabs (a group), 16 bytes for each of the
+    // BM A rows then the BN B rows, double-buffered by group
+    __shared__ __attribute__((aligned(1024))) uint8_t s_sc[MX ? 2 : 1][MX ? (BM + BN) * 16 : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -370,6 +389,87 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 
     f32x16_t acc[4][TNW];
 
+    // ---------------------------------------------------------- MX scales
+    // The block scales of 4 slabs travel together: one 16-byte copy per A row
+    // and per B row (wavefronts 0-3 the A rows, 4-7 the B rows) straight into
+    // LDS, a group ahead; each lane then reads its rows' words one slab ahead.
+    // Bytes past a row's valid K read whatever follows (or 0 past the region)
+    // and are never used.
+    auto make_scales = [&](const Tile& tl) -> ScaleSrc {
+        ScaleSrc sc;
+        sc.as_base = p.as + (int64_t)tl.row0 * p.kb;
+        sc.as_bytes = (uint32_t)((int64_t)(tl.row_end - tl.row0) * p.kb);
+        sc.bs_base = p.bs + ((int64_t)tl.e * p.N + tl.n0) * p.kb;
+        sc.bs_bytes = (uint32_t)((int64_t)(p.N - tl.n0) * p.kb);
+        return sc;
+    };
+    auto issue_scales = [&](const ScaleSrc& sr, int g, int sbuf) {
+        if constexpr (MX) {
+            const bool a_side = wave < kWaves / 2;
+            const int row = (wave % (kWaves / 2)) * 64 + lane;
+            const i32x4_t r = a_side ? rsrc_words(sr.as_base, sr.as_bytes) : rsrc_words(sr.bs_base, sr.bs_bytes);
+            const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_sc[sbuf][0]) + wave * 1024;
+            lds_copy16(r, l, (uint32_t)(row * p.kb + g * 16));
+        }
+    };
+    uint32_t sa[4], sb[TNW], na[4], nb_[TNW];  // MX: this lane's scale words (current, next slab)
+    auto read_scales = [&](int sbuf, int kt4) {
+        const uint8_t* base = s_sc[sbuf] + kt4 * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) na[i] = *(const uint32_t*)(base + (wm * 128 + 32 * i + (lane & 31)) * 16);
+#pragma unroll
+        for (int j = 0; j < TNW; ++j)
+            nb_[j] = *(const uint32_t*)(base + (BM + wn * WN + 32 * j + (lane & 31)) * 16);
+    };
+    // shifted by this half-wave's block: K step ks then finds its scale in
+    // byte 0 after a further shift by 16 ks
+    auto take_scales = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[i] = na[i] >> (8 * (lane >> 5));
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) sb[j] = nb_[j] >> (8 * (lane >> 5));
+    };
+    // one 128-byte slab on the scaled MFMA: a lane's operand for K step ks is
+    // 16-byte chunks h and 2 + h of its row's 64 step bytes (h = lane half),
+    // the scale of block b coming from lane half b
+    auto mx_slab = [&](int buf) {
+        const uint8_t* sA = (const uint8_t*)s_ab[buf];
+        const uint8_t* sB = sA + BM * BK * 2;
+        const int hh = lane >> 5;
+        static_for<2>([&](auto KS) {
+            constexpr int ks = KS;
+            i32x8_t xa[4], xb[TNW];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wm * 128 + 32 * i + (lane & 31);
+                const i32x4_t lo = *(const i32x4_t*)(sA + kmaj_byte(r, 4 * ks + hh));
+                const i32x4_t hi = *(const i32x4_t*)(sA + kmaj_byte(r, 4 * ks + 2 + hh));
+                xa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) {
+                const int r = wn * WN + 32 * j + (lane & 31);
+                const i32x4_t lo = *(const i32x4_t*)(sB + kmaj_byte(r, 4 * ks + hh));
+                const i32x4_t hi = *(const i32x4_t*)(sB + kmaj_byte(r, 4 * ks + 2 + hh));
+                xb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            __builtin_amdgcn_s_setprio(1);
+            static_for<4>([&](auto I) {
+                static_for<TNW>([&](auto J) {
+                    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        xb[J], xa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0, (int)(sa[I] >> (16 * ks)));
+                });
+            });
+            __builtin_amdgcn_s_setprio(0);
+        });
+        // keep the MFMAs above the slab barrier (left alone, the compiler sinks
+        // them below it and serialises the copy wait with the multiply)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TNW; ++j) asm volatile("" : "+v"(acc[i][j]));
+    };
+
     // ---------------------------------------------------------- tile loop
     int round = 0;
     int t = logical(0);
@@ -389,8 +489,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             __syncthreads();
         }
         issue(src, 0, 0);
+        if constexpr (MX) issue_scales(make_scales(tl), 0, 0);
         if constexpr (kTok) fetch_toks(tl, 1);
     }
+    int sg0 = 0;  // MX: scale buffer holding group 0 of the current tile
     bool have_next = false;
     for (;;) {
 #pragma unroll
@@ -410,11 +512,17 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             nk_next = (tl_next.k_end - tl_next.k_begin) / BK;
         }
         int next_buf0 = buf0;
+        const int ng = (nk + 3) / 4;  // MX: scale groups of this tile
         if (nk > 0) {
             __builtin_amdgcn_s_waitcnt(0);
             stash_toks();
             __syncthreads();
-            load_frags(0, buf0, 0);
+            if constexpr (MX) {
+                read_scales(sg0, 0);
+                take_scales();
+            } else {
+                load_frags(0, buf0, 0);
+            }
             for (int kt = 0; kt < nk; ++kt) {
                 // No vector-memory load is in flight here in the steady state (the
                 // previous slab ended with a full wait), so this wait is free; it
@@ -432,8 +540,18 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     }
                 } else if (nk_next > 0) {
                     issue(src_next, 0, cur ^ 1);
+                    if constexpr (MX) issue_scales(make_scales(tl_next), 0, (sg0 + ng) & 1);
                     if constexpr (kTok) fetch_toks(tl_next, 1);
                 }
+                if constexpr (MX) {
+                    // the next group's scales go to the buffer the previous group
+                    // left (its last reads ended before the previous slab barrier);
+                    // the next slab's words come from a group that landed at least
+                    // one slab barrier ago
+                    if ((kt & 3) == 0 && kt + 4 < nk) issue_scales(make_scales(tl), kt / 4 + 1, (sg0 + kt / 4 + 1) & 1);
+                    if (!last) read_scales((sg0 + (kt + 1) / 4) & 1, (kt + 1) & 3);
+                    mx_slab(cur);
+                } else {
                 const uint16_t* sa = s_ab[cur];
                 const uint16_t* sb = s_ab[cur] + BM * BK;
                 static_for<BK / 16>([&](auto KS) {
@@ -453,11 +571,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
                     __builtin_amdgcn_s_setprio(0);
                 });
+                }
                 if (!last) {
                     __builtin_amdgcn_s_waitcnt(0);
                     stash_toks();
                     __syncthreads();
-                    load_frags(0, cur ^ 1, 0);
+                    if constexpr (MX)
+                        take_scales();
+                    else
+                        load_frags(0, cur ^ 1, 0);
                 } else {
                     next_buf0 = cur ^ 1;
                 }
@@ -470,6 +592,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 __syncthreads();
             }
             issue(src_next, 0, buf0);
+            if constexpr (MX) issue_scales(make_scales(tl_next), 0, sg0);
             if constexpr (kTok) fetch_toks(tl_next, 1);
         }
         const int e = tl.e, row0 = tl.row0, row_end = tl.row_end, n0 = tl.n0, m0 = tl.m0;
@@ -750,6 +873,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         src = src_next;
         nk = nk_next;
         buf0 = next_buf0;
+        sg0 = (sg0 + ng) & 1;
     }
 }
 
@@ -767,10 +891,10 @@ __global__ void __launch_bounds__(256) ds_reduce_kernel(const float* __restrict_
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT = 0, int GATHER = 0>
+template <bool RAGGED_K, bool A_KMAJ, bool B_KMAJ, int EPI, int ACT = 0, int GATHER = 0, bool MX = false>
 static int run(const GemmArgs& a, int64_t tile_bound, hipStream_t s) {
     if (tile_bound <= 0) return 0;
-    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI, ACT, GATHER>
+    grouped_gemm_kernel<RAGGED_K, A_KMAJ, B_KMAJ, EPI, ACT, GATHER, MX>
         <<<persistent_grid(tile_bound), kThreads, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
@@ -829,6 +953,25 @@ int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t*
     return run_glu<false, EPI_GLU_MX>(g, act, gx.src_of != nullptr, ragged_m_grid(M_cap, E, 2 * n), s);
 }
 
+// MXFP8 operands: codes are passed as 2-byte units (K, lda, ldb, b_estride
+// halved), so the slab copies are the bf16 kernel's byte for byte.
+int launch_fc1_glu_mxin(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w1t_q,
+                        const uint8_t* w1t_s, const int32_t* offsets, int E, int d, int n,
+                        int64_t M_cap, int act, uint16_t* h, uint16_t* a, uint8_t* a_q, uint8_t* a_s,
+                        uint8_t* at_q, uint8_t* at_s, hipStream_t s) {
+    GemmArgs g = zero_args();
+    g.A = (const uint16_t*)x_q; g.lda = d / 2;
+    g.B = (const uint16_t*)w1t_q; g.ldb = d / 2; g.b_estride = (int64_t)2 * n * (d / 2);
+    g.offsets = offsets; g.E = E; g.N = 2 * n; g.K = d / 2;
+    g.as = x_s; g.bs = w1t_s; g.kb = d / 32;
+    g.out0 = h; g.ld0 = 2 * n;
+    g.out1 = a; g.ld1 = n;
+    g.q_row = a_q; g.s_row = a_s; g.q_col = at_q; g.s_col = at_s; g.M_cap = M_cap;
+    const int64_t tb = ragged_m_grid(M_cap, E, 2 * n);
+    return act ? run<false, true, true, EPI_GLU_MX, 1, 0, true>(g, tb, s)
+               : run<false, true, true, EPI_GLU_MX, 0, 0, true>(g, tb, s);
+}
+
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
                int64_t M_cap, uint16_t* y, hipStream_t s) {
     GemmArgs g = zero_args();
@@ -875,6 +1018,29 @@ int launch_dgrad2_dglu_mx(const uint16_t* dy_u, const uint16_t* w2, const uint16
     g.q2_col = awt_q; g.s2_col = awt_s; g.M_cap = M_cap;
     set_gather(g, gdy);
     return run_glu<true, EPI_DGLU_MX>(g, act, gdy.src_of != nullptr, ragged_m_grid(M_cap, E, n), s);
+}
+
+int launch_dgrad2_dglu_mxin(const uint8_t* dy_q, const uint8_t* dy_s, const uint8_t* w2_q,
+                            const uint8_t* w2_s, const uint16_t* h, const float* topk_w,
+                            const int32_t* src_of, const int32_t* offsets, int E, int d, int n,
+                            int64_t M_cap, int act, uint16_t* dh, uint16_t* a_w, float* ds_part,
+                            uint8_t* dh_q, uint8_t* dh_s, uint8_t* dht_q, uint8_t* dht_s,
+                            uint8_t* awt_q, uint8_t* awt_s, hipStream_t s) {
+    GemmArgs g = zero_args();
+    g.A = (const uint16_t*)dy_q; g.lda = d / 2;
+    g.B = (const uint16_t*)w2_q; g.ldb = d / 2; g.b_estride = (int64_t)n * (d / 2);
+    g.offsets = offsets; g.E = E; g.N = n; g.K = d / 2;
+    g.as = dy_s; g.bs = w2_s; g.kb = d / 32;
+    g.out0 = dh; g.ld0 = 2 * n;
+    g.out1 = a_w; g.ld1 = n;
+    g.outf = ds_part; g.n_part = ds_partials_per_row(n);
+    g.aux = h; g.ld_aux = 2 * n;
+    g.topk_w = topk_w; g.src_of = src_of;
+    g.q_row = dh_q; g.s_row = dh_s; g.q_col = dht_q; g.s_col = dht_s;
+    g.q2_col = awt_q; g.s2_col = awt_s; g.M_cap = M_cap;
+    const int64_t tb = ragged_m_grid(M_cap, E, n);
+    return act ? run<false, true, true, EPI_DGLU_MX, 1, 0, true>(g, tb, s)
+               : run<false, true, true, EPI_DGLU_MX, 0, 0, true>(g, tb, s);
 }
 
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,

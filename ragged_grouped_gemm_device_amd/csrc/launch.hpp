@@ -67,6 +67,17 @@ int launch_dgrad2_dglu_mx(const uint16_t* dy_u, const uint16_t* w2, const uint16
                           uint16_t* a_w, float* ds_part, uint8_t* dh_q, uint8_t* dh_s,
                           uint8_t* dht_q, uint8_t* dht_s, uint8_t* awt_q, uint8_t* awt_s,
                           hipStream_t s);
+// FC1 / FC2 dgrad on MXFP8 operands (codes + block scales along K = d)
+int launch_fc1_glu_mxin(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w1t_q,
+                        const uint8_t* w1t_s, const int32_t* offsets, int E, int d, int n,
+                        int64_t M_cap, int act, uint16_t* h, uint16_t* a, uint8_t* a_q, uint8_t* a_s,
+                        uint8_t* at_q, uint8_t* at_s, hipStream_t s);
+int launch_dgrad2_dglu_mxin(const uint8_t* dy_q, const uint8_t* dy_s, const uint8_t* w2_q,
+                            const uint8_t* w2_s, const uint16_t* h, const float* topk_w,
+                            const int32_t* src_of, const int32_t* offsets, int E, int d, int n,
+                            int64_t M_cap, int act, uint16_t* dh, uint16_t* a_w, float* ds_part,
+                            uint8_t* dh_q, uint8_t* dh_s, uint8_t* dht_q, uint8_t* dht_s,
+                            uint8_t* awt_q, uint8_t* awt_s, hipStream_t s);
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,
                      float* ds, hipStream_t s);
 int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets, int E, int d,

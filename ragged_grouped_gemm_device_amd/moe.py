@@ -67,12 +67,13 @@ class MoEError(RuntimeError):
         self.status = status
 
 
-class moe_mx_fwd(C.Structure):
-    _fields_ = [("a_q", _P), ("a_s", _P), ("at_q", _P), ("at_s", _P), ("w2t_q", _P), ("w2t_s", _P)]
-
-
+MX_FWD_FIELDS = ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s", "x_q", "x_s", "w1t_q", "w1t_s")
 MX_BWD_FIELDS = ("dh_q", "dh_s", "dht_q", "dht_s", "awt_q", "awt_s", "dyt_q", "dyt_s", "xt_q", "xt_s",
-                 "w1_q", "w1_s")
+                 "w1_q", "w1_s", "dy_q", "dy_s", "w2_q", "w2_s")
+
+
+class moe_mx_fwd(C.Structure):
+    _fields_ = [(name, _P) for name in MX_FWD_FIELDS]
 
 
 class moe_mx_bwd(C.Structure):
@@ -172,7 +173,7 @@ def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD,
     T = x_perm.shape[0] if (stages & MOE_GATHER_ROWS) else 0
     mxp = None
     if mx is not None:
-        mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s")])
+        mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in MX_FWD_FIELDS])
         mxp = C.byref(mxs)
     rc = _lib().moe_grouped_mlp_fwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(offsets), _ptr(src_of), T,
                                     k, E, d, n2 // 2, M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y),
@@ -261,28 +262,52 @@ class Buffers:
             self.xt_s = torch.empty(d, M // 32, dtype=u8, device=dev)
             self.w1_q = torch.empty(E, d, 2 * n, dtype=u8, device=dev)
             self.w1_s = torch.empty(E, d, 2 * n // 32, dtype=u8, device=dev)
+            self.x_q = torch.empty(M, d, dtype=u8, device=dev)
+            self.x_s = torch.empty(M, d // 32, dtype=u8, device=dev)
+            self.w1t_q = torch.empty(E, 2 * n, d, dtype=u8, device=dev)
+            self.w1t_s = torch.empty(E, 2 * n, d // 32, dtype=u8, device=dev)
+            self.dy_q = torch.empty(M, d, dtype=u8, device=dev)
+            self.dy_s = torch.empty(M, d // 32, dtype=u8, device=dev)
+            self.w2_q = torch.empty(E, n, d, dtype=u8, device=dev)
+            self.w2_s = torch.empty(E, n, d // 32, dtype=u8, device=dev)
+        self.xt_from_forward = False
 
     def quantize_weights(self, w1, w2):
-        """MXFP8 weight copies: W2_e along n, transposed [E, d, n] (FC2), and W1_e along 2n
-        [E, d, 2n] (FC1 dgrad)."""
-        moe_quant_mxfp8(w2, MOE_QUANT_COLWISE, None, None, self.w2t_q, self.w2t_s)
-        moe_quant_mxfp8(w1, MOE_QUANT_ROWWISE, self.w1_q, self.w1_s)
+        """MXFP8 weight copies: W1_e along 2n [E, d, 2n] (FC1 dgrad) and along d, transposed
+        [E, 2n, d] (FC1); W2_e along d [E, n, d] (FC2 dgrad) and along n, transposed [E, d, n]
+        (FC2)."""
+        moe_quant_mxfp8(w1, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, self.w1_q, self.w1_s, self.w1t_q,
+                        self.w1t_s)
+        moe_quant_mxfp8(w2, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, self.w2_q, self.w2_s, self.w2t_q,
+                        self.w2t_s)
 
-    def mx_fwd(self):
-        return dict(a_q=self.a_q, a_s=self.a_s, at_q=self.at_q, at_s=self.at_s, w2t_q=self.w2t_q,
-                    w2t_s=self.w2t_s)
+    def mx_fwd(self, fc1=True):
+        keys = MX_FWD_FIELDS if fc1 else MX_FWD_FIELDS[:6]
+        return {key: getattr(self, key) for key in keys}
 
-    def mx_bwd(self):
-        return {key: getattr(self, key) for key in MX_BWD_FIELDS}
+    def mx_bwd(self, dgrad2=True):
+        keys = MX_BWD_FIELDS if dgrad2 else MX_BWD_FIELDS[:12]
+        return {key: getattr(self, key) for key in keys}
 
 
 def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True,
-            act=MOE_ACT_SWIGLU, gather=False):
+            act=MOE_ACT_SWIGLU, gather=False, mx=False):
     """route -> permute -> FC1+GLU -> FC2 -> combine (all enqueued, no sync). With gather, FC1
-    reads the rows of x through src_of and no permuted copy is made."""
+    reads the rows of x through src_of and no permuted copy is made. With mx (buffers made with
+    mx=True, quantize_weights done), X_perm is quantized row-wise (FC1 operand) and column-wise
+    (FC1 wgrad operand) in one pass and both GEMMs run on MXFP8."""
     moe_route_counts(logits, buf.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
                      buf.src_of, buf.M_cap, buf.err, buf.route_ws, renorm)
-    if gather:
+    buf.xt_from_forward = bool(mx)
+    if mx:
+        if gather:
+            raise ValueError("the MXFP8 FC1 reads the quantized permuted copy: no row gather")
+        moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
+        moe_quant_mxfp8(buf.x_perm, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, buf.x_q, buf.x_s, buf.xt_q,
+                        buf.xt_s)
+        moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a,
+                            buf.y, fwd_stages, mx=buf.mx_fwd(), act=act)
+    elif gather:
         moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
                             fwd_stages | MOE_GATHER_ROWS, act=act, src_of=buf.src_of, k=buf.k)
     else:
@@ -293,21 +318,27 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
 
 
 def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU, logits=None,
-             renorm=False, x=None, mx=False):
+             renorm=False, x=None, mx=False, dgrad2_mx=True):
     """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum, and with
     the forward's logits also the router backward dS -> dlogits. With x given (the un-permuted
     input), the GEMMs read x and dO through src_of instead of permuted copies. With mx (buffers
-    made with mx=True and quantize_weights done), dY_u and X_perm are quantized column-wise and
-    the last three GEMMs run on MXFP8."""
+    made with mx=True and quantize_weights done), dY_u is quantized (row-wise for the FC2 dgrad
+    when dgrad2_mx, column-wise for the FC2 wgrad), X_perm column-wise unless the MXFP8 forward
+    already did, and the GEMMs run on MXFP8 (the FC2 dgrad only with dgrad2_mx)."""
     if mx:
         if x is not None:
             raise ValueError("the MXFP8 backward quantizes the permuted copies: no row gather")
         moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
-        moe_quant_mxfp8(buf.dy_u, MOE_QUANT_COLWISE, None, None, buf.dyt_q, buf.dyt_s)
-        moe_quant_mxfp8(buf.x_perm, MOE_QUANT_COLWISE, None, None, buf.xt_q, buf.xt_s)
+        if dgrad2_mx:
+            moe_quant_mxfp8(buf.dy_u, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, buf.dy_q, buf.dy_s,
+                            buf.dyt_q, buf.dyt_s)
+        else:
+            moe_quant_mxfp8(buf.dy_u, MOE_QUANT_COLWISE, None, None, buf.dyt_q, buf.dyt_s)
+        if not buf.xt_from_forward:
+            moe_quant_mxfp8(buf.x_perm, MOE_QUANT_COLWISE, None, None, buf.xt_q, buf.xt_s)
         moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
                             buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                            buf.bwd_ws, stages, act=act, mx=buf.mx_bwd())
+                            buf.bwd_ws, stages, act=act, mx=buf.mx_bwd(dgrad2_mx))
     elif x is not None:
         moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
                             buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,

@@ -216,3 +216,56 @@ def test_mx_fc2_on_identical_codes(M):
     err = rel_err(bf16_values(buf.y)[:end], Y[:end])
     print(f"  MX FC2 on identical codes: {err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+FC1_MX_CASES = [
+    W.small("mx1-small", T=600, k=2, E=4, d=256, n=256, seed=41, routing="zipf"),
+    W.small("mx1-empty", T=300, k=2, E=16, d=384, n=128, seed=22, routing="zipf"),
+]
+
+
+@pytest.mark.parametrize("wl,act", [(c, "swiglu") for c in FC1_MX_CASES] + [(FC1_MX_CASES[0], "geglu")],
+                         ids=[c.name for c in FC1_MX_CASES] + [FC1_MX_CASES[0].name + "-geglu"])
+def test_mx_fc1_forward_parity(M, wl, act):
+    """FC1 on MXFP8 too: X_perm and W1 copies bit-exact against the oracle's
+    quantization, H and A from identical codes within 2e-2 (one bf16 rounding;
+    the scaled MFMA's own deviation is ~1e-4), Y and out within 6e-2 of the
+    oracle's MXFP8 forward (a few A codes may round differently)."""
+    print(f"mx fc1 case {wl} act={act}", flush=True)
+    inp = W.make_inputs(wl)
+    buf = _mx_buffers(M, wl)
+    for name in ("h", "a", "y", "out"):
+        getattr(buf, name).fill_(float("nan"))
+    x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
+    buf.quantize_weights(w1, w2)
+    gact = M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU
+    M.forward(buf, x, f32_tensor(inp["logits"]), w1, w2, act=gact, mx=True)
+    torch.cuda.synchronize()
+    xo, w1o, w2o = O.from_bf16(inp["x"]), O.from_bf16(inp["w1"]), O.from_bf16(inp["w2"])
+    f = O.forward(xo, inp["logits"], w1o, w2o, wl.k, act=act)
+    m = O.mlp_forward_mx(f["x_perm"], w1o, w2o, f["counts"], f["offsets"], act=act)
+    end = int(f["offsets"][-1])
+    assert np.array_equal(buf.x_q.cpu().numpy()[:end], m["x_q"])
+    assert np.array_equal(buf.x_s.cpu().numpy()[:end], m["x_s"])
+    assert np.array_equal(buf.w1t_q.cpu().numpy(), m["w1t_q"])
+    assert np.array_equal(buf.w1t_s.cpu().numpy(), m["w1t_s"])
+    # the column-wise X copy made in the same pass (the FC1 wgrad operand)
+    _, _, xt_q, xt_s = O.quant_mxfp8(f["x_perm"][:end], rowwise=False, colwise=True)
+    assert np.array_equal(buf.xt_q.cpu().numpy()[:, :end], xt_q)
+    assert np.array_equal(buf.xt_s.cpu().numpy()[:, :end // 32], xt_s)
+    for name, got, ref, tol in (("H", bf16_values(buf.h)[:end], m["H"][:end], 2e-2),
+                                ("A", bf16_values(buf.a)[:end], m["A"][:end], 2e-2),
+                                ("Y", bf16_values(buf.y)[:end], m["Y"][:end], 6e-2)):
+        assert np.isfinite(got).all(), name
+        err = rel_err(got, ref)
+        print(f"  {name}: {err:.3e}", flush=True)
+        assert err <= tol, (name, err)
+    out = O.combine(m["Y"], f["row_of"], wl.k, f["topk_w"])
+    err = rel_err(bf16_values(buf.out), out)
+    print(f"  out: {err:.3e}", flush=True)
+    assert err <= 6e-2
+    # the fused A copy equals the standalone quantization of the same bf16 A
+    a_bits = buf.a.view(torch.int16).cpu().numpy().view(np.uint16)
+    g = _gpu_quant(M, a_bits[:end], 1)
+    assert np.array_equal(buf.a_q.cpu().numpy()[:end], g[0][0])
+

@@ -45,7 +45,7 @@ def _np(t):
     return t.cpu().numpy()
 
 
-def _run_gpu(M, wl, inp, act):
+def _run_gpu(M, wl, inp, act, dgrad2_mx=False):
     buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
     for name in ("dh", "a_w", "ds", "dx_perm", "dx", "dw1", "dw2"):
         getattr(buf, name).fill_(float("nan"))
@@ -55,7 +55,7 @@ def _run_gpu(M, wl, inp, act):
     logits, dout = f32_tensor(inp["logits"]), bf16_tensor(inp["dout"])
     buf.quantize_weights(w1, w2)
     M.forward(buf, x, logits, w1, w2, act=act)
-    M.backward(buf, dout, w1, w2, act=act, mx=True)
+    M.backward(buf, dout, w1, w2, act=act, mx=True, dgrad2_mx=dgrad2_mx)
     torch.cuda.synchronize()
     return buf
 
@@ -80,21 +80,32 @@ def _check(name, got, ref, tol):
     assert err <= tol, f"{name}: {err}"
 
 
-@pytest.mark.parametrize("wl,act", [(c, "swiglu") for c in CASES] + [(CASES[1], "geglu")],
-                         ids=[c.name for c in CASES] + [CASES[1].name + "-geglu"])
-def test_mx_backward_parity(M, wl, act):
-    print(f"mx backward case {wl} act={act}", flush=True)
+# dgrad2_mx: the FC2 dgrad also on MXFP8 (dY_u row-wise x W2_e along d); d must be a
+# multiple of 128 for it
+MX_DG2 = [(c, "swiglu", False) for c in CASES] + [(CASES[1], "geglu", False)] + [
+    (CASES[0], "swiglu", True), (CASES[2], "swiglu", True), (CASES[3], "geglu", True)]
+
+
+@pytest.mark.parametrize("wl,act,dgrad2_mx", MX_DG2,
+                         ids=[f"{c.name}-{a}" + ("-dgrad2mx" if g else "") for c, a, g in MX_DG2])
+def test_mx_backward_parity(M, wl, act, dgrad2_mx):
+    print(f"mx backward case {wl} act={act} dgrad2_mx={dgrad2_mx}", flush=True)
     inp = W.make_inputs(wl)
-    buf = _run_gpu(M, wl, inp, M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU)
+    buf = _run_gpu(M, wl, inp, M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU, dgrad2_mx)
     x, w1, w2 = O.from_bf16(inp["x"]), O.from_bf16(inp["w1"]), O.from_bf16(inp["w2"])
     f = O.forward(x, inp["logits"], w1, w2, wl.k, act=act)
     b = O.mlp_backward_mx(f["x_perm"], w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"]), f["topk_w"],
-                          f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k, act=act)
+                          f["counts"], f["offsets"], f["row_of"], f["src_of"], wl.k, act=act,
+                          dgrad2_mx=dgrad2_mx)
     offsets = f["offsets"]
     end = int(offsets[-1])
     assert np.array_equal(_np(buf.offsets), offsets)
+    if dgrad2_mx:   # the FC2 dgrad operands: the oracle's quantization of the same bf16 values
+        assert np.array_equal(_np(buf.dy_q)[:end], b["dy_q"]) and np.array_equal(
+            _np(buf.dy_s)[:end], b["dy_s"]), "dY_u row copy"
+        assert np.array_equal(_np(buf.w2_q), b["w2q"]) and np.array_equal(_np(buf.w2_s), b["w2s"]), "W2 copy"
 
-    # DGRAD2 (bf16) as in the bf16 path
+    # DGRAD2 (bf16, or MX on codes identical to the oracle's) as in the bf16 path
     _check("dS", _np(buf.ds), b["dS"], 2e-2)
     _check("dH", bf16_values(buf.dh)[:end], b["dH"][:end], 2e-2)
     _check("A'", bf16_values(buf.a_w)[:end], b["a_w"][:end], 2e-2)
