@@ -156,12 +156,13 @@ def main():
     def step(record=False):
         M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
-        if not args.gather:
-            M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
-        if mx_mode:   # FC1 operand (row-wise) and FC1 wgrad operand (column-wise) in one pass
-            M.moe_quant_mxfp8(buf.x_perm, M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE, buf.x_q, buf.x_s,
-                              buf.xt_q, buf.xt_s)
+        if mx_mode:
+            # X_perm only as MXFP8: row-wise (FC1) and column-wise (FC1 wgrad), fused with the permute
+            M.moe_permute_quant_mxfp8(x, buf.src_of, wl.k, wl.E, M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE,
+                                      buf.x_q, buf.x_s, buf.xt_q, buf.xt_s)
             buf.xt_from_forward = True
+        elif not args.gather:
+            M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -302,6 +303,9 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
             ("quant X row+col", lambda: M.moe_quant_mxfp8(buf.x_perm, 3, buf.x_q, buf.x_s, buf.xt_q,
                                                           buf.xt_s),
              None, 2.0 * buf.M_cap * d + 2.0 * buf.M_cap * d * 33 / 32),
+            ("permute+quant X", lambda: M.moe_permute_quant_mxfp8(x, buf.src_of, wl.k, wl.E, 3, buf.x_q,
+                                                                  buf.x_s, buf.xt_q, buf.xt_s),
+             None, 2.0 * end * d + 2.0 * buf.M_cap * d * 33 / 32),
             ("FC2 MXFP8", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a,
                                                         buf.y, M.MOE_STAGE_FC2, mx=mx),
              2.0 * Mr * d * n, None, PEAK_MXFP8_TFLOPS),

@@ -327,6 +327,24 @@ int moe_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode,
                     uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                     moe_stream_t stream);
 
+/*
+ * moe_permute_quant_mxfp8 -- the expert-major permutation of x [T, d] fused
+ * with its MXFP8 quantization: row r of the permuted matrix is
+ * x[src_of[r] / k] (zeros where src_of[r] < 0), and it is quantized as
+ * moe_quant_mxfp8 would quantize X_perm [M_cap, d], without the bf16 copy
+ * ever being written [P1, problem section: the BF16 -> MXFP8 pass and its
+ * transposed copy; P3, three-components section: group-aware MXFP8
+ * quantization on the expert-major buffer].
+ *   x [T, d] bf16, src_of [M_cap] (in, from moe_route_counts); mode, q_row
+ *   [M_cap, d] + s_row [M_cap, d/32], q_col [d, M_cap] + s_col [d, M_cap/32]
+ *   as in moe_quant_mxfp8 (out, every row of [0, M_cap)).
+ * Requires d % 32 == 0, M_cap % 128 == 0, M_cap >= moe_capacity_rows(T, k, E),
+ * 16-byte aligned x and code buffers.
+ */
+int moe_permute_quant_mxfp8(const uint16_t* x, const int32_t* src_of, int T, int k, int E, int d,
+                            int64_t M_cap, int mode, uint8_t* q_row, uint8_t* s_row,
+                            uint8_t* q_col, uint8_t* s_col, moe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -278,4 +278,23 @@ int moe_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, 
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
+int moe_permute_quant_mxfp8(const uint16_t* x, const int32_t* src_of, int T, int k, int E, int d,
+                            int64_t M_cap, int mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                            uint8_t* s_col, moe_stream_t stream) {
+    if (!x || !src_of || d <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
+    const int64_t cap = capacity(T, k, E);
+    if (cap < 0) return MOE_ERR_INVALID_ARG;
+    if (M_cap < cap) return MOE_ERR_WORKSPACE;
+    if (mode <= 0 || (mode & ~(MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE))) return MOE_ERR_INVALID_ARG;
+    if ((mode & MOE_QUANT_ROWWISE) && (!q_row || !s_row)) return MOE_ERR_INVALID_ARG;
+    if ((mode & MOE_QUANT_COLWISE) && (!q_col || !s_col)) return MOE_ERR_INVALID_ARG;
+    if (d % MOE_MX_BLOCK || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || (q_row && !aligned16(q_row)) || (q_col && !aligned16(q_col)))
+        return MOE_ERR_INVALID_ARG;
+    if (M_cap * d >= ((int64_t)1 << 40) || (M_cap + 127) / 128 > 65535) return MOE_ERR_UNSUPPORTED;
+    const int rc = moe::launch_permute_quant_mxfp8(x, src_of, k, M_cap, d, mode, q_row, s_row, q_col, s_col,
+                                                   S(stream));
+    return rc ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
 }  // extern "C"

@@ -90,5 +90,8 @@ int ds_partials_per_row(int n);
 // MXFP8
 int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
                        uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s);
+int launch_permute_quant_mxfp8(const uint16_t* x, const int32_t* src_of, int k, int64_t M_cap, int d,
+                               int mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                               hipStream_t s);
 
 }  // namespace moe

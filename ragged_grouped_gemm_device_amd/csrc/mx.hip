@@ -31,12 +31,16 @@ __device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
     return max((uint32_t)d.x, (uint32_t)d.y);
 }
 
-template <bool ROW, bool COL>
+// GATHER: row r of the matrix is row src_of[r] / k of src [T, C] (the
+// expert-major permutation, with zeros for padding rows, src_of[r] < 0), so
+// the permuted bf16 copy is never written.
+template <bool ROW, bool COL, bool GATHER>
 __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t R,
                                                           int C, uint8_t* __restrict__ q_row,
                                                           uint8_t* __restrict__ s_row,
                                                           uint8_t* __restrict__ q_col,
-                                                          uint8_t* __restrict__ s_col) {
+                                                          uint8_t* __restrict__ s_col,
+                                                          const int32_t* __restrict__ src_of, int k) {
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int cc = l & 15, rg = 4 * w + (l >> 4);
     const int64_t b = blockIdx.z;
@@ -48,7 +52,12 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         v[i] = make_uint4(0, 0, 0, 0);
-        if (cok && r + i < R) v[i] = *(const uint4*)(src + (r + i) * C + c);
+        if constexpr (GATHER) {
+            const int sr = cok && r + i < R ? src_of[r + i] : -1;
+            if (sr >= 0) v[i] = *(const uint4*)(src + (int64_t)(sr / k) * C + c);
+        } else {
+            if (cok && r + i < R) v[i] = *(const uint4*)(src + (r + i) * C + c);
+        }
     }
     if constexpr (ROW) {
         uint8_t* qr = q_row + b * R * C;
@@ -99,15 +108,29 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
     }
 }
 
-int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
-                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s) {
+template <bool GATHER>
+static void quant_dispatch(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
+                           uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, const int32_t* src_of, int k,
+                           hipStream_t s) {
     const dim3 grid((C + QT - 1) / QT, (unsigned)((R + QT - 1) / QT), batch);
     if ((mode & 3) == 3)
-        quant_mxfp8_kernel<true, true><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+        quant_mxfp8_kernel<true, true, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
     else if (mode & 1)
-        quant_mxfp8_kernel<true, false><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+        quant_mxfp8_kernel<true, false, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
     else
-        quant_mxfp8_kernel<false, true><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col);
+        quant_mxfp8_kernel<false, true, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
+}
+
+int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
+                       uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s) {
+    quant_dispatch<false>(src, batch, R, C, mode, q_row, s_row, q_col, s_col, nullptr, 1, s);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_permute_quant_mxfp8(const uint16_t* x, const int32_t* src_of, int k, int64_t M_cap, int d,
+                               int mode, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                               hipStream_t s) {
+    quant_dispatch<true>(x, 1, M_cap, d, mode, q_row, s_row, q_col, s_col, src_of, k, s);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -58,6 +58,7 @@ SIGNATURES = {
     "moe_grouped_mlp_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _I,
                                  C.c_uint, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
     "moe_quant_mxfp8": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_permute_quant_mxfp8": (_I, [_P, _P, _I, _I, _I, _I, _I64, _I, _P, _P, _P, _P, _P]),
 }
 
 
@@ -211,6 +212,13 @@ def moe_quant_mxfp8(src, mode, q_row=None, s_row=None, q_col=None, s_col=None):
     _check("moe_quant_mxfp8", rc)
 
 
+def moe_permute_quant_mxfp8(x, src_of, k, E, mode, q_row=None, s_row=None, q_col=None, s_col=None):
+    T, d = x.shape
+    rc = _lib().moe_permute_quant_mxfp8(_ptr(x), _ptr(src_of), T, k, E, d, src_of.shape[0], mode,
+                                        _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream())
+    _check("moe_permute_quant_mxfp8", rc)
+
+
 # ------------------------------------------------------------------ buffers
 class Buffers:
     """Device buffers of one forward + backward pass (plain torch allocations)."""
@@ -302,10 +310,10 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
     if mx:
         if gather:
             raise ValueError("the MXFP8 FC1 reads the quantized permuted copy: no row gather")
-        moe_permute(x, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.x_perm)
-        moe_quant_mxfp8(buf.x_perm, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, buf.x_q, buf.x_s, buf.xt_q,
-                        buf.xt_s)
-        moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h if store_h else None, buf.a,
+        # X_perm only as its MXFP8 copies: row-wise (FC1) and column-wise (FC1 wgrad)
+        moe_permute_quant_mxfp8(x, buf.src_of, buf.k, buf.E, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE,
+                                buf.x_q, buf.x_s, buf.xt_q, buf.xt_s)
+        moe_grouped_mlp_fwd(None, w1, w2, buf.offsets, buf.h if store_h else None, buf.a,
                             buf.y, fwd_stages, mx=buf.mx_fwd(), act=act)
     elif gather:
         moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h if store_h else None, buf.a, buf.y,
@@ -328,11 +336,11 @@ def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIG
     if mx:
         if x is not None:
             raise ValueError("the MXFP8 backward quantizes the permuted copies: no row gather")
-        moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
-        if dgrad2_mx:
-            moe_quant_mxfp8(buf.dy_u, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, buf.dy_q, buf.dy_s,
-                            buf.dyt_q, buf.dyt_s)
+        if dgrad2_mx:   # dY_u only as its MXFP8 copies
+            moe_permute_quant_mxfp8(dout, buf.src_of, buf.k, buf.E, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE,
+                                    buf.dy_q, buf.dy_s, buf.dyt_q, buf.dyt_s)
         else:
+            moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
             moe_quant_mxfp8(buf.dy_u, MOE_QUANT_COLWISE, None, None, buf.dyt_q, buf.dyt_s)
         if not buf.xt_from_forward:
             moe_quant_mxfp8(buf.x_perm, MOE_QUANT_COLWISE, None, None, buf.xt_q, buf.xt_s)

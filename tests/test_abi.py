@@ -131,6 +131,15 @@ def test_host_validation_returns_before_launch():
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x10,
                                  f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)
     assert rc == M.MOE_ERR_INVALID_ARG             # misaligned codes
+    # fused permute + quant: shape and capacity checks
+    rc = lib.moe_permute_quant_mxfp8(f, f, 8, 2, 4, 48, 1024, 3, f, f, f, f, None)
+    assert rc == M.MOE_ERR_UNSUPPORTED              # d % 32
+    rc = lib.moe_permute_quant_mxfp8(f, f, 8, 2, 4, 64, 256, 3, f, f, f, f, None)
+    assert rc == M.MOE_ERR_WORKSPACE                # M_cap below capacity
+    rc = lib.moe_permute_quant_mxfp8(f, None, 8, 2, 4, 64, 1024, 3, f, f, f, f, None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # no src_of
+    rc = lib.moe_permute_quant_mxfp8(f, f, 8, 2, 4, 64, 1024, 1, None, f, None, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # row-wise without codes
     # quant: bad mode / shape
     rc = lib.moe_quant_mxfp8(f, 1, 64, 64, 0, f, f, f, f, None)
     assert rc == M.MOE_ERR_INVALID_ARG

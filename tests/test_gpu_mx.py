@@ -269,3 +269,43 @@ def test_mx_fc1_forward_parity(M, wl, act):
     g = _gpu_quant(M, a_bits[:end], 1)
     assert np.array_equal(buf.a_q.cpu().numpy()[:end], g[0][0])
 
+
+PQ_CASES = [
+    W.small("pq-k1", T=700, k=1, E=4, d=256, n=64, seed=51, routing="zipf"),
+    W.small("pq-k3", T=333, k=3, E=6, d=96, n=64, seed=52, routing="normal"),
+    W.small("pq-empty", T=200, k=2, E=16, d=160, n=64, seed=53, routing="zipf"),
+]
+
+
+@pytest.mark.parametrize("wl", PQ_CASES, ids=[c.name for c in PQ_CASES])
+def test_permute_quant_bit_exact(M, wl):
+    """The fused permute + quantization equals the oracle's quantization of the
+    oracle's permutation, bit for bit, on every row of [0, M_cap) (rows past
+    the last region are zero codes), for k = 1 and k > 1 and partial column
+    tiles."""
+    print(f"permute-quant case {wl}", flush=True)
+    inp = W.make_inputs(wl)
+    M_cap = M.moe_capacity_rows(wl.T, wl.k, wl.E)
+    idx, w = O.route(inp["logits"], wl.k)
+    counts, offsets, row_of, src_of = O.layout(idx, wl.E, M_cap)
+    x = bf16_tensor(inp["x"])
+    so = torch.from_numpy(src_of).cuda()
+    d = wl.d
+    bufs = [torch.full(shape, 0xAB, dtype=U8, device="cuda")
+            for shape in ((M_cap, d), (M_cap, d // 32), (d, M_cap), (d, M_cap // 32))]
+    M.moe_permute_quant_mxfp8(x, so, wl.k, wl.E, 3, *bufs)
+    torch.cuda.synchronize()
+    xp = O.permute(O.from_bf16(inp["x"]), row_of, wl.k, M_cap)     # zero rows where src_of < 0
+    ref = O.quant_mxfp8(xp, rowwise=True, colwise=True)
+    for name, got, want in zip(("row codes", "row scales", "col codes", "col scales"), bufs, ref):
+        assert np.array_equal(got.cpu().numpy(), want), name
+    # row-wise only and column-wise only give the same bytes
+    for mode in (1, 2):
+        part = [torch.full_like(b_, 0xAB) for b_ in bufs]
+        M.moe_permute_quant_mxfp8(x, so, wl.k, wl.E, mode, *(part if mode == 3 else
+                                  (part[0], part[1], None, None) if mode == 1 else (None, None, part[2], part[3])))
+        torch.cuda.synchronize()
+        sel = (0, 1) if mode == 1 else (2, 3)
+        for i in sel:
+            assert np.array_equal(part[i].cpu().numpy(), ref[i]), (mode, i)
+
