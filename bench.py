@@ -204,6 +204,7 @@ def main():
     flops = 18.0 * M_rows * wl.d * wl.n
     fc1_flops = 4.0 * M_rows * wl.d * wl.n
     fc1_tf = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    fc1_peak = PEAK_MXFP8_TFLOPS if mx_mode else PEAK_BF16_TFLOPS   # the FC1 launch's own dtype
     value = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
           f"FC1+{glu} {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
@@ -244,12 +245,12 @@ def main():
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         },
         "roofline": {
-            "kernel": f"grouped_gemm FC1+{glu}",
+            "kernel": f"grouped_gemm FC1+{glu}" + (" on MXFP8 operands" if mx_mode else ""),
             "bound": "mfma",
             "achieved": round(fc1_tf, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": fc1_peak,
             "unit": "TFLOP/s",
-            "frac": round(fc1_tf / PEAK_BF16_TFLOPS, 4),
+            "frac": round(fc1_tf / fc1_peak, 4),
             "traffic": measured_traffic(wl.name) if act == M.MOE_ACT_SWIGLU else None,
             "traffic_unit": "bytes per launch",
         },
