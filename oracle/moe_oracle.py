@@ -263,6 +263,26 @@ GLU_ACTS = {
 }
 
 
+def srelu(v):
+    """Squared ReLU, relu(v)^2 [P1 problem and published-evidence sections: the
+    sReLU family of fused epilogues; the plain reading is the non-gated squared
+    ReLU, so FC1 then has n output columns instead of 2n]."""
+    r = np.maximum(v, 0.0)
+    return r * r
+
+
+def srelu_grad(v):
+    return 2.0 * np.maximum(v, 0.0)
+
+
+# non-gated activations: A = f(H) with H of width n
+PLAIN_ACTS = {"srelu": (srelu, srelu_grad)}
+
+
+def is_gated(act: str) -> bool:
+    return act in GLU_ACTS
+
+
 # --------------------------------------------------------------------------
 # O5/O6: per-expert FC1 + SwiGLU and FC2  [P1 problem and core-idea sections:
 # the GLU activation applied to the FC1 output inside the GEMM epilogue;
@@ -275,19 +295,21 @@ def expert_segments(counts, offsets):
 
 def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, rounding: bool = True,
                 act: str = "swiglu"):
-    """Grouped FC1 -> GLU (SwiGLU or GeGLU) -> FC2 over the ragged expert-major rows.
+    """Grouped FC1 -> GLU (SwiGLU or GeGLU) or sReLU -> FC2 over the ragged expert-major rows.
 
-    x_perm fp64 [M_cap, d], w1 fp64 [E, d, 2n] (interleaved), w2 fp64 [E, n, d].
+    x_perm fp64 [M_cap, d], w1 fp64 [E, d, 2n] (interleaved; [E, d, n] for the
+    non-gated sReLU, A = relu(H)^2), w2 fp64 [E, n, d].
     Returns H [M_cap, 2n] (bf16-rounded when stored), A [M_cap, n], Y [M_cap, d];
     rows outside the real segments are zero.
     A is computed from the unrounded FC1 output: A = act(gate) * up, act = silu
     (SwiGLU) or gelu (GeGLU).
     """
-    act_fn = GLU_ACTS[act][0]
+    gated = is_gated(act)
+    act_fn = (GLU_ACTS if gated else PLAIN_ACTS)[act][0]
     x_perm = np.asarray(x_perm, dtype=np.float64)
     M_cap, d = x_perm.shape
     E, _, n2 = w1.shape
-    n = n2 // 2
+    n = n2 // 2 if gated else n2
     H = np.zeros((M_cap, n2))
     A = np.zeros((M_cap, n))
     Y = np.zeros((M_cap, d))
@@ -295,8 +317,11 @@ def mlp_forward(x_perm, w1, w2, counts, offsets, g: int = GLU_INTERLEAVE, roundi
         if r1 == r0:
             continue
         h = x_perm[r0:r1] @ w1[e]
-        hg, hu = deinterleave(h, g)
-        a = _maybe_round(act_fn(hg) * hu, rounding)
+        if gated:
+            hg, hu = deinterleave(h, g)
+            a = _maybe_round(act_fn(hg) * hu, rounding)
+        else:
+            a = _maybe_round(act_fn(h), rounding)
         H[r0:r1] = _maybe_round(h, rounding)
         A[r0:r1] = a
         Y[r0:r1] = _maybe_round(a @ w2[e], rounding)
@@ -344,7 +369,8 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
     x_perm = np.asarray(x_perm, dtype=np.float64)
     M_cap, d = x_perm.shape
     E, _, n2 = w1.shape
-    n = n2 // 2
+    gated = is_gated(act)
+    n = n2 // 2 if gated else n2
     T = dout.shape[0]
     dout = np.asarray(dout, dtype=np.float64)
     rows = np.asarray(row_of, dtype=np.int64)
@@ -368,15 +394,20 @@ def mlp_backward(x_perm, w1, w2, H, Y, dout, topk_w, counts, offsets, row_of, sr
         if r1 == r0:
             continue
         da_u = dy_u[r0:r1] @ w2[e].T if dap is None else dap[r0:r1]   # dA' (unweighted)
-        hg, hu = deinterleave(H[r0:r1], g)
-        f, f_grad = GLU_ACTS[act]
-        fg = f(hg)
-        a = fg * hu
-        ds_row[r0:r1] = np.einsum("rc,rc->r", da_u, a)
         da = w_row[r0:r1, None] * da_u
-        dg = da * hu * f_grad(hg)
-        du = da * fg
-        dh = _maybe_round(interleave(dg, du, g), rounding)
+        if gated:
+            hg, hu = deinterleave(H[r0:r1], g)
+            f, f_grad = GLU_ACTS[act]
+            fg = f(hg)
+            a = fg * hu
+            dg = da * hu * f_grad(hg)
+            du = da * fg
+            dh = _maybe_round(interleave(dg, du, g), rounding)
+        else:
+            f, f_grad = PLAIN_ACTS[act]
+            a = f(H[r0:r1])
+            dh = _maybe_round(da * f_grad(H[r0:r1]), rounding)
+        ds_row[r0:r1] = np.einsum("rc,rc->r", da_u, a)
         aw = _maybe_round(w_row[r0:r1, None] * a, rounding)
         dH[r0:r1] = dh
         a_w[r0:r1] = aw
