@@ -72,7 +72,7 @@ def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
 
     def run(R):
         x = O.from_bf16(inp["x"][:R])
-        w1 = O.from_bf16(inp["w1"])
+        w1 = O.from_bf16(inp["w1"])       # [E, d, n] already for the non-gated sReLU
         w2 = O.from_bf16(inp["w2"])
         t0 = time.perf_counter()
         f = O.forward(x, inp["logits"][:R], w1, w2, wl.k, act=act)
@@ -86,7 +86,7 @@ def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
     R2 = int(min(wl.T, max(R, R * target_s / max(dt, 1e-3))))
     R2 = max(128, R2 // 128 * 128)
     dt2 = run(R2)
-    flops = 18.0 * R2 * wl.k * wl.d * wl.n
+    flops = (12.0 if act == "srelu" else 18.0) * R2 * wl.k * wl.d * wl.n
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": flops / dt2 / 1e12,
@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="balanced")
-    ap.add_argument("--act", choices=["swiglu", "geglu"], default="swiglu",
+    ap.add_argument("--act", choices=["swiglu", "geglu", "srelu"], default="swiglu",
                     help="gate activation of the GLU epilogues")
     ap.add_argument("--gather", action="store_true",
                     help="GEMMs read x and dO rows through src_of (no permuted copies)")
@@ -127,8 +127,12 @@ def main():
     M.load()
     wl = W.WORKLOADS[args.workload]
     mx_mode = args.workload == "mxfp8"
-    act = M.MOE_ACT_GEGLU if args.act == "geglu" else M.MOE_ACT_SWIGLU
-    glu = "GeGLU" if args.act == "geglu" else "SwiGLU"
+    act = {"swiglu": M.MOE_ACT_SWIGLU, "geglu": M.MOE_ACT_GEGLU, "srelu": M.MOE_ACT_SRELU}[args.act]
+    glu = {"swiglu": "SwiGLU", "geglu": "GeGLU", "srelu": "sReLU"}[args.act]
+    gated = args.act != "srelu"
+    if mx_mode and not gated:
+        print("the MXFP8 workload runs the gated (GLU) forms only", file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -138,12 +142,15 @@ def main():
         del src, dst
     t_gen = time.perf_counter()
     inp = W.make_inputs(wl)
+    if not gated:   # non-gated FC1: W1_e [d, n], the first n columns of the generated weights
+        inp = dict(inp)
+        inp["w1"] = np.ascontiguousarray(inp["w1"][:, :, :wl.n])
     print(f"[bench] inputs for {wl.name} generated in {time.perf_counter() - t_gen:.1f} s",
           file=sys.stderr, flush=True)
     torch.cuda.set_device(0)
     x, w1, w2, dout = (_t16(inp[key], torch) for key in ("x", "w1", "w2", "dout"))
     logits = torch.from_numpy(inp["logits"]).cuda()
-    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=mx_mode)
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=mx_mode, gated=gated)
     stream = torch.cuda.current_stream()
     mx = None
     if mx_mode:
@@ -201,8 +208,10 @@ def main():
     assert int(buf.err.item()) == 0
 
     M_rows = wl.T * wl.k
-    flops = 18.0 * M_rows * wl.d * wl.n
-    fc1_flops = 4.0 * M_rows * wl.d * wl.n
+    # FC1 is 2 M d n1 with n1 = 2n (gated) or n (sReLU); FC2, and each of the four backward
+    # GEMMs, match FC1 or FC2
+    fc1_flops = (4.0 if gated else 2.0) * M_rows * wl.d * wl.n
+    flops = 3.0 * fc1_flops + 3.0 * 2.0 * M_rows * wl.d * wl.n
     fc1_tf = fc1_flops / (fc1_ms * 1e-3) / 1e12
     fc1_peak = PEAK_MXFP8_TFLOPS if mx_mode else PEAK_BF16_TFLOPS   # the FC1 launch's own dtype
     value = flops / (ms * 1e-3) / 1e12
@@ -211,7 +220,8 @@ def main():
 
     if args.detail:
         buf.logits_for_detail = logits
-        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu, gather=args.gather)
+        _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu, gather=args.gather,
+                gated=gated)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,7 +270,7 @@ def main():
 
 
 def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0, glu="SwiGLU",
-            gather=False):
+            gather=False, gated=True):
     """Time each stage alone (stderr only)."""
     def timeit(fn):
         fn()
@@ -275,13 +285,14 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
 
     Mr = wl.T * wl.k
     d, n = wl.d, wl.n
+    g1 = 4.0 if gated else 2.0   # FC1-shaped GEMMs: 2 M d n1, n1 = 2n or n
     end = int(buf.offsets[-1].item())
     rows = [
         ("permute", lambda: M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm),
          None, 2.0 * wl.T * d + 2.0 * end * d + 4.0 * end),
         (f"FC1+{glu}", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a,
                                                      buf.y, M.MOE_STAGE_FC1, act=act),
-         4.0 * Mr * d * n, None),
+         g1 * Mr * d * n, None),
         ("FC2", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, buf.y,
                                               M.MOE_STAGE_FC2), 2.0 * Mr * d * n, None),
         ("combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out), None,
@@ -317,7 +328,7 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
     rows.append(("route bwd", lambda: M.moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits), None,
                  8.0 * wl.T * wl.E + 8.0 * Mr))
     for st, fl in ((M.MOE_STAGE_DGRAD2, 2.0 * Mr * d * n), (M.MOE_STAGE_WGRAD2, 2.0 * Mr * d * n),
-                   (M.MOE_STAGE_DGRAD1, 4.0 * Mr * d * n), (M.MOE_STAGE_WGRAD1, 4.0 * Mr * d * n)):
+                   (M.MOE_STAGE_DGRAD1, g1 * Mr * d * n), (M.MOE_STAGE_WGRAD1, g1 * Mr * d * n)):
         xa, da, gflag = (x, dout, M.MOE_GATHER_ROWS) if gather else (buf.x_perm, buf.dy_u, 0)
         rows.append((f"bwd stage 0x{st:02x}", (lambda s=st, xa=xa, da=da, gflag=gflag: M.moe_grouped_mlp_bwd(
             xa, w1, w2, buf.h, da, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,

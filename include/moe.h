@@ -67,9 +67,12 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-3)    /* workspace or M_cap too small           */
 #define MOE_ERR_LAUNCH (-4)       /* a kernel launch reported an error      */
 
-/* activation of the gated MLP */
+/* activation of the expert MLP */
 #define MOE_ACT_SWIGLU 0       /* silu(gate) * up, silu(x) = x / (1 + e^-x) */
 #define MOE_ACT_GEGLU 1        /* gelu(gate) * up, gelu(x) = x * Phi(x) (exact, erf form) */
+#define MOE_ACT_SRELU 2        /* relu(h)^2, non-gated: FC1 has n columns, w1 [E, d, n],
+                                  h and dh [M_cap, n], dw1 [E, d, n] [P1, problem and
+                                  published-evidence sections: the sReLU family] */
 
 /* stage bits of moe_grouped_mlp_fwd / moe_grouped_mlp_bwd */
 #define MOE_STAGE_FC1 0x01     /* H = X_perm W1_e, A = GLU(H)               */
@@ -230,7 +233,10 @@ typedef struct moe_mx_fwd {
  *   optionally MOE_GATHER_ROWS: x_perm is then x [T, d] and FC1 reads its
  *   rows through src_of [M_cap] (T, k: the routing shape; both are ignored
  *   without the bit; T * d * 2 < 2^31).
- * Requires d % 64 == 0, n % 64 == 0, act MOE_ACT_SWIGLU or MOE_ACT_GEGLU,
+ * With act = MOE_ACT_SRELU the MLP is non-gated: FC1 = X_perm[R_e] W1_e with
+ * w1 [E, d, n], A = bf16(relu(H)^2), h [M_cap, n]; no MXFP8 form (mx must be
+ * NULL).
+ * Requires d % 64 == 0, n % 64 == 0, act MOE_ACT_SWIGLU, MOE_ACT_GEGLU or MOE_ACT_SRELU,
  * M_cap % 128 == 0, M_cap * max(d, 2n) * 2 < 2^31 and d * 2n * 2 < 2^31
  * (operands are addressed with 32-bit byte offsets); 16-byte aligned
  * pointers. Otherwise MOE_ERR_UNSUPPORTED.
@@ -279,6 +285,8 @@ typedef struct moe_mx_bwd {
  *   WGRAD2: dW2_e = A'[R_e]^T dY_u[R_e] (fp32; exactly 0 for empty experts).
  *   DGRAD1: dX_perm[R_e] = bf16(dH[R_e] W1_e^T).
  *   WGRAD1: dW1_e = X_perm[R_e]^T dH[R_e] (fp32, interleaved like w1).
+ *   Non-gated act = MOE_ACT_SRELU: dH = bf16(w dA' * 2 relu(h)), A' = w relu(h)^2,
+ *   dS partials += dA' . relu(h)^2; h, dh [M_cap, n], w1 and dw1 [E, d, n].
  *   dy_u = moe_permute of dO (unweighted). Stages run in the order above.
  *   With MOE_GATHER_ROWS in stages, x_perm is x [T, d] and dy_u is dO [T, d]
  *   (un-permuted) and every GEMM reads their rows through src_of.

@@ -20,11 +20,12 @@ int64_t capacity(int T, int k, int E) {
 // Shapes of the grouped MLP that the kernels support.
 int check_mlp_shape(int E, int d, int n, int64_t M_cap, int act) {
     if (E <= 0 || E > MOE_MAX_EXPERTS || d <= 0 || n <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
-    if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GEGLU) return MOE_ERR_UNSUPPORTED;
+    if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GEGLU && act != MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;
     if (d % 64 || n % 64 || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
     // the GEMMs address operands with 32-bit buffer offsets (bytes)
-    const int64_t widest = d > 2 * n ? d : 2 * n;
-    if (M_cap * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * 2 * n * 2 >= ((int64_t)1 << 31))
+    const int64_t n1 = act == MOE_ACT_SRELU ? n : 2 * n;
+    const int64_t widest = d > n1 ? d : n1;
+    if (M_cap * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * n1 * 2 >= ((int64_t)1 << 31))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -127,6 +128,7 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     moe::GatherSpec gx;
     if ((rc = gather_spec(stages, src_of, T, k, E, d, gx))) return rc;
     if (mx) {
+        if (act == MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;  // MXFP8 copies exist for the GLU forms
         if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
         if (!mx->a_q || !mx->a_s || !aligned16(mx->a_q) || !aligned16(mx->a_s)) return MOE_ERR_INVALID_ARG;
         if ((mx->at_q == nullptr) != (mx->at_s == nullptr)) return MOE_ERR_INVALID_ARG;
@@ -214,6 +216,8 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if (!dw1 || !aligned16(dw1)) return MOE_ERR_INVALID_ARG;
         if (!mx && (!x_perm || !dh || !aligned16(x_perm) || !aligned16(dh))) return MOE_ERR_INVALID_ARG;
     }
+    if (mx && act == MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;
+    const int n1 = act == MOE_ACT_SRELU ? n : 2 * n;  // FC1 width
     if (mx) {
         auto ok = [](const void* p, const void* q) { return p && q && aligned16(p); };
         if ((stages & MOE_STAGE_DGRAD2) &&
@@ -250,13 +254,13 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     if (stages & MOE_STAGE_DGRAD1) {
         const int rc1 = mx ? moe::launch_mx_ragged_m(mx->dh_q, mx->dh_s, mx->w1_q, mx->w1_s, offsets, E, d,
                                                       2 * n, M_cap, dx_perm, s)
-                           : moe::launch_dgrad1(dh, w1, offsets, E, d, n, M_cap, dx_perm, s);
+                           : moe::launch_dgrad1(dh, w1, offsets, E, d, n1, M_cap, dx_perm, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_WGRAD1) {
         const int rc1 = mx ? moe::launch_mx_wgrad(mx->xt_q, mx->xt_s, d, mx->dht_q, mx->dht_s, 2 * n, offsets,
                                                    E, M_cap, dw1, s)
-                           : moe::launch_wgrad(x_perm, d, dh, 2 * n, offsets, E, 1, gs, dw1, s);
+                           : moe::launch_wgrad(x_perm, d, dh, n1, offsets, E, 1, gs, dw1, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     return MOE_OK;

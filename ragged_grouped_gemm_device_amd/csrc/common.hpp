@@ -67,6 +67,15 @@ __device__ __forceinline__ void glu_gate_grad(float x, float& f, float& df) {
     }
 }
 
+// Non-gated activation (ACT == 2: squared ReLU, relu(x)^2) and its derivative 2 relu(x).
+template <int ACT>
+__device__ __forceinline__ void plain_act_grad(float x, float& f, float& df) {
+    static_assert(ACT == 2, "squared ReLU only");
+    const float r = fmaxf(x, 0.f);
+    f = r * r;
+    df = 2.f * r;
+}
+
 // Unpack 4 bf16 held in a uint2 into floats.
 __device__ __forceinline__ void unpack_bf16x4(uint2 v, float* f) {
     f[0] = __uint_as_float(v.x << 16);

@@ -44,7 +44,11 @@ namespace moe {
 constexpr int BK = 64;                    // K elements per LDS slab
 constexpr int kLoads = BM * BK * 2 / (kThreads * 16);  // 16-byte copies per thread per slab
 
-enum Epi { EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4, EPI_DGLU_MX = 5 };
+enum Epi {
+    EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4, EPI_DGLU_MX = 5,
+    EPI_ACT = 6,   // non-gated activation (sReLU): H and A = f(H), same columns
+    EPI_DACT = 7,  // its backward: dH = w dA' f'(H), A' = w f(H), dS partials
+};
 
 struct GemmArgs {
     const uint16_t* A;  // activations (token rows)
@@ -697,6 +701,73 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             }
         });
+    } else if constexpr (EPI == EPI_ACT) {
+        // non-gated: A[m, c] = f(H[m, c]) from the fp32 accumulator, H stored when asked
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            if (m < row_end) {
+                static_for<TNW>([&](auto J) {
+                    const int c0 = n0 + wn * WN + 32 * J;
+                    if (c0 < p.N) {
+                        static_for<4>([&](auto Q) {
+                            const int c = c0 + 8 * Q + 4 * h;
+                            float av[4];
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                float f, df;
+                                plain_act_grad<ACT>(acc[I][J][4 * Q + s], f, df);
+                                av[s] = f;
+                            }
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + c) =
+                                make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+                            if (p.out0)
+                                *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) =
+                                    make_uint2(pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]),
+                                               pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]));
+                        });
+                    }
+                });
+            }
+        });
+    } else if constexpr (EPI == EPI_DACT) {
+        // acc = dA' (unweighted) over columns c; H [M, n] holds the pre-activation
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            const bool row_ok = m < row_end;
+            float w = 0.f;
+            if (row_ok) {
+                const int src = p.src_of[m];
+                w = src >= 0 ? p.topk_w[src] : 0.f;
+            }
+            float dsum = 0.f;
+            if (row_ok) {
+                static_for<TNW>([&](auto J) {
+                    const int c0 = n0 + wn * WN + 32 * J;
+                    if (c0 < p.N) {
+                        static_for<4>([&](auto Q) {
+                            const int c = c0 + 8 * Q + 4 * h;
+                            float hv[4], dh[4], aw[4];
+                            unpack_bf16x4(*(const uint2*)(p.aux + (int64_t)m * p.ld_aux + c), hv);
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) {
+                                float f, df;
+                                plain_act_grad<ACT>(hv[s], f, df);
+                                const float dap = acc[I][J][4 * Q + s];
+                                dsum = fmaf(dap, f, dsum);
+                                dh[s] = w * dap * df;
+                                aw[s] = w * f;
+                            }
+                            *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) =
+                                make_uint2(pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3]));
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + c) =
+                                make_uint2(pack_bf16x2(aw[0], aw[1]), pack_bf16x2(aw[2], aw[3]));
+                        });
+                    }
+                });
+            }
+            dsum += __shfl_xor(dsum, 32, 64);  // the partner lane holds the other half
+            if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
+        });
     } else if constexpr (EPI == EPI_GLU) {
         // columns come in (gate 32, up 32) pairs: tiles j = 2u (gate), 2u+1 (up)
         static_for<4>([&](auto I) {
@@ -910,6 +981,13 @@ int ds_partials_per_row(int n) { return (BN / WN) * ((n + BN - 1) / BN); }
 // A GLU-epilogue launch with the activation and gather chosen at run time.
 template <bool B_KMAJ, int EPI>
 static int run_glu(const GemmArgs& g, int act, bool gather, int64_t tile_bound, hipStream_t s) {
+    if constexpr (EPI == EPI_GLU || EPI == EPI_DGLU) {
+        if (act == 2) {  // non-gated squared ReLU
+            constexpr int EA = EPI == EPI_GLU ? EPI_ACT : EPI_DACT;
+            return gather ? run<false, true, B_KMAJ, EA, 2, 1>(g, tile_bound, s)
+                          : run<false, true, B_KMAJ, EA, 2, 0>(g, tile_bound, s);
+        }
+    }
     if (gather)
         return act ? run<false, true, B_KMAJ, EPI, 1, 1>(g, tile_bound, s)
                    : run<false, true, B_KMAJ, EPI, 0, 1>(g, tile_bound, s);
@@ -928,14 +1006,15 @@ static void set_gather(GemmArgs& g, const GatherSpec& gs) {
 int launch_fc1_glu(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E, int d,
                    int n, int64_t M_cap, int act, const GatherSpec& gx, uint16_t* h, uint16_t* a,
                    hipStream_t s) {
+    const int n1 = act == 2 ? n : 2 * n;  // FC1 width: gate+up interleaved, or n (non-gated)
     GemmArgs g = zero_args();
     g.A = x_perm; g.lda = d;
-    g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;
-    g.offsets = offsets; g.E = E; g.N = 2 * n; g.K = d;
-    g.out0 = h; g.ld0 = 2 * n;
+    g.B = w1; g.ldb = n1; g.b_estride = (int64_t)d * n1;
+    g.offsets = offsets; g.E = E; g.N = n1; g.K = d;
+    g.out0 = h; g.ld0 = n1;
     g.out1 = a; g.ld1 = n;
     set_gather(g, gx);
-    return run_glu<false, EPI_GLU>(g, act, gx.src_of != nullptr, ragged_m_grid(M_cap, E, 2 * n), s);
+    return run_glu<false, EPI_GLU>(g, act, gx.src_of != nullptr, ragged_m_grid(M_cap, E, n1), s);
 }
 
 int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t* offsets, int E,
@@ -989,11 +1068,12 @@ int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t*
     GemmArgs g = zero_args();
     g.A = dy_u; g.lda = d;
     g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;  // row c of W2_e is column c of W2_e^T
+    const int n1 = act == 2 ? n : 2 * n;  // width of H and dH
     g.offsets = offsets; g.E = E; g.N = n; g.K = d;
-    g.out0 = dh; g.ld0 = 2 * n;
+    g.out0 = dh; g.ld0 = n1;
     g.out1 = a_w; g.ld1 = n;
     g.outf = ds_part; g.n_part = ds_partials_per_row(n);
-    g.aux = h; g.ld_aux = 2 * n;
+    g.aux = h; g.ld_aux = n1;
     g.topk_w = topk_w; g.src_of = src_of;
     set_gather(g, gdy);
     return run_glu<true, EPI_DGLU>(g, act, gdy.src_of != nullptr, ragged_m_grid(M_cap, E, n), s);
@@ -1052,11 +1132,11 @@ int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, 
 }
 
 int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets, int E, int d,
-                  int n, int64_t M_cap, uint16_t* dx_perm, hipStream_t s) {
+                  int n1, int64_t M_cap, uint16_t* dx_perm, hipStream_t s) {
     GemmArgs g = zero_args();
-    g.A = dh; g.lda = 2 * n;
-    g.B = w1; g.ldb = 2 * n; g.b_estride = (int64_t)d * 2 * n;  // row r of W1_e = column r of W1_e^T
-    g.offsets = offsets; g.E = E; g.N = d; g.K = 2 * n;
+    g.A = dh; g.lda = n1;
+    g.B = w1; g.ldb = n1; g.b_estride = (int64_t)d * n1;  // row r of W1_e = column r of W1_e^T
+    g.offsets = offsets; g.E = E; g.N = d; g.K = n1;
     g.out0 = dx_perm; g.ld0 = d;
     return run<false, true, true, EPI_BF16>(g, ragged_m_grid(M_cap, E, d), s);
 }

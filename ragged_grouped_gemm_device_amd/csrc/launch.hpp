@@ -80,8 +80,9 @@ int launch_dgrad2_dglu_mxin(const uint8_t* dy_q, const uint8_t* dy_s, const uint
                             uint8_t* awt_q, uint8_t* awt_s, hipStream_t s);
 int launch_ds_reduce(const float* ds_part, const int32_t* row_of, int T, int k, int n,
                      float* ds, hipStream_t s);
+// n1: the FC1 width (2n gated, n non-gated), the K of this GEMM
 int launch_dgrad1(const uint16_t* dh, const uint16_t* w1, const int32_t* offsets, int E, int d,
-                  int n, int64_t M_cap, uint16_t* dx_perm, hipStream_t s);
+                  int n1, int64_t M_cap, uint16_t* dx_perm, hipStream_t s);
 // gather: 0 none, 1 = the A operand (act) is gathered, 2 = the B operand (grad)
 int launch_wgrad(const uint16_t* act, int Ma, const uint16_t* grad, int Nb, const int32_t* offsets,
                  int E, int gather, const GatherSpec& gs, float* dw, hipStream_t s);

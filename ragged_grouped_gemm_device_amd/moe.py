@@ -26,6 +26,7 @@ MOE_GLU_INTERLEAVE = 32
 MOE_MAX_EXPERTS = 1024
 MOE_ACT_SWIGLU = 0
 MOE_ACT_GEGLU = 1
+MOE_ACT_SRELU = 2   # non-gated relu(h)^2: FC1 width n
 MOE_STAGE_FC1 = 0x01
 MOE_STAGE_FC2 = 0x02
 MOE_STAGE_DGRAD2 = 0x04
@@ -169,7 +170,8 @@ def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD,
                         act=MOE_ACT_SWIGLU, src_of=None, k=0):
     """With MOE_GATHER_ROWS in stages, x_perm is the un-permuted x [T, d] and src_of, k are
     required."""
-    E, d, n2 = w1.shape
+    E, d, n1 = w1.shape
+    n = n1 if act == MOE_ACT_SRELU else n1 // 2
     M_cap = a.shape[0]
     T = x_perm.shape[0] if (stages & MOE_GATHER_ROWS) else 0
     mxp = None
@@ -177,7 +179,7 @@ def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD,
         mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in MX_FWD_FIELDS])
         mxp = C.byref(mxs)
     rc = _lib().moe_grouped_mlp_fwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(offsets), _ptr(src_of), T,
-                                    k, E, d, n2 // 2, M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y),
+                                    k, E, d, n, M_cap, act, stages, _ptr(h), _ptr(a), _ptr(y),
                                     mxp, _stream())
     _check("moe_grouped_mlp_fwd", rc)
 
@@ -187,7 +189,11 @@ def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets
                         mx=None, shape=None):
     """mx: dict of the moe_mx_bwd fields (missing ones pass NULL). shape = (E, d, n) when w1
     is not given (an MX call that reads only the quantized copies)."""
-    E, d, n2 = w1.shape if w1 is not None else (shape[0], shape[1], 2 * shape[2])
+    if w1 is not None:
+        E, d, n1 = w1.shape
+        n = n1 if act == MOE_ACT_SRELU else n1 // 2
+    else:
+        E, d, n = shape
     mxp = None
     if mx is not None:
         mxp = C.byref(moe_mx_bwd(*[_ptr(mx.get(key)) for key in MX_BWD_FIELDS]))
@@ -195,7 +201,7 @@ def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets
     M_cap = src_of.shape[0]
     rc = _lib().moe_grouped_mlp_bwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(h), _ptr(dy_u),
                                     _ptr(topk_w), _ptr(src_of), _ptr(row_of), _ptr(offsets), T, k,
-                                    E, d, n2 // 2, M_cap, act, stages, _ptr(dh), _ptr(a_w), _ptr(ds),
+                                    E, d, n, M_cap, act, stages, _ptr(dh), _ptr(a_w), _ptr(ds),
                                     _ptr(dx_perm), _ptr(dw1), _ptr(dw2), _ptr(workspace),
                                     0 if workspace is None else workspace.numel() * workspace.element_size(),
                                     mxp, _stream())
@@ -223,7 +229,8 @@ def moe_permute_quant_mxfp8(x, src_of, k, E, mode, q_row=None, s_row=None, q_col
 class Buffers:
     """Device buffers of one forward + backward pass (plain torch allocations)."""
 
-    def __init__(self, T: int, k: int, E: int, d: int, n: int, device="cuda", mx: bool = False):
+    def __init__(self, T: int, k: int, E: int, d: int, n: int, device="cuda", mx: bool = False,
+                 gated: bool = True):
         dev = torch.device(device)
         bf, i32, f32, u8 = torch.bfloat16, torch.int32, torch.float32, torch.uint8
         self.T, self.k, self.E, self.d, self.n = T, k, E, d, n
@@ -237,17 +244,18 @@ class Buffers:
         self.err = torch.zeros(1, dtype=i32, device=dev)
         self.route_ws = torch.empty(max(16, moe_route_workspace_bytes(T, k, E)), dtype=u8, device=dev)
         self.x_perm = torch.empty(M, d, dtype=bf, device=dev)
-        self.h = torch.empty(M, 2 * n, dtype=bf, device=dev)
+        n1 = 2 * n if gated else n   # FC1 width (non-gated sReLU: n)
+        self.h = torch.empty(M, n1, dtype=bf, device=dev)
         self.a = torch.empty(M, n, dtype=bf, device=dev)
         self.y = torch.empty(M, d, dtype=bf, device=dev)
         self.out = torch.empty(T, d, dtype=bf, device=dev)
         self.dy_u = torch.empty(M, d, dtype=bf, device=dev)
-        self.dh = torch.empty(M, 2 * n, dtype=bf, device=dev)
+        self.dh = torch.empty(M, n1, dtype=bf, device=dev)
         self.a_w = torch.empty(M, n, dtype=bf, device=dev)
         self.ds = torch.empty(T, k, dtype=f32, device=dev)
         self.dx_perm = torch.empty(M, d, dtype=bf, device=dev)
         self.dx = torch.empty(T, d, dtype=bf, device=dev)
-        self.dw1 = torch.empty(E, d, 2 * n, dtype=f32, device=dev)
+        self.dw1 = torch.empty(E, d, n1, dtype=f32, device=dev)
         self.dw2 = torch.empty(E, n, d, dtype=f32, device=dev)
         self.dlogits = torch.empty(T, E, dtype=f32, device=dev)
         self.bwd_ws = torch.empty(max(16, moe_mlp_bwd_workspace_bytes(n, M)), dtype=u8, device=dev)

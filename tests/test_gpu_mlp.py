@@ -125,6 +125,45 @@ def test_forward_backward_parity(M, wl, act, gather):
         assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
 
 
+# non-gated squared ReLU: W1_e [d, n] (the first n columns of the generated W1)
+SRELU_CASES = [CASES[0], CASES[1], CASES[2], CASES[4]]
+
+
+@pytest.mark.parametrize("wl,gather", [(c, False) for c in SRELU_CASES] + [(CASES[1], True)],
+                         ids=[c.name for c in SRELU_CASES] + [CASES[1].name + "-gather"])
+def test_srelu_forward_backward_parity(M, wl, gather):
+    print(f"mlp case {wl} act=srelu gather={gather}", flush=True)
+    inp = dict(W.make_inputs(wl))
+    inp["w1"] = np.ascontiguousarray(inp["w1"][:, :, :wl.n])
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, gated=False)
+    _poison(buf)
+    x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
+    dout = bf16_tensor(inp["dout"])
+    M.forward(buf, x, f32_tensor(inp["logits"]), w1, w2, act=M.MOE_ACT_SRELU, gather=gather)
+    M.backward(buf, dout, w1, w2, act=M.MOE_ACT_SRELU, x=x if gather else None)
+    torch.cuda.synchronize()
+    f, b = _oracle(wl, inp, "srelu")
+    end = int(f["offsets"][-1])
+    assert buf.h.shape[1] == wl.n
+    _check("H", bf16_values(buf.h), f["H"], end)
+    _check("A", bf16_values(buf.a), f["A"], end)
+    _check("Y", bf16_values(buf.y), f["Y"], end)
+    _check("out", bf16_values(buf.out), f["out"])
+    _check("dS", buf.ds.cpu().numpy(), b["dS"])
+    _check("dH", bf16_values(buf.dh), b["dH"], end)
+    _check("A'", bf16_values(buf.a_w), b["a_w"], end)
+    _check("dX_perm", bf16_values(buf.dx_perm), b["dx_perm"], end)
+    _check("dX", bf16_values(buf.dx), b["dx"])
+    _check("dW1", buf.dw1.cpu().numpy(), b["dW1"])
+    _check("dW2", buf.dw2.cpu().numpy(), b["dW2"])
+    pad = f["src_of"][:end] < 0
+    for name in ("h", "a", "y", "dh", "a_w", "dx_perm"):
+        v = bf16_bits(getattr(buf, name))[:end][pad]
+        assert np.all((v == 0) | (v == 0x8000)), name
+    for e in np.nonzero(f["counts"] == 0)[0]:
+        assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
+
+
 def test_all_tokens_to_one_expert(M):
     wl = W.small("one", T=520, k=1, E=8, d=128, n=128, seed=31)
     inp = W.make_inputs(wl)
