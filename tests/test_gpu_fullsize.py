@@ -170,27 +170,95 @@ def test_fullsize_forward_backward(M, name, gather):
         assert torch.all(buf.dw1[e] == 0) and torch.all(buf.dw2[e] == 0)
 
 
-def test_fullsize_mxfp8_forward(M):
+def _oracle_tokens_mx(wl, inp, ts):
+    """The oracle's MXFP8 forward and backward (every GEMM on MXFP8) on the tokens ts.
+    Row-wise copies are per row, so these rows equal the full-size ones; the
+    column-wise copies (wgrads) mix rows and are checked separately."""
+    idx, w = O.route(inp["logits"][ts], wl.k)
+    used = np.unique(idx)
+    remap = np.full(wl.E, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    w1 = O.from_bf16(inp["w1"][used])
+    w2 = O.from_bf16(inp["w2"][used])
+    M_cap = O.capacity_rows(len(ts), wl.k, used.size)
+    counts, offsets, row_of, src_of = O.layout(remap[idx], used.size, M_cap)
+    x_perm = O.permute(O.from_bf16(inp["x"][ts]), row_of, wl.k, M_cap)
+    f = O.mlp_forward_mx(x_perm, w1, w2, counts, offsets)
+    r = dict(idx=idx, w=w, row_of=row_of, used=used, **f)
+    r["out"] = O.combine(f["Y"], row_of, wl.k, w)
+    b = O.mlp_backward_mx(x_perm, w1, w2, f["H"], f["Y"], O.from_bf16(inp["dout"][ts]), w, counts,
+                          offsets, row_of, src_of, wl.k, dgrad2_mx=True)
+    for key in ("dS", "dH", "a_w", "dx_perm", "dx"):
+        r[key] = b[key]
+    return r
+
+
+def test_fullsize_mxfp8_step(M):
+    """The mxfp8 workload as bench.py runs it: fused permute + quantization,
+    MX FC1 + SwiGLU + MXFP8 A, MX FC2, combine, then the MX FC2 dgrad + dGLU
+    with MXFP8 dH / A', MX wgrads and MX FC1 dgrad, and the router backward."""
     wl = W.WORKLOADS["mxfp8"]
-    print(f"full-size case {wl}", flush=True)
+    print(f"full-size case {wl} (every GEMM on MXFP8)", flush=True)
     inp = W.make_inputs(wl)
-    buf = _gpu(M, wl, inp, mx=True)
+    buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
+    x, w1, w2, dout = (bf16_tensor(inp[key]) for key in ("x", "w1", "w2", "dout"))
+    logits = f32_tensor(inp["logits"])
+    buf.quantize_weights(w1, w2)
+    M.forward(buf, x, logits, w1, w2, mx=True)
+    M.backward(buf, dout, w1, w2, logits=logits, mx=True)
+    torch.cuda.synchronize()
     idx, w = O.route(inp["logits"], wl.k)
     M_cap = O.capacity_rows(wl.T, wl.k, wl.E)
     counts, offsets, row_of, src_of = O.layout(idx, wl.E, M_cap)
     assert np.array_equal(buf.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(buf.row_of.cpu().numpy(), row_of)
     rng = np.random.default_rng(wl.seed)
-    # tokens of two experts keep the oracle's W2 quantization small
+    # tokens of two experts keep the oracle's weight quantization small
     ts = np.concatenate([rng.choice(np.arange(0, 4096), 5, replace=False),
                          rng.choice(np.arange(28672, 32768), 5, replace=False)])
     ts.sort()
-    r = _oracle_tokens(wl, inp, ts, mx=True)
-    for i, e in enumerate(r["used"]):
+    r = _oracle_tokens_mx(wl, inp, ts)
+    for i, e in enumerate(r["used"]):   # weight copies of the sampled experts
+        assert np.array_equal(buf.w1t_q[e].cpu().numpy(), r["w1t_q"][i])
         assert np.array_equal(buf.w2t_q[e].cpu().numpy(), r["w2t_q"][i])
-        assert np.array_equal(buf.w2t_s[e].cpu().numpy(), r["w2t_s"][i])
     g_rows = row_of.reshape(wl.T, wl.k)[ts].reshape(-1)
-    got = bf16_values(buf.y[torch.from_numpy(g_rows).long().cuda()])
-    e1 = rel_err(got, r["Y"][r["row_of"]])
-    e2 = rel_err(bf16_values(buf.out[torch.from_numpy(ts).long().cuda()]), r["out"])
-    print(f"  MX Y: {e1:.3e}  out: {e2:.3e}", flush=True)
-    assert e1 <= 6e-2 and e2 <= 6e-2
+    gsel = torch.from_numpy(g_rows).long().cuda()
+    o_rows = r["row_of"]
+    assert np.array_equal(buf.x_q[gsel].cpu().numpy(), r["x_q"][o_rows])   # row-wise X copy
+    for key, gt, ref, tol in (("H", buf.h, r["H"], 2e-2), ("A", buf.a, r["A"], 2e-2),
+                              ("Y", buf.y, r["Y"], 6e-2), ("dH", buf.dh, r["dH"], 2e-2),
+                              ("A'", buf.a_w, r["a_w"], 2e-2), ("dX_perm", buf.dx_perm, r["dx_perm"], 6e-2)):
+        err = rel_err(bf16_values(gt[gsel]), ref[o_rows])
+        print(f"  {key}: {err:.3e}", flush=True)
+        assert err <= tol, key
+    tsel = torch.from_numpy(ts).long().cuda()
+    for key, got, ref, tol in (("out", bf16_values(buf.out[tsel]), r["out"], 6e-2),
+                               ("dX", bf16_values(buf.dx[tsel]), r["dx"], 6e-2),
+                               ("dS", buf.ds[tsel].cpu().numpy(), r["dS"], 2e-2)):
+        err = rel_err(got, ref)
+        print(f"  {key}: {err:.3e}", flush=True)
+        assert err <= tol, key
+    # column-wise copies of two 32-row blocks of expert 0: X from the oracle's
+    # permutation, dH and A' from the GPU's own bf16 values (bit-exact)
+    xp = O.from_bf16(inp["x"][:4096])          # expert 0 holds tokens 0..4095 in order
+    for blk in (0, 77):
+        r0 = 32 * blk
+        rows = slice(r0, r0 + 32)
+        _, _, q, sc = O.quant_mxfp8(xp[rows], rowwise=False, colwise=True)
+        assert np.array_equal(buf.xt_q[:, rows].cpu().numpy(), q)
+        assert np.array_equal(buf.xt_s[:, blk].cpu().numpy(), sc[:, 0])
+        _, _, q, sc = O.quant_mxfp8(bf16_values(buf.dh[rows]), rowwise=False, colwise=True)
+        assert np.array_equal(buf.dht_q[:, rows].cpu().numpy(), q)
+        _, _, q, sc = O.quant_mxfp8(bf16_values(buf.a_w[rows]), rowwise=False, colwise=True)
+        assert np.array_equal(buf.awt_q[:, rows].cpu().numpy(), q)
+    # MX wgrads of one 64-column block of expert 0, on the GPU's own codes
+    e, R = 0, slice(0, 4096)
+    cb = slice(64 * 5, 64 * 6)
+    xt = O.mx_dequant(buf.xt_q[:, R].cpu().numpy(), buf.xt_s[:, :128].cpu().numpy())
+    dht = O.mx_dequant(buf.dht_q[cb, R].cpu().numpy(), buf.dht_s[cb, :128].cpu().numpy())
+    e1 = rel_err(buf.dw1[e][:, cb].cpu().numpy(), xt @ dht.T)
+    awt = O.mx_dequant(buf.awt_q[32 * 5:32 * 6, R].cpu().numpy(), buf.awt_s[32 * 5:32 * 6, :128].cpu().numpy())
+    dyt = O.mx_dequant(buf.dyt_q[:, R].cpu().numpy(), buf.dyt_s[:, :128].cpu().numpy())
+    e2 = rel_err(buf.dw2[e][32 * 5:32 * 6, :].cpu().numpy(), awt @ dyt.T)
+    print(f"  MX dW1 block (own codes): {e1:.3e}  MX dW2 block: {e2:.3e}", flush=True)
+    assert e1 <= 1e-3 and e2 <= 1e-3
