@@ -1,6 +1,7 @@
 // Routing and ragged layout kernels (gfx950).
 //
-// route_topk_kernel: softmax over E + top-k per token, one wavefront per token.
+// route_topk_kernel: softmax over E + top-k per token, one group of lanes per
+//   token (8, 16, 32 or 64 lanes, the smallest that holds E, 64 beyond 32).
 //   [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, section on ragged
 //   tensors: a learned router activates each token's top-K experts.]
 // route_bwd_kernel: the router's softmax backward from dS.
@@ -17,25 +18,31 @@
 
 namespace moe {
 
-constexpr int kMaxPerLane = MOE_MAX_E / 64;   // logits held per lane (E <= 1024)
+constexpr int kMaxPerLane = MOE_MAX_E / 64;   // logits per lane of a full wavefront (E <= 1024)
 
+// One group of G lanes per token (G = 8, 16 or 32 when E <= G, one logit per
+// lane; G = 64 otherwise, up to MOE_MAX_E / 64 logits per lane), so small
+// expert counts do not leave most of a wavefront idle. Reductions are lane
+// exchanges inside the group.
+template <int G, int PER>
 __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int renorm,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
                                                          int32_t* __restrict__ err_word) {
     const int lane = lane_id();
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+    const int gl = lane % G;  // lane inside the token's group
+    const int t = (int)(((int64_t)blockIdx.x * 256 + threadIdx.x) / G);
+    const bool active = t < T;
     const float* row = logits + (int64_t)t * E;
-    float v[kMaxPerLane];
+    float v[PER];
     bool bad = false;
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
+    for (int i = 0; i < PER; ++i) {
+        const int e = gl + G * i;
         float x = -INFINITY;
-        if (e < E) {
+        if (active && e < E) {
             x = row[e];
             if (!isfinite(x)) {
                 bad = true;
@@ -47,12 +54,13 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
     }
     if (__ballot(bad) != 0ull && lane == 0 && err_word) atomicOr(err_word, MOE_ERRBIT_NONFINITE_LOGIT);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    for (int o = G / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-        if (lane + 64 * i < E && v[i] > -INFINITY) s += expf(v[i] - mx);
-    s = wave_sum(s);
+    for (int i = 0; i < PER; ++i)
+        if (gl + G * i < E && v[i] > -INFINITY) s += expf(v[i] - mx);
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
     if (!(mx > -INFINITY)) s = 1.f;  // every logit non-finite: weights become 0
 
     uint32_t taken = 0;  // bit i: v[i] already selected
@@ -62,15 +70,15 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
         float bv = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + 64 * i;
+        for (int i = 0; i < PER; ++i) {
+            const int e = gl + G * i;
             if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7fffffff)) {
                 bv = v[i];
                 bi = e;
             }
         }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
+        for (int o = G / 2; o > 0; o >>= 1) {
             const float ov = __shfl_xor(bv, o, 64);
             const int oi = __shfl_xor(bi, o, 64);
             if (ov > bv || (ov == bv && oi < bi)) {
@@ -78,16 +86,16 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
                 bi = oi;
             }
         }
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if ((bi % G) == gl) taken |= 1u << (bi / G);
         const float p = (bv > -INFINITY) ? expf(bv - mx) / s : 0.f;
         wsum += p;
         if (j < 8) chosen_w[j] = p;
-        if (lane == 0) {
+        if (active && gl == 0) {
             topk_idx[(int64_t)t * k + j] = bi;
             if (!renorm) topk_w[(int64_t)t * k + j] = p;
         }
     }
-    if (renorm && lane == 0) {
+    if (renorm && active && gl == 0) {
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
         for (int j = 0; j < k; ++j) {
             float p;
@@ -307,7 +315,18 @@ int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* 
     const int nchunks = (int)((P + kChunkPairs - 1) / kChunkPairs);
     int32_t* hist = (int32_t*)ws;
     int32_t* base = hist + (int64_t)nchunks * E;
-    route_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w, err_word);
+    auto topk = [&](auto kern, int g) {
+        const int64_t blocks = ((int64_t)T * g + 255) / 256;
+        kern<<<(unsigned)blocks, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w, err_word);
+    };
+    if (E <= 8)
+        topk(route_topk_kernel<8, 1>, 8);
+    else if (E <= 16)
+        topk(route_topk_kernel<16, 1>, 16);
+    else if (E <= 32)
+        topk(route_topk_kernel<32, 1>, 32);
+    else
+        topk(route_topk_kernel<64, MOE_MAX_E / 64>, 64);
     const int nblk = (nchunks + 3) / 4;
     const size_t lds = 4 * (size_t)E * sizeof(int32_t);
     layout_hist_kernel<<<nblk, 256, lds, s>>>(topk_idx, P, E, nchunks, hist, src_of, M_cap);
