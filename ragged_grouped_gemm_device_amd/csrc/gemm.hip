@@ -811,9 +811,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         // 32-row blocks, stored transposed [2n, M_cap]) and of A' (column-wise,
         // transposed [n, M_cap]). A 32-row block lies wholly inside or wholly
         // past an expert region (regions are 128-row multiples), so whole blocks
-        // are skipped together.
+        // are skipped together. The column-wise codes of a wavefront's 128-row
+        // band are assembled in LDS (the last slab's buffer, free once every
+        // wavefront is past it) and leave as whole 128-byte column lines.
         const int n2 = 2 * p.N;
         const int64_t ls = p.M_cap / 32;
+        __syncthreads();
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;  // gate: 0, up: 4096
+        const int band = row0 + wm * 128;                                  // first row of the band
+        const int band_rows = min(max(row_end - band, 0), 128);
         auto rowq = [&](const uint32_t* pk, int m, int col0) {  // 16 bf16 here, 16 in lane l ^ 32
             uint32_t am = 0;
 #pragma unroll
@@ -829,60 +835,93 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             });
             p.s_row[(int64_t)m * (n2 / 32) + col0 / 32] = (uint8_t)(er + 127);  // same byte from both halves
         };
+        float wI[4], dsum[4];
         static_for<4>([&](auto I) {
             const int m = rbase + 32 * I;
-            const int mb = row0 + wm * 128 + 32 * I;  // first row of this 32-row block
-            if (mb < row_end) {
+            wI[I] = 0.f;
+            dsum[I] = 0.f;
+            if (band + 32 * I < row_end) {
                 const int src = p.src_of[m];
-                const float w = src >= 0 ? p.topk_w[src] : 0.f;
-                float dsum = 0.f;
-                const int64_t hrow = (int64_t)m * p.ld_aux;
-                const int64_t drow = (int64_t)m * p.ld0;
-                static_for<TNW>([&](auto J) {
-                    const int ct = n0 + wn * WN + 32 * J;  // first activation column of the tile
-                    if (ct < p.N) {
-                        const int gcol = 2 * ct;
-                        uint32_t dgp[8], dup[8], awp[8];  // bf16 pairs: slots 2p, 2p + 1
+                wI[I] = src >= 0 ? p.topk_w[src] : 0.f;
+            }
+        });
+        static_for<TNW>([&](auto J) {
+            const int ct = n0 + wn * WN + 32 * J;  // first activation column of the tile
+            if (ct < p.N) {
+                const int gcol = 2 * ct;
+                // pass 1: dH (bf16 stores, row-wise codes, column-wise codes staged)
+                static_for<4>([&](auto I) {
+                    const int m = rbase + 32 * I;
+                    const int mb = band + 32 * I;  // first row of this 32-row block
+                    if (mb < row_end) {
+                        const float w = wI[I];
+                        const int64_t hrow = (int64_t)m * p.ld_aux;
+                        const int64_t drow = (int64_t)m * p.ld0;
+                        uint32_t dgp[8], dup[8];  // bf16 pairs, slots 2p, 2p + 1
                         static_for<4>([&](auto Q) {
                             const int cc = 8 * Q + 4 * h;
-                            float g[4], uu[4], dg[4], du[4], aw[4];
+                            float g[4], uu[4], dg[4], du[4];
                             unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
                             unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 float fg, dfg;
                                 glu_gate_grad<ACT>(g[s], fg, dfg);
-                                const float a = fg * uu[s];
                                 const float dap = acc[I][J][4 * Q + s];
-                                dsum = fmaf(dap, a, dsum);
+                                dsum[I] = fmaf(dap, fg * uu[s], dsum[I]);
                                 const float da = w * dap;
                                 dg[s] = da * uu[s] * dfg;
                                 du[s] = da * fg;
-                                aw[s] = w * a;
                             }
                             dgp[2 * Q] = pack_bf16x2(dg[0], dg[1]);
                             dgp[2 * Q + 1] = pack_bf16x2(dg[2], dg[3]);
                             dup[2 * Q] = pack_bf16x2(du[0], du[1]);
                             dup[2 * Q + 1] = pack_bf16x2(du[2], du[3]);
-                            awp[2 * Q] = pack_bf16x2(aw[0], aw[1]);
-                            awp[2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
                             *(uint2*)(p.out0 + drow + gcol + cc) = make_uint2(dgp[2 * Q], dgp[2 * Q + 1]);
                             *(uint2*)(p.out0 + drow + gcol + 32 + cc) = make_uint2(dup[2 * Q], dup[2 * Q + 1]);
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
                         });
                         rowq(dgp, m, gcol);
                         rowq(dup, m, gcol + 32);
-                        mx_colq32(dgp, lane, p.q_col + (int64_t)gcol * p.M_cap + mb, p.M_cap,
-                                  p.s_col + (int64_t)gcol * ls + mb / 32, ls);
-                        mx_colq32(dup, lane, p.q_col + (int64_t)(gcol + 32) * p.M_cap + mb, p.M_cap,
-                                  p.s_col + (int64_t)(gcol + 32) * ls + mb / 32, ls);
-                        mx_colq32(awp, lane, p.q2_col + (int64_t)ct * p.M_cap + mb, p.M_cap,
-                                  p.s2_col + (int64_t)ct * ls + mb / 32, ls);
+                        mx_colq32_stage(dgp, lane, stg, I, p.s_col + (int64_t)gcol * ls + mb / 32, ls);
+                        mx_colq32_stage(dup, lane, stg + 4096, I, p.s_col + (int64_t)(gcol + 32) * ls + mb / 32, ls);
                     }
                 });
-                dsum += __shfl_xor(dsum, 32, 64);
-                if (h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
+                wave_lds_sync();
+                mx_stage_flush(stg, lane, p.q_col + (int64_t)gcol * p.M_cap + band, p.M_cap, band_rows);
+                mx_stage_flush(stg + 4096, lane, p.q_col + (int64_t)(gcol + 32) * p.M_cap + band, p.M_cap,
+                               band_rows);
+                wave_lds_sync();
+                // pass 2: A' = w a (bf16 stores, column-wise codes staged), a recomputed from H
+                static_for<4>([&](auto I) {
+                    const int m = rbase + 32 * I;
+                    const int mb = band + 32 * I;
+                    if (mb < row_end) {
+                        const float w = wI[I];
+                        const int64_t hrow = (int64_t)m * p.ld_aux;
+                        uint32_t awp[8];
+                        static_for<4>([&](auto Q) {
+                            const int cc = 8 * Q + 4 * h;
+                            float g[4], uu[4], aw[4];
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
+                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) aw[s] = w * (glu_gate<ACT>(g[s]) * uu[s]);
+                            awp[2 * Q] = pack_bf16x2(aw[0], aw[1]);
+                            awp[2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
+                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
+                        });
+                        mx_colq32_stage(awp, lane, stg, I, p.s2_col + (int64_t)ct * ls + mb / 32, ls);
+                    }
+                });
+                wave_lds_sync();
+                mx_stage_flush(stg, lane, p.q2_col + (int64_t)ct * p.M_cap + band, p.M_cap, band_rows);
+                wave_lds_sync();
             }
+        });
+        static_for<4>([&](auto I) {
+            const int m = rbase + 32 * I;
+            float d = dsum[I] + __shfl_xor(dsum[I], 32, 64);
+            if (band + 32 * I < row_end && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = d;
         });
     } else if constexpr (EPI == EPI_DGLU) {
         // acc = dA' over activation columns c; H holds (gate, up) interleaved.

@@ -105,8 +105,9 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 // maximum (9 exchanges for 16 columns instead of 5 per column). The E8M0
 // codes travel back the same way. Codes go to q[c * ldq + row], the scale of
 // column c to sc[c * lds] (each lane of a pair stores the same byte).
-__device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_t* q, int64_t ldq,
-                                          uint8_t* sc, int64_t lds) {
+template <class Sink>
+__device__ __forceinline__ void mx_colq32_impl(const uint32_t pk[8], int lane, uint8_t* sc, int64_t lds,
+                                               Sink sink) {
     const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
     const int h = (lane >> 5) & 1;
     uint32_t t1[4], t2[2];
@@ -152,7 +153,6 @@ __device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_
     const int row = lane & 31, t = row & 3;
     const uint32_t sel1 = (t & 1) ? 0x03070105u : 0x06020400u;  // bytes 0-3: own word, 4-7: partner's
     const uint32_t sel2 = (t & 2) ? 0x03020706u : 0x05040100u;
-    uint8_t* qr = q + (row & ~3);
 #pragma unroll
     for (int Q = 0; Q < 4; ++Q) {
         float y[4];
@@ -166,8 +166,53 @@ __device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_
         uint32_t w = e4m3x4(y[0], y[1], y[2], y[3]);
         w = __builtin_amdgcn_perm(xor_lane<1>(w), w, sel1);  // 16-bit pairs: rows (2i, 2i + 1)
         w = __builtin_amdgcn_perm(xor_lane<2>(w), w, sel2);  // words: rows 4i .. 4i + 3
-        *(uint32_t*)(qr + (int64_t)(8 * Q + 4 * h + t) * ldq) = w;
+        sink(Q, w);  // column 8 Q + 4 h + t, rows (row & ~3) .. (row & ~3) + 3
     }
+}
+
+// Codes to q[c * ldq + row] directly.
+__device__ __forceinline__ void mx_colq32(const uint32_t pk[8], int lane, uint8_t* q, int64_t ldq,
+                                          uint8_t* sc, int64_t lds) {
+    const int row = lane & 31, t = row & 3, h = (lane >> 5) & 1;
+    uint8_t* qr = q + (row & ~3);
+    mx_colq32_impl(pk, lane, sc, lds,
+                   [&](int Q, uint32_t w) { *(uint32_t*)(qr + (int64_t)(8 * Q + 4 * h + t) * ldq) = w; });
+}
+
+// Codes to an LDS stage of 32 columns x 128 rows (block I holds rows 32 I ..
+// 32 I + 31), 128 bytes per column whose 16-byte row segments are XOR-swizzled
+// by the column (segment g of column c at (g ^ (c & 7)) * 16): the quads' word
+// writes then hit distinct banks, and mx_stage_flush sends each column out as
+// whole 16-byte pieces (one 128-byte line per column and band) instead of the
+// 32-byte pieces the direct stores leave scattered over 16 columns.
+__device__ __forceinline__ void mx_colq32_stage(const uint32_t pk[8], int lane, uint8_t* stage, int I,
+                                                uint8_t* sc, int64_t lds) {
+    const int row = lane & 31, t = row & 3, h = (lane >> 5) & 1;
+    const int r = 32 * I + (row & ~3);
+    mx_colq32_impl(pk, lane, sc, lds, [&](int Q, uint32_t w) {
+        const int c = 8 * Q + 4 * h + t;
+        *(uint32_t*)(stage + c * 128 + (((r >> 4) ^ (c & 7)) << 4) + (r & 15)) = w;
+    });
+}
+
+// The stage's columns to q[c * ldq + row], rows [0, rows) of the band only
+// (rows is a multiple of 16), 16 bytes per lane and piece.
+__device__ __forceinline__ void mx_stage_flush(const uint8_t* stage, int lane, uint8_t* q, int64_t ldq,
+                                               int rows) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 64 + lane;
+        const int c = idx >> 3, g = idx & 7;
+        if (g * 16 < rows)
+            *(uint4*)(q + (int64_t)c * ldq + g * 16) = *(const uint4*)(stage + c * 128 + ((g ^ (c & 7)) << 4));
+    }
+}
+
+// Order this wavefront's LDS writes before its later reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace moe
