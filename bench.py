@@ -306,7 +306,8 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
         rows += [
             (f"FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
                                                              buf.a, buf.y, M.MOE_STAGE_FC1,
-                                                             mx=buf.mx_fwd(fc1=False), act=act),
+                                                             mx=buf.mx_fwd(fc1=False, transposed_a=True),
+                                                             act=act),
              4.0 * Mr * d * n, None),
             (f"MX FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
                                                                 buf.a, buf.y, M.MOE_STAGE_FC1, mx=mx,

@@ -297,9 +297,15 @@ class Buffers:
         moe_quant_mxfp8(w2, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, self.w2_q, self.w2_s, self.w2t_q,
                         self.w2t_s)
 
-    def mx_fwd(self, fc1=True):
+    def mx_fwd(self, fc1=True, transposed_a=False):
+        """The moe_mx_fwd fields: FC1 on MXFP8 operands when fc1; the transposed copy of A
+        only when asked (the training step's FC2 wgrad reads A' = w A, quantized by the FC2
+        dgrad, not A)."""
         keys = MX_FWD_FIELDS if fc1 else MX_FWD_FIELDS[:6]
-        return {key: getattr(self, key) for key in keys}
+        d = {key: getattr(self, key) for key in keys}
+        if not transposed_a:
+            d["at_q"] = d["at_s"] = None
+        return d
 
     def mx_bwd(self, dgrad2=True):
         keys = MX_BWD_FIELDS if dgrad2 else MX_BWD_FIELDS[:12]
