@@ -116,7 +116,8 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path has no "
-              "collectives; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "collectives (experts would shard across GPUs with an all-to-all dispatch and combine)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
