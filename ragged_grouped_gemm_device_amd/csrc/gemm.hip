@@ -608,39 +608,59 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     const int rbase = (RAGGED_K ? m0 : row0) + wm * 128 + (lane & 31);
     const int cbase = n0 + wn * WN + 4 * h;
 
-    if constexpr (EPI == EPI_F32) {
-        float* out = p.outf + (int64_t)e * p.f_estride;
+    // EPI_F32 and EPI_BF16 store through this wavefront's 8 KiB of the LDS
+    // stage the tile no longer reads (the next tile's first slab goes to the
+    // other one): 32 rows at a time, written in the MFMA layout, read back in
+    // whole-row runs. A store instruction then covers 4 rows x 256 B (fp32) or
+    // 8 rows x 128 B (bf16) instead of 32 rows x 32 B or 16 B, a quarter of
+    // the memory requests for the same bytes. The 16-byte chunks of a staged
+    // row are XOR-swizzled by the row so both sides stay free of LDS bank
+    // conflicts.
+    if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
+        const int r = lane & 31;
+        const int rband = (RAGGED_K ? m0 : row0) + wm * 128;
+        const int col0 = n0 + wn * WN;
         static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
-            if (m < p.M) {
+            if constexpr (EPI == EPI_F32) {
+                // row r: 64 floats = 16 chunks, chunk 8J + 2Q + h from this lane
                 static_for<TNW>([&](auto J) {
-                    if (n0 + wn * WN + 32 * J < p.N) {
-                        static_for<4>([&](auto Q) {
-                            const int c = cbase + 32 * J + 8 * Q;
-                            const float4 v = make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1],
-                                                         acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
-                            *(float4*)(out + (int64_t)m * p.ldf + c) = v;
-                        });
-                    }
+                    static_for<4>([&](auto Q) {
+                        const int ch = 8 * J + 2 * Q + h;
+                        *(float4*)(stg + r * 256 + ((ch ^ (r & 15)) << 4)) =
+                            make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
+                                        acc[I][J][4 * Q + 3]);
+                    });
+                });
+                wave_lds_sync();
+                float* out = p.outf + (int64_t)e * p.f_estride;
+                static_for<8>([&](auto It) {
+                    const int R = 4 * It + (lane >> 4), c = lane & 15;
+                    const float4 v = *(const float4*)(stg + R * 256 + ((c ^ (R & 15)) << 4));
+                    const int m = rband + 32 * I + R, col = col0 + 4 * c;
+                    if (m < p.M && col < p.N) *(float4*)(out + (int64_t)m * p.ldf + col) = v;
+                });
+            } else {
+                // row r: 64 bf16 = 8 chunks, half h of chunk 4J + Q from this lane
+                static_for<TNW>([&](auto J) {
+                    static_for<4>([&](auto Q) {
+                        const int ch = 4 * J + Q;
+                        uint2 v;
+                        v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                        v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                        *(uint2*)(stg + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h) = v;
+                    });
+                });
+                wave_lds_sync();
+                static_for<4>([&](auto It) {
+                    const int R = 8 * It + (lane >> 3), c = lane & 7;
+                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                    const int m = rband + 32 * I + R, col = col0 + 8 * c;
+                    if (m < row_end && col < p.N) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + col) = v;
                 });
             }
-        });
-    } else if constexpr (EPI == EPI_BF16) {
-        static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
-            if (m < row_end) {
-                static_for<TNW>([&](auto J) {
-                    if (n0 + wn * WN + 32 * J < p.N) {
-                        static_for<4>([&](auto Q) {
-                            const int c = cbase + 32 * J + 8 * Q;
-                            uint2 v;
-                            v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
-                            v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
-                            *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) = v;
-                        });
-                    }
-                });
-            }
+            wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
     } else if constexpr (EPI == EPI_GLU_MX) {
         // GLU as below, then the MXFP8 copies of the bf16-rounded A: row-wise
@@ -769,41 +789,54 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
         });
     } else if constexpr (EPI == EPI_GLU) {
-        // columns come in (gate 32, up 32) pairs: tiles j = 2u (gate), 2u+1 (up)
+        // Columns come in (gate 32, up 32) pairs: tiles 0 (gate) and 1 (up) of
+        // the wavefront. Staged through LDS like EPI_BF16, 32 rows at a time:
+        // the H rows of the pair (64 columns, 128 B) at 0, the A rows (32
+        // columns, 64 B) at 4096.
+        static_assert(TNW == 2, "one (gate, up) pair per wavefront");
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
+        const int r = lane & 31;
+        const int rband = row0 + wm * 128;
+        const int hc = n0 + wn * WN;  // first gate column of the pair
+        const bool pair_ok = hc < p.N;
         static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
-            if (m < row_end) {
-                static_for<TNW / 2>([&](auto U) {
-                    const int hc = n0 + wn * WN + 64 * U;  // first gate column of the pair
-                    if (hc < p.N) {
-                        const int ac = hc / 2 + 4 * h;      // output column base
-                        static_for<4>([&](auto Q) {
-                            const f32x16_t& G = acc[I][2 * U];
-                            const f32x16_t& Up = acc[I][2 * U + 1];
-                            float av[4];
+            const f32x16_t& G = acc[I][0];
+            const f32x16_t& Up = acc[I][1];
+            static_for<4>([&](auto Q) {
+                float av[4];
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) {
-                                const float g = G[4 * Q + s];
-                                av[s] = glu_gate<ACT>(g) * Up[4 * Q + s];
-                            }
-                            uint2 v;
-                            v.x = pack_bf16x2(av[0], av[1]);
-                            v.y = pack_bf16x2(av[2], av[3]);
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 8 * Q) = v;
-                            if (p.out0) {
-                                uint2 g2, u2;
-                                g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
-                                g2.y = pack_bf16x2(G[4 * Q + 2], G[4 * Q + 3]);
-                                u2.x = pack_bf16x2(Up[4 * Q], Up[4 * Q + 1]);
-                                u2.y = pack_bf16x2(Up[4 * Q + 2], Up[4 * Q + 3]);
-                                const int64_t rowp = (int64_t)m * p.ld0;
-                                *(uint2*)(p.out0 + rowp + hc + 4 * h + 8 * Q) = g2;
-                                *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * Q) = u2;
-                            }
-                        });
-                    }
+                for (int s = 0; s < 4; ++s) av[s] = glu_gate<ACT>(G[4 * Q + s]) * Up[4 * Q + s];
+                uint2 v;
+                v.x = pack_bf16x2(av[0], av[1]);
+                v.y = pack_bf16x2(av[2], av[3]);
+                *(uint2*)(stg + 4096 + r * 64 + ((Q ^ ((r >> 1) & 3)) << 4) + 8 * h) = v;
+                if (p.out0) {
+                    uint2 g2, u2;
+                    g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
+                    g2.y = pack_bf16x2(G[4 * Q + 2], G[4 * Q + 3]);
+                    u2.x = pack_bf16x2(Up[4 * Q], Up[4 * Q + 1]);
+                    u2.y = pack_bf16x2(Up[4 * Q + 2], Up[4 * Q + 3]);
+                    *(uint2*)(stg + r * 128 + ((Q ^ ((r >> 1) & 7)) << 4) + 8 * h) = g2;
+                    *(uint2*)(stg + r * 128 + (((4 + Q) ^ ((r >> 1) & 7)) << 4) + 8 * h) = u2;
+                }
+            });
+            wave_lds_sync();
+            static_for<2>([&](auto It) {  // A: 4 lanes x 16 B a row
+                const int R = 16 * It + (lane >> 2), c = lane & 3;
+                const uint4 v = *(const uint4*)(stg + 4096 + R * 64 + ((c ^ ((R >> 1) & 3)) << 4));
+                const int m = rband + 32 * I + R;
+                if (m < row_end && pair_ok) *(uint4*)(p.out1 + (int64_t)m * p.ld1 + hc / 2 + 8 * c) = v;
+            });
+            if (p.out0) {
+                static_for<4>([&](auto It) {  // H: 8 lanes x 16 B a row
+                    const int R = 8 * It + (lane >> 3), c = lane & 7;
+                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                    const int m = rband + 32 * I + R;
+                    if (m < row_end && pair_ok) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + hc + 8 * c) = v;
                 });
             }
+            wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
     } else if constexpr (EPI == EPI_DGLU_MX) {
         // The dGLU epilogue below, then MXFP8 copies of the bf16-rounded dH
@@ -924,9 +957,30 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             if (band + 32 * I < row_end && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = d;
         });
     } else if constexpr (EPI == EPI_DGLU) {
-        // acc = dA' over activation columns c; H holds (gate, up) interleaved.
+        // acc = dA' over activation columns c; H holds (gate, up) interleaved by
+        // 32-column block. Per 32 rows and 32-column block J, the block's H rows
+        // (gate and up, 128 B) come in as whole-row loads into LDS, each lane
+        // takes its values in the MFMA layout and writes dH back in place, and
+        // dH and A' (64 B a row, at 4096) leave as whole-row stores. The H rows
+        // of the next block are loaded while this one is worked on.
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
+        const int r = lane & 31;
+        const int rband = row0 + wm * 128;
+        uint4 hv[4];
+        auto load_h = [&](int I, int J) {  // 8 lanes x 16 B a row, 8 rows per load
+            const int ct = n0 + wn * WN + 32 * J;
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int m = rband + 32 * I + 8 * it + (lane >> 3);
+                hv[it] = make_uint4(0, 0, 0, 0);
+                if (m < row_end && ct < p.N)
+                    hv[it] = *(const uint4*)(p.aux + (int64_t)m * p.ld_aux + 2 * ct + 8 * (lane & 7));
+            }
+        };
+        load_h(0, 0);
         static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
+            const int m = rband + 32 * I + r;
             const bool row_ok = m < row_end;
             float w = 0.f;
             if (row_ok) {
@@ -934,45 +988,66 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 w = src >= 0 ? p.topk_w[src] : 0.f;
             }
             float dsum = 0.f;
-            if (row_ok) {
-                const int64_t hrow = (int64_t)m * p.ld_aux;
-                const int64_t drow = (int64_t)m * p.ld0;
-                static_for<TNW>([&](auto J) {
-                    const int ct = n0 + wn * WN + 32 * J;  // first column of the tile
-                    if (ct < p.N) {
-                        const int gcol = 2 * ct;             // gate block of this 32-column tile
-                        static_for<4>([&](auto Q) {
-                            const int cc = 8 * Q + 4 * h;    // column within the tile
-                            float g[4], uu[4];
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
-                            float dg[4], du[4], aw[4];
+            static_for<TNW>([&](auto J) {
+                const int ct = n0 + wn * WN + 32 * J;  // first column of the block
+                const bool blk_ok = ct < p.N;
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) {
-                                float fg, dfg;
-                                glu_gate_grad<ACT>(g[s], fg, dfg);
-                                const float a = fg * uu[s];
-                                const float dap = acc[I][J][4 * Q + s];
-                                dsum = fmaf(dap, a, dsum);
-                                const float da = w * dap;
-                                dg[s] = da * uu[s] * dfg;
-                                du[s] = da * fg;
-                                aw[s] = w * a;
-                            }
-                            uint2 v;
-                            v.x = pack_bf16x2(dg[0], dg[1]);
-                            v.y = pack_bf16x2(dg[2], dg[3]);
-                            *(uint2*)(p.out0 + drow + gcol + cc) = v;
-                            v.x = pack_bf16x2(du[0], du[1]);
-                            v.y = pack_bf16x2(du[2], du[3]);
-                            *(uint2*)(p.out0 + drow + gcol + 32 + cc) = v;
-                            v.x = pack_bf16x2(aw[0], aw[1]);
-                            v.y = pack_bf16x2(aw[2], aw[3]);
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = v;
-                        });
+                for (int it = 0; it < 4; ++it) {
+                    const int R = 8 * it + (lane >> 3), c = lane & 7;
+                    *(uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4)) = hv[it];
+                }
+                if constexpr (J + 1 < TNW) load_h(I, J + 1);
+                else if constexpr (I + 1 < 4) load_h(I + 1, 0);
+                wave_lds_sync();
+                // rows past the region or columns past N hold zeros here and in
+                // acc, so they add nothing to dsum and are not stored
+                static_for<4>([&](auto Q) {
+                    uint2* pg = (uint2*)(stg + r * 128 + ((Q ^ ((r >> 1) & 7)) << 4) + 8 * h);
+                    uint2* pu = (uint2*)(stg + r * 128 + (((4 + Q) ^ ((r >> 1) & 7)) << 4) + 8 * h);
+                    float g[4], uu[4];
+                    unpack_bf16x4(*pg, g);
+                    unpack_bf16x4(*pu, uu);
+                    float dg[4], du[4], aw[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        float fg, dfg;
+                        glu_gate_grad<ACT>(g[s], fg, dfg);
+                        const float a = fg * uu[s];
+                        const float dap = acc[I][J][4 * Q + s];
+                        dsum = fmaf(dap, a, dsum);
+                        const float da = w * dap;
+                        dg[s] = da * uu[s] * dfg;
+                        du[s] = da * fg;
+                        aw[s] = w * a;
                     }
+                    uint2 v;
+                    v.x = pack_bf16x2(dg[0], dg[1]);
+                    v.y = pack_bf16x2(dg[2], dg[3]);
+                    *pg = v;
+                    v.x = pack_bf16x2(du[0], du[1]);
+                    v.y = pack_bf16x2(du[2], du[3]);
+                    *pu = v;
+                    v.x = pack_bf16x2(aw[0], aw[1]);
+                    v.y = pack_bf16x2(aw[2], aw[3]);
+                    *(uint2*)(stg + 4096 + r * 64 + ((Q ^ ((r >> 1) & 3)) << 4) + 8 * h) = v;
                 });
-            }
+                wave_lds_sync();
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {  // dH: 8 lanes x 16 B a row
+                    const int R = 8 * it + (lane >> 3), c = lane & 7;
+                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                    const int mr = rband + 32 * I + R;
+                    if (mr < row_end && blk_ok) *(uint4*)(p.out0 + (int64_t)mr * p.ld0 + 2 * ct + 8 * c) = v;
+                }
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {  // A': 4 lanes x 16 B a row
+                    const int R = 16 * it + (lane >> 2), c = lane & 3;
+                    const uint4 v = *(const uint4*)(stg + 4096 + R * 64 + ((c ^ ((R >> 1) & 3)) << 4));
+                    const int mr = rband + 32 * I + R;
+                    if (mr < row_end && blk_ok) *(uint4*)(p.out1 + (int64_t)mr * p.ld1 + ct + 8 * c) = v;
+                }
+                wave_lds_sync();  // read out before the next block overwrites it
+            });
             dsum += __shfl_xor(dsum, 32, 64);  // the partner lane holds the other half
             if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
         });
