@@ -431,43 +431,53 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
             issue(src_next, 0, buf0);
             issue_scales(src_next, 0, sg0);
         }
-        // epilogue: lane = row (l & 31), columns 8q + 4h + s of each 32-wide tile
-        if constexpr (!RAGGED_K) {
-            const int rbase = tl.row0 + wm * 128 + (lane & 31);
-            static_for<4>([&](auto I) {
-                const int m = rbase + 32 * I;
-                if (m < tl.row_end) {
-                    static_for<TNW>([&](auto J) {
-                        if (tl.n0 + wn * WN + 32 * J < p.N) {
-                            static_for<4>([&](auto Q) {
-                                const int c = tl.n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
-                                uint2 v;
-                                v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
-                                v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
-                                *(uint2*)(p.out + (int64_t)m * p.N + c) = v;
-                            });
-                        }
+        // Epilogue: lane = row (l & 31), columns 8q + 4h + s of each 32-wide
+        // tile. Staged through this wavefront's 8 KiB of the LDS stage the tile
+        // no longer reads, 32 rows at a time, so each store covers whole rows
+        // (8 rows x 128 B of bf16, 4 rows x 256 B of fp32) instead of 32 rows
+        // x 16 or 32 B; 16-byte chunks XOR-swizzled by row against bank
+        // conflicts.
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = &s_ab[next_buf0 ^ 1][0] + wave * 8192;
+        const int r = lane & 31;
+        const int col0 = tl.n0 + wn * WN;
+        static_for<4>([&](auto I) {
+            if constexpr (!RAGGED_K) {
+                static_for<TNW>([&](auto J) {
+                    static_for<4>([&](auto Q) {
+                        uint2 v;
+                        v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
+                        v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                        *(uint2*)(stg + r * 128 + (((4 * J + Q) ^ ((r >> 1) & 7)) << 4) + 8 * h) = v;
                     });
-                }
-            });
-        } else {
-            float* o = p.outf + (int64_t)tl.e * p.M * p.N;
-            const int rbase = tl.m0 + wm * 128 + (lane & 31);
-            static_for<4>([&](auto I) {
-                const int m = rbase + 32 * I;
-                if (m < p.M) {
-                    static_for<TNW>([&](auto J) {
-                        static_for<4>([&](auto Q) {
-                            const int c = tl.n0 + wn * WN + 32 * J + 8 * Q + 4 * h;
-                            if (c < p.N)
-                                *(float4*)(o + (int64_t)m * p.N + c) =
-                                    make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
-                                                acc[I][J][4 * Q + 3]);
-                        });
+                });
+                wave_lds_sync();
+                static_for<4>([&](auto It) {
+                    const int R = 8 * It + (lane >> 3), c = lane & 7;
+                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                    const int m = tl.row0 + wm * 128 + 32 * I + R, col = col0 + 8 * c;
+                    if (m < tl.row_end && col < p.N) *(uint4*)(p.out + (int64_t)m * p.N + col) = v;
+                });
+            } else {
+                static_for<TNW>([&](auto J) {
+                    static_for<4>([&](auto Q) {
+                        const int ch = 8 * J + 2 * Q + h;
+                        *(float4*)(stg + r * 256 + ((ch ^ (r & 15)) << 4)) =
+                            make_float4(acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
+                                        acc[I][J][4 * Q + 3]);
                     });
-                }
-            });
-        }
+                });
+                wave_lds_sync();
+                float* o = p.outf + (int64_t)tl.e * p.M * p.N;
+                static_for<8>([&](auto It) {
+                    const int R = 4 * It + (lane >> 4), c = lane & 15;
+                    const float4 v = *(const float4*)(stg + R * 256 + ((c ^ (R & 15)) << 4));
+                    const int m = tl.m0 + wm * 128 + 32 * I + R, col = col0 + 4 * c;
+                    if (m < p.M && col < p.N) *(float4*)(o + (int64_t)m * p.N + col) = v;
+                });
+            }
+            wave_lds_sync();  // read out before the next 32 rows overwrite it
+        });
         if (!have_next) break;
         ++round;
         buf0 = next_buf0;
