@@ -385,10 +385,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     auto load_frags = [&](int set, int buf, int ks) {
         const uint16_t* sa = s_ab[buf];
         const uint16_t* sb = s_ab[buf] + BM * BK;
+        // the first MFMA's operands first: B0, A0, B1, then the rest of A
+        fb[set][0] = frag(sb, B_KMAJ, wn * WN, ks);
+        fa[set][0] = frag(sa, A_KMAJ, wm * 128, ks);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[set][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks);
+        for (int j = 1; j < TNW; ++j) fb[set][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks);
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) fb[set][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks);
+        for (int i = 1; i < 4; ++i) fa[set][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks);
     };
 
     f32x16_t acc[4][TNW];
@@ -561,15 +564,25 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 static_for<BK / 16>([&](auto KS) {
                     constexpr int ks = KS;
                     constexpr int c = ks & 1;
-                    if constexpr (ks + 1 < BK / 16) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
-#pragma unroll
-                        for (int j = 0; j < TNW; ++j) fb[c ^ 1][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks + 1);
-                    }
+                    // The next step's fragments are requested after the first row of
+                    // this step's MFMAs, not before them: right after the slab barrier
+                    // all eight wavefronts ask LDS for fragments at once, and a first
+                    // MFMA that also waits behind the next step's loads starts later.
+                    // The first MFMA's operands (B0, A0) are requested first.
                     __builtin_amdgcn_s_setprio(1);  // the MFMA phase wins issue over the sibling wavefront
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int j = 0; j < TNW; ++j)
+                        acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][0], acc[0][j], 0, 0, 0);
+                    if constexpr (ks + 1 < BK / 16) {
+                        fb[c ^ 1][0] = frag(sb, B_KMAJ, wn * WN, ks + 1);
+                        fa[c ^ 1][0] = frag(sa, A_KMAJ, wm * 128, ks + 1);
+#pragma unroll
+                        for (int j = 1; j < TNW; ++j) fb[c ^ 1][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks + 1);
+#pragma unroll
+                        for (int i = 1; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
+                    }
+#pragma unroll
+                    for (int i = 1; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < TNW; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);

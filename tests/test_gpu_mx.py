@@ -30,23 +30,30 @@ def M():
     return moe
 
 
-def _gpu_quant(M, bits, mode=3):
+def _scales(shape, offset):
+    """0xAB-filled uint8 scale array of `shape` starting `offset` bytes into its allocation
+    (offset 1: no longer word-aligned, so the kernel must fall back to byte stores)."""
+    n = int(np.prod(shape))
+    return torch.full((n + offset,), 0xAB, dtype=U8, device="cuda")[offset:].view(shape)
+
+
+def _gpu_quant(M, bits, mode=3, scale_offset=0):
     """bits: uint16 [batch, R, C] or [R, C] -> numpy codes/scales (None if not requested)."""
     x = bf16_tensor(bits)
     shp = bits.shape if bits.ndim == 3 else (1,) + bits.shape
     B, R, C = shp
     q_row = torch.full((B, R, C), 0xAB, dtype=U8, device="cuda") if mode & 1 else None
-    s_row = torch.full((B, R, C // 32), 0xAB, dtype=U8, device="cuda") if mode & 1 else None
+    s_row = _scales((B, R, C // 32), scale_offset) if mode & 1 else None
     q_col = torch.full((B, C, R), 0xAB, dtype=U8, device="cuda") if mode & 2 else None
-    s_col = torch.full((B, C, R // 32), 0xAB, dtype=U8, device="cuda") if mode & 2 else None
+    s_col = _scales((B, C, R // 32), scale_offset) if mode & 2 else None
     M.moe_quant_mxfp8(x.view(B, R, C), mode, q_row, s_row, q_col, s_col)
     torch.cuda.synchronize()
     f = (lambda t: None if t is None else t.cpu().numpy())
     return f(q_row), f(s_row), f(q_col), f(s_col)
 
 
-def _check_quant(M, bits, mode=3):
-    g = _gpu_quant(M, bits, mode)
+def _check_quant(M, bits, mode=3, scale_offset=0):
+    g = _gpu_quant(M, bits, mode, scale_offset)
     b3 = bits if bits.ndim == 3 else bits[None]
     for b in range(b3.shape[0]):
         q_r, s_r, q_c, s_c = O.quant_mxfp8(O.from_bf16(b3[b]), rowwise=bool(mode & 1),
@@ -60,13 +67,23 @@ def _check_quant(M, bits, mode=3):
 
 
 @pytest.mark.parametrize("R,C,mode", [(256, 256, 3), (96, 160, 3), (4096, 2048, 3), (160, 64, 1),
-                                      (64, 96, 2), (1000, 32, 1)])
+                                      (64, 96, 2), (1000, 32, 1), (2560, 384, 3), (4608, 256, 2),
+                                      (1152, 416, 3)])
 def test_quant_bit_exact_seeded(M, R, C, mode):
     print(f"quant case R={R} C={C} mode={mode}", flush=True)
     rng = np.random.default_rng(R * 31 + C)
     v = rng.standard_normal((R, C)).astype(np.float32)
     v[rng.random((R, C)) < 0.01] *= 50.0
     _check_quant(M, W.f32_to_bf16_bits(v), mode)
+
+
+def test_quant_unaligned_scale_arrays(M):
+    """Scale arrays that start off a word boundary take the byte-store paths
+    (row scales per byte, column scales per byte) with the same results."""
+    rng = np.random.default_rng(17)
+    v = rng.standard_normal((2560, 384)).astype(np.float32)
+    v[rng.random(v.shape) < 0.01] *= 50.0
+    _check_quant(M, W.f32_to_bf16_bits(v), 3, scale_offset=1)
 
 
 def test_quant_every_bf16_pattern(M):
@@ -98,6 +115,9 @@ def test_quant_edge_cases(M):
 def test_quant_batched(M):
     rng = np.random.default_rng(9)
     v = rng.standard_normal((3, 128, 96)).astype(np.float32) * np.exp(rng.standard_normal((3, 128, 96))).astype(np.float32)
+    _check_quant(M, W.f32_to_bf16_bits(v), 3)
+    # whole strips of 1024 rows in every matrix of the batch (the 16-byte column-scale runs)
+    v = rng.standard_normal((2, 1536, 256)).astype(np.float32)
     _check_quant(M, W.f32_to_bf16_bits(v), 3)
 
 
@@ -274,6 +294,7 @@ PQ_CASES = [
     W.small("pq-k1", T=700, k=1, E=4, d=256, n=64, seed=51, routing="zipf"),
     W.small("pq-k3", T=333, k=3, E=6, d=96, n=64, seed=52, routing="normal"),
     W.small("pq-empty", T=200, k=2, E=16, d=160, n=64, seed=53, routing="zipf"),
+    W.small("pq-strips", T=1536, k=1, E=4, d=256, n=64, seed=54, routing="zipf"),  # M_cap = 2048
 ]
 
 
