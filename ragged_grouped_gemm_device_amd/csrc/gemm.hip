@@ -382,18 +382,16 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         }
     };
     bf16x8_t fa[2][4], fb[2][TNW];
-    auto load_frags = [&](int set, int buf, int ks) {
+    // the first MFMA row's operands of K step ks (B fragments, A fragment 0);
+    // the other A fragments are requested after that row's MFMAs are issued
+    auto load_row0 = [&](int set, int buf, int ks) {
         const uint16_t* sa = s_ab[buf];
         const uint16_t* sb = s_ab[buf] + BM * BK;
-        // the first MFMA's operands first: B0, A0, B1, then the rest of A
         fb[set][0] = frag(sb, B_KMAJ, wn * WN, ks);
         fa[set][0] = frag(sa, A_KMAJ, wm * 128, ks);
 #pragma unroll
         for (int j = 1; j < TNW; ++j) fb[set][j] = frag(sb, B_KMAJ, wn * WN + 32 * j, ks);
-#pragma unroll
-        for (int i = 1; i < 4; ++i) fa[set][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks);
     };
-
     f32x16_t acc[4][TNW];
 
     // ---------------------------------------------------------- MX scales
@@ -528,7 +526,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 read_scales(sg0, 0);
                 take_scales();
             } else {
-                load_frags(0, buf0, 0);
+                load_row0(0, buf0, 0);
             }
             for (int kt = 0; kt < nk; ++kt) {
                 // No vector-memory load is in flight here in the steady state (the
@@ -539,6 +537,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 const int cur = (buf0 + kt) & 1;
                 const bool last = kt + 1 == nk;
+                // The next slab's copies. In the bf16 modes they are issued after
+                // the second MFMA row of the slab's first K step, so that the
+                // first MFMAs after the barrier do not wait behind the copies'
+                // issue; they still have most of the slab to land.
+                auto do_issue = [&]() {
                 if (!last) {
                     issue(src, kt + 1, cur ^ 1);
                     if constexpr (kTok) {
@@ -550,6 +553,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     if constexpr (MX) issue_scales(make_scales(tl_next), 0, (sg0 + ng) & 1);
                     if constexpr (kTok) fetch_toks(tl_next, 1);
                 }
+                };
+                if constexpr (MX) do_issue();
                 if constexpr (MX) {
                     // the next group's scales go to the buffer the previous group
                     // left (its last reads ended before the previous slab barrier);
@@ -573,6 +578,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int j = 0; j < TNW; ++j)
                         acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][0], acc[0][j], 0, 0, 0);
+                    if constexpr (ks == 0) {  // the rest of step 0's A fragments (after the barrier
+                                              // only the first row's operands were requested)
+#pragma unroll
+                        for (int i = 1; i < 4; ++i) fa[0][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, 0);
+                    }
                     if constexpr (ks + 1 < BK / 16) {
                         fb[c ^ 1][0] = frag(sb, B_KMAJ, wn * WN, ks + 1);
                         fa[c ^ 1][0] = frag(sa, A_KMAJ, wm * 128, ks + 1);
@@ -582,7 +592,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         for (int i = 1; i < 4; ++i) fa[c ^ 1][i] = frag(sa, A_KMAJ, wm * 128 + 32 * i, ks + 1);
                     }
 #pragma unroll
-                    for (int i = 1; i < 4; ++i)
+                    for (int j = 0; j < TNW; ++j)
+                        acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][1], acc[1][j], 0, 0, 0);
+                    if constexpr (ks == 0) do_issue();  // the next slab's copies, after the second MFMA row
+#pragma unroll
+                    for (int i = 2; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < TNW; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
@@ -596,7 +610,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     if constexpr (MX)
                         take_scales();
                     else
-                        load_frags(0, cur ^ 1, 0);
+                        load_row0(0, cur ^ 1, 0);
                 } else {
                     next_buf0 = cur ^ 1;
                 }
