@@ -179,16 +179,19 @@ def main():
                                   M.MOE_STAGE_FC1 | M.MOE_GATHER_ROWS, mx=mx, act=act,
                                   src_of=buf.src_of, k=wl.k)
         else:
-            M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
-                                  M.MOE_STAGE_FC1, mx=mx, act=act)
+            # with MXFP8 the bf16 A is not written: FC2 reads its MXFP8 copy
+            M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a,
+                                  buf.y, M.MOE_STAGE_FC1, mx=mx, act=act)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
-        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC2,
-                              mx=mx)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a, buf.y,
+                              M.MOE_STAGE_FC2, mx=mx)
         M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
+        # with MXFP8 the FC2 dgrad writes only the MXFP8 copies of dH and A' (all the later
+        # MXFP8 GEMMs read)
         M.backward(buf, dout, w1, w2, act=act, logits=logits, x=x if args.gather else None,
-                   mx=mx_mode)
+                   mx=mx_mode, mx_bf16_copies=False)
 
     for _ in range(args.warmup):
         step()

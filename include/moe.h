@@ -227,7 +227,8 @@ typedef struct moe_mx_fwd {
  *        from x_q/x_s and w1t_q/w1t_s instead of x_perm and w1 (then
  *        d % 128 == 0 and no MOE_GATHER_ROWS).
  *   x_perm [M_cap, d], w1 [E, d, 2n], w2 [E, n, d] (bf16, in);
- *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out),
+ *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out;
+ *   nullable when mx != NULL, whose FC2 reads only A's MXFP8 copy),
  *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
  *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a), plus
  *   optionally MOE_GATHER_ROWS: x_perm is then x [T, d] and FC1 reads its
@@ -303,7 +304,9 @@ typedef struct moe_mx_bwd {
  *   transposed) and of A' (column-wise transposed); the other three GEMMs
  *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q, WGRAD2 from awt_q x
  *   dyt_q, WGRAD1 from xt_q x dht_q (K = the expert's row region). Only the
- *   rows of expert regions are written in the transposed copies. With
+ *   rows of expert regions are written in the transposed copies; dh and
+ *   a_w may then be NULL (their bf16 stores are skipped; no stage reads
+ *   them). With
  *   dy_q != NULL DGRAD2 also runs on MX-scaled MFMA (dy_q x w2_q, then d %
  *   128 == 0 and no MOE_GATHER_ROWS), its dGLU epilogue taking that product
  *   as dA' and dS on the rewritten side as always.

@@ -122,7 +122,7 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
                         uint16_t* y, const moe_mx_fwd* mx, moe_stream_t stream) {
     int rc = check_mlp_shape(E, d, n, M_cap, act);
     if (rc) return rc;
-    if (!offsets || !a) return MOE_ERR_INVALID_ARG;
+    if (!offsets || (!a && !mx)) return MOE_ERR_INVALID_ARG;  // with mx, FC2 reads A's MXFP8 copy
     if ((stages & ~(unsigned)(MOE_STAGES_FWD | MOE_GATHER_ROWS)) || !(stages & MOE_STAGES_FWD))
         return MOE_ERR_INVALID_ARG;
     moe::GatherSpec gx;
@@ -147,7 +147,7 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
     }
     if ((stages & MOE_STAGE_FC1) && h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(a)) return MOE_ERR_INVALID_ARG;
+    if (a && !aligned16(a)) return MOE_ERR_INVALID_ARG;
     if (stages & MOE_STAGE_FC2) {
         if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
         if (!mx && (!w2 || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
@@ -190,9 +190,10 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     if ((rc = gather_spec(stages, src_of, T, k, E, d, gs))) return rc;
     const bool dgrad2_mx = mx && mx->dy_q;  // FC2 dgrad on MXFP8 operands
     if (stages & MOE_STAGE_DGRAD2) {
-        if (!h || !topk_w || !src_of || !row_of || !dh || !a_w || !ds || !workspace)
+        // with mx the bf16 dH and A' are optional (the later stages read their MXFP8 copies)
+        if (!h || !topk_w || !src_of || !row_of || !ds || !workspace || (!mx && (!dh || !a_w)))
             return MOE_ERR_INVALID_ARG;
-        if (!aligned16(h) || !aligned16(dh) || !aligned16(a_w) || !aligned16(workspace))
+        if (!aligned16(h) || (dh && !aligned16(dh)) || (a_w && !aligned16(a_w)) || !aligned16(workspace))
             return MOE_ERR_INVALID_ARG;
         if (dgrad2_mx) {
             if (d % 128 || (stages & MOE_GATHER_ROWS)) return MOE_ERR_UNSUPPORTED;

@@ -714,8 +714,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             am = max_u16x2(am, abp[r] & 0x7fff7fffu);
                         }
                         static_for<4>([&](auto Q) {
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) =
-                                make_uint2(abp[2 * Q], abp[2 * Q + 1]);
+                            if (p.out1)  // the bf16 A is optional: the MX FC2 reads its codes
+                                *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) =
+                                    make_uint2(abp[2 * Q], abp[2 * Q + 1]);
                             if (p.out0) {
                                 uint2 g2, u2;
                                 g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
@@ -866,7 +867,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
     } else if constexpr (EPI == EPI_DGLU_MX) {
-        // The dGLU epilogue below, then MXFP8 copies of the bf16-rounded dH
+        // The dGLU epilogue below (its bf16 dH and A' stores are skipped when
+        // out0 / out1 are null), then MXFP8 copies of the bf16-rounded dH
         // (row-wise: 32-column gate or up blocks, two lanes per row; column-wise:
         // 32-row blocks, stored transposed [2n, M_cap]) and of A' (column-wise,
         // transposed [n, M_cap]). A 32-row block lies wholly inside or wholly
@@ -937,8 +939,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             dgp[2 * Q + 1] = pack_bf16x2(dg[2], dg[3]);
                             dup[2 * Q] = pack_bf16x2(du[0], du[1]);
                             dup[2 * Q + 1] = pack_bf16x2(du[2], du[3]);
-                            *(uint2*)(p.out0 + drow + gcol + cc) = make_uint2(dgp[2 * Q], dgp[2 * Q + 1]);
-                            *(uint2*)(p.out0 + drow + gcol + 32 + cc) = make_uint2(dup[2 * Q], dup[2 * Q + 1]);
+                            if (p.out0) {  // the bf16 dH is optional: later MX stages read its codes
+                                *(uint2*)(p.out0 + drow + gcol + cc) = make_uint2(dgp[2 * Q], dgp[2 * Q + 1]);
+                                *(uint2*)(p.out0 + drow + gcol + 32 + cc) = make_uint2(dup[2 * Q], dup[2 * Q + 1]);
+                            }
                         });
                         rowq(dgp, m, gcol);
                         rowq(dup, m, gcol + 32);
@@ -968,7 +972,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                             for (int s = 0; s < 4; ++s) aw[s] = w * (glu_gate<ACT>(g[s]) * uu[s]);
                             awp[2 * Q] = pack_bf16x2(aw[0], aw[1]);
                             awp[2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
+                            if (p.out1)  // the bf16 A' is optional as well
+                                *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
                         });
                         mx_colq32_stage(awp, lane, stg, I, p.s2_col + (int64_t)ct * ls + mb / 32, ls);
                     }

@@ -172,3 +172,55 @@ def test_mx_wgrad_all_tokens_to_one_expert(M):
     _check("dW1", _np(buf.dw1), b["dW1"], 6e-2)
     _check("dW2", _np(buf.dw2), b["dW2"], 6e-2)
     assert torch.all(buf.dw1[1:] == 0) and torch.all(buf.dw2[1:] == 0)
+
+
+@pytest.mark.parametrize("wl", [CASES[0], CASES[2]], ids=[CASES[0].name, CASES[2].name])
+def test_mx_step_without_bf16_copies(M, wl):
+    """The MXFP8 step as bench.py runs it: permute fused with the quantization
+    of x, FC1 on MXFP8 operands keeping A only as its MXFP8 copy (a = NULL),
+    the MX FC2, and a backward whose FC2 dgrad writes only the MXFP8 copies of
+    dH and A' (dh = a_w = NULL). Every output, and every MXFP8 copy, equals
+    bit for bit the same step with the bf16 A, dH and A' written."""
+    print(f"mx step without bf16 copies: {wl}", flush=True)
+    inp = W.make_inputs(wl)
+    x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
+    logits, dout = f32_tensor(inp["logits"]), bf16_tensor(inp["dout"])
+    outs = ("y", "out", "ds", "dx_perm", "dx", "dw1", "dw2", "dlogits", "h")
+    codes = ("a_q", "a_s", "x_q", "x_s", "xt_q", "xt_s", "dy_q", "dy_s", "dyt_q", "dyt_s",
+             "dh_q", "dh_s", "dht_q", "dht_s", "awt_q", "awt_s")
+
+    def run(bf16_copies):
+        buf = M.Buffers(wl.T, wl.k, wl.E, wl.d, wl.n, mx=True)
+        for name in outs + ("a", "dh", "a_w"):
+            getattr(buf, name).fill_(float("nan"))
+        for name in codes:
+            getattr(buf, name).fill_(0xAB)
+        buf.quantize_weights(w1, w2)
+        mx = buf.mx_fwd()
+        M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
+                           buf.src_of, buf.M_cap, buf.err, buf.route_ws)
+        M.moe_permute_quant_mxfp8(x, buf.src_of, wl.k, wl.E, M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE,
+                                  buf.x_q, buf.x_s, buf.xt_q, buf.xt_s)
+        buf.xt_from_forward = True
+        a = buf.a if bf16_copies else None
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, a, buf.y, M.MOE_STAGE_FC1, mx=mx)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, a, buf.y, M.MOE_STAGE_FC2, mx=mx)
+        M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
+        M.backward(buf, dout, w1, w2, logits=logits, mx=True, mx_bf16_copies=bf16_copies)
+        torch.cuda.synchronize()
+        end = int(buf.offsets[-1].item())
+        got = {}
+        for name in outs + codes:
+            t = getattr(buf, name)
+            got[name] = t.contiguous().view(torch.uint8).cpu().numpy()
+        return got, end, buf
+
+    full, end, buf_full = run(True)
+    lean, end2, buf_lean = run(False)
+    assert end == end2
+    for name in full:
+        assert np.array_equal(full[name], lean[name]), f"{name} differs without the bf16 copies"
+    # the lean run left its bf16 A, dH and A' untouched (still the NaN fill)
+    for name in ("a", "dh", "a_w"):
+        assert torch.isnan(getattr(buf_lean, name).float()).all(), f"{name} was written"
+        assert not torch.isnan(getattr(buf_full, name)[:end].float()).all(), f"{name} was not written"
