@@ -106,6 +106,11 @@ def test_host_validation_returns_before_launch():
     assert rc == M.MOE_ERR_INVALID_ARG
     rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 0, 3, None, f, None, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG              # FC2 without y
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 0, 3, None, None, f, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # a may be NULL only with mx
+    rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 64, 1024, 0, 1, None, _fake(0x1004), f, None,
+                                 None)
+    assert rc == M.MOE_ERR_INVALID_ARG              # misaligned a
     # gathered rows need src_of, and a valid routing shape
     rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 8, 2, 4, 128, 64, 1024, 0, 0x101, None, f, f, None, None)
     assert rc == M.MOE_ERR_INVALID_ARG
@@ -118,6 +123,11 @@ def test_host_validation_returns_before_launch():
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 256, 0, 0x04,
                                  f, f, f, f, f, f, f, 1 << 20, None, None)
     assert rc == M.MOE_ERR_WORKSPACE               # M_cap below capacity
+    # dh and a_w may be NULL only with mx (their MXFP8 copies are then what the later stages read)
+    for dh, a_w in ((None, f), (f, None)):
+        rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x04,
+                                     dh, a_w, f, f, f, f, f, 1 << 20, None, None)
+        assert rc == M.MOE_ERR_INVALID_ARG
     # MXFP8 backward: every copy a requested stage reads or writes must be given
     full = {key: f for key in M.MX_BWD_FIELDS}
     for stage, needed in ((0x04, ("dh_q", "dht_s", "awt_q")), (0x08, ("awt_s", "dyt_q")),
