@@ -16,7 +16,8 @@ namespace moe {
 // 16-byte row pieces (16 lanes cover a 256-byte row segment). A row-wise
 // block (32 columns) spans 4 neighbouring lanes, a column-wise block (32 rows)
 // the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 of one wavefront, so both block maxima
-// are two lane exchanges away; the transposed copy is assembled in LDS and
+// are two lane exchanges away (done on packed pairs of 16-bit magnitudes: two
+// rows, or two columns, per exchange); the transposed copy is assembled in LDS and
 // leaves in 16-byte pieces. Conversion uses gfx950's packed E4M3
 // instruction, which rounds to nearest-even like the codec above (the scale
 // keeps every value within +-448, so it never saturates).
@@ -48,6 +49,14 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
     const int64_t r = (int64_t)blockIdx.y * QT + 8 * rg;  // first row
     const bool cok = c < C;
     src += b * R * C;
+    // Scale bytes leave as whole 4-byte words (one per row, one per column of
+    // the tile) through LDS when the column pass and its barrier run: 4 single
+    // bytes to the same word were 4 separate partial writes. Words need a
+    // tile's 4 blocks present and word-aligned scale arrays; else bytes.
+    __shared__ __attribute__((aligned(16))) uint8_t s_rs[ROW && COL ? QT * 4 : 4];
+    __shared__ __attribute__((aligned(16))) uint8_t s_cs[COL ? QT * 4 : 4];
+    const bool rs_words = ROW && COL && (C % 128) == 0 && ((uintptr_t)s_row & 3) == 0;
+    const bool cs_words = COL && (R % 128) == 0 && ((uintptr_t)s_col & 3) == 0;
     uint4 v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -62,11 +71,18 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
     if constexpr (ROW) {
         uint8_t* qr = q_row + b * R * C;
         uint8_t* sr = s_row + b * R * (C / 32);
+        // block maxima of rows (i, i + 1) travel together as one packed pair
+        uint32_t pam[4];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+            uint32_t pk = abs_max_bf16x8(v[2 * i2]) | (abs_max_bf16x8(v[2 * i2 + 1]) << 16);
+            pk = max_u16x2(pk, (uint32_t)__shfl_xor((int)pk, 1, 64));
+            pk = max_u16x2(pk, (uint32_t)__shfl_xor((int)pk, 2, 64));
+            pam[i2] = pk;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            uint32_t amax = abs_max_bf16x8(v[i]);
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+            const uint32_t amax = (i & 1) ? pam[i >> 1] >> 16 : pam[i >> 1] & 0xffffu;
             const int e = mx_block_exp(amax);
             const float inv = mx_inv_scale(e);
             const uint4 x = v[i];
@@ -75,7 +91,12 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
             q.y = e4m3x4(bf16_lo(x.z) * inv, bf16_hi(x.z) * inv, bf16_lo(x.w) * inv, bf16_hi(x.w) * inv);
             if (cok && r + i < R) {
                 *(uint2*)(qr + (r + i) * C + c) = q;
-                if ((cc & 3) == 0) sr[(r + i) * (C / 32) + c / 32] = (uint8_t)(e + 127);
+                if ((cc & 3) == 0) {
+                    if (rs_words)
+                        s_rs[(8 * rg + i) * 4 + (cc >> 2)] = (uint8_t)(e + 127);
+                    else
+                        sr[(r + i) * (C / 32) + c / 32] = (uint8_t)(e + 127);
+                }
             }
         }
     }
@@ -91,29 +112,49 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
         uint8_t* qc = q_col + b * R * C;
         uint8_t* sc = s_col + b * R * (C / 32);
         const int64_t RB = R / 32;
+        // word p (columns 2p, 2p + 1) of row i of this thread
+        auto word = [&](int i, int p) -> uint32_t { return p == 0 ? v[i].x : p == 1 ? v[i].y : p == 2 ? v[i].z : v[i].w; };
         // element (row i, column j) of this thread
         auto elt = [&](int i, int j) -> float {
-            const uint32_t word = j < 2 ? v[i].x : j < 4 ? v[i].y : j < 6 ? v[i].z : v[i].w;
-            return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+            const uint32_t w_ = word(i, j >> 1);
+            return (j & 1) ? bf16_hi(w_) : bf16_lo(w_);
         };
+        // block maxima of columns (2p, 2p + 1) travel together as one packed pair
+        uint32_t cam[4];
+#pragma unroll
+        for (int p2 = 0; p2 < 4; ++p2) {
+            uint32_t pk = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pk = max_u16x2(pk, word(i, p2) & 0x7fff7fffu);
+            pk = max_u16x2(pk, (uint32_t)__shfl_xor((int)pk, 16, 64));
+            pk = max_u16x2(pk, (uint32_t)__shfl_xor((int)pk, 32, 64));
+            cam[p2] = pk;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            uint32_t amax = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) amax = max(amax, (__float_as_uint(elt(i, j)) >> 16) & 0x7fffu);
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
-            amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+            const uint32_t amax = (j & 1) ? cam[j >> 1] >> 16 : cam[j >> 1] & 0xffffu;
             const int e = mx_block_exp(amax);
             const float inv = mx_inv_scale(e);
             uint2 q;
             q.x = e4m3x4(elt(0, j) * inv, elt(1, j) * inv, elt(2, j) * inv, elt(3, j) * inv);
             q.y = e4m3x4(elt(4, j) * inv, elt(5, j) * inv, elt(6, j) * inv, elt(7, j) * inv);
             *(uint2*)(tq + (8 * cc + j) * QT + ((rg ^ (2 * (cc & 7))) * 8)) = q;
-            if ((l >> 4) == 0 && cok && r < R) sc[(int64_t)(c + j) * RB + r / 32] = (uint8_t)(e + 127);
+            if ((l >> 4) == 0) {
+                if (cs_words)
+                    s_cs[(8 * cc + j) * 4 + w] = (uint8_t)(e + 127);
+                else if (cok && r < R)
+                    sc[(int64_t)(c + j) * RB + r / 32] = (uint8_t)(e + 127);
+            }
         }
         __syncthreads();
         const int64_t r0 = (int64_t)blockIdx.y * QT;
         const int c0 = blockIdx.x * QT;
+        if (rs_words && threadIdx.x < QT && r0 + threadIdx.x < R)
+            *(uint32_t*)(s_row + b * R * (C / 32) + (r0 + threadIdx.x) * (C / 32) + c0 / 32) =
+                *(const uint32_t*)(s_rs + 4 * threadIdx.x);
+        if (cs_words && threadIdx.x >= QT && c0 + (int)threadIdx.x - QT < C)
+            *(uint32_t*)(sc + (int64_t)(c0 + threadIdx.x - QT) * RB + r0 / 32) =
+                *(const uint32_t*)(s_cs + 4 * (threadIdx.x - QT));
 #pragma unroll
         for (int it = 0; it < QT * QT / (16 * 256); ++it) {
             const int idx = it * 256 + threadIdx.x;
