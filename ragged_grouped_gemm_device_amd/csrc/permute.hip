@@ -16,12 +16,25 @@
 namespace moe {
 
 constexpr int kUnroll = 4;
+// Streaming (non-temporal) 16-byte accesses: data touched once and larger than
+// the last-level cache bypasses it instead of evicting what the next kernel reads.
+typedef uint32_t nt_u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const nt_u32x4_t*)p));
+}
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4_t, v), (nt_u32x4_t*)p);
+}
+// bytes one launch moves above which it streams (twice the 256 MB last-level cache)
+constexpr int64_t kStreamBytes = 512ll << 20;
+
 
 // x_perm[row_of[t*k + j]] = x[t]; padding rows of every expert region are
 // zero. Token-major: each token row is read from HBM once and written to its
 // k rows (a destination-major gather would read it k times). The workgroups
 // past main_blocks clear the padding, which sits in the last 127 rows of a
 // region (regions are 128-row multiples and start with their real rows).
+template <bool NT_STORE>
 __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ x,
                                                       const int32_t* __restrict__ row_of,
                                                       const int32_t* __restrict__ src_of,
@@ -37,7 +50,7 @@ __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ 
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t i = i0 + (int64_t)u * 256;
-                if (i < total) v[u] = x[i];
+                if (i < total) v[u] = ld_stream(x + i);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -48,7 +61,10 @@ __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ 
                     const int32_t* ro = row_of + t * k;
                     for (int j = 0; j < k; ++j) {
                         const int64_t r = ro[j];
-                        if ((uint64_t)r < (uint64_t)M_cap) x_perm[r * cpr + c] = v[u];  // guard only
+                        if ((uint64_t)r < (uint64_t)M_cap) {  // guard only
+                            if constexpr (NT_STORE) st_stream(x_perm + r * cpr + c, v[u]);
+                            else x_perm[r * cpr + c] = v[u];
+                        }
                     }
                 }
             }
@@ -68,6 +84,7 @@ __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ 
 }
 
 // out[t] = sum_j w[t, j] * y[row_of[t*k+j]] in ascending j (fp32), bf16 once.
+template <bool NT>
 __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ y,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, int k, int cpr,
@@ -93,7 +110,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
                     const int c = (int)(i - t * cpr);
                     const int64_t r = row_of[t * k + j];
                     wj[u] = w ? w[t * k + j] : 1.f;
-                    v[u] = y[r * cpr + c];
+                    v[u] = NT ? ld_stream(y + r * cpr + c) : y[r * cpr + c];
                 }
             }
 #pragma unroll
@@ -114,7 +131,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
                 o.y = pack_bf16x2(acc[u][2], acc[u][3]);
                 o.z = pack_bf16x2(acc[u][4], acc[u][5]);
                 o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-                out[i] = o;
+                if constexpr (NT) st_stream(out + i, o);
+                else out[i] = o;
             }
         }
     }
@@ -133,8 +151,16 @@ int launch_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_
     const int cpr = d / 8;
     const int main_blocks = grid_for((int64_t)T * cpr, 256 * kUnroll);
     const int pad_blocks = std::min(256, (E * 127 + 3) / 4);
-    permute_kernel<<<main_blocks + pad_blocks, 256, 0, s>>>((const uint4*)x, row_of, src_of, offsets,
-                                                            T, k, E, cpr, M_cap, main_blocks, (uint4*)x_perm);
+    // x is read once: streaming loads. The permuted copy streams too when it is
+    // one plain copy (k = 1) too large for the last-level cache; with k > 1, or
+    // smaller, the normal stores measured faster over the whole step.
+    const bool nt_store = k == 1 && (int64_t)T * d * 2 >= kStreamBytes;
+    if (nt_store)
+        permute_kernel<true><<<main_blocks + pad_blocks, 256, 0, s>>>((const uint4*)x, row_of, src_of, offsets, T, k,
+                                                                    E, cpr, M_cap, main_blocks, (uint4*)x_perm);
+    else
+        permute_kernel<false><<<main_blocks + pad_blocks, 256, 0, s>>>((const uint4*)x, row_of, src_of, offsets, T, k,
+                                                                     E, cpr, M_cap, main_blocks, (uint4*)x_perm);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
@@ -142,8 +168,11 @@ int launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, int
                    uint16_t* out, hipStream_t s) {
     const int cpr = d / 8;
     const int64_t total = (int64_t)T * cpr;
-    combine_kernel<<<grid_for(total, 512), 256, 0, s>>>((const uint4*)y, row_of, w, k, cpr, total,
-                                                        (uint4*)out);
+    const bool nt = (int64_t)T * k * d * 2 >= kStreamBytes;  // the Y rows read
+    if (nt)
+        combine_kernel<true><<<grid_for(total, 512), 256, 0, s>>>((const uint4*)y, row_of, w, k, cpr, total, (uint4*)out);
+    else
+        combine_kernel<false><<<grid_for(total, 512), 256, 0, s>>>((const uint4*)y, row_of, w, k, cpr, total, (uint4*)out);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
