@@ -129,18 +129,23 @@ struct ScaleSrc {
 // buffer end: the API bounds keep every operand region under 2^31 bytes, so
 // the sums cannot wrap.
 template <int GATHER>
-__device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave) {
+// part: 0 = the A slab's copies only, 1 = the B slab's only, 2 = both.
+__device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave, int part = 2) {
     const uint32_t da = (uint32_t)ks * sr.a_step, db = (uint32_t)ks * sr.b_step;
     const i32x4_t ra = rsrc_words(sr.a_base, sr.a_bytes);
     const i32x4_t rb = rsrc_words(sr.b_base, sr.b_bytes);
     const uint32_t l0 = (uint32_t)(uintptr_t)lds + wave * 1024;
+    if (part != 1) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
         lds_copy16(ra, l0 + i * kWaves * 1024, GATHER == 1 ? sr.g_off[i] + da : sr.a_off + (da + i * sr.a_istep));
+    }
+    if (part != 0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
         lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024,
                    GATHER == 2 ? sr.g_off[i] + db : sr.b_off + (db + i * sr.b_istep));
+    }
 }
 
 // GATHER: 0, or the operand (1 = A, 2 = B) whose rows are read from an
@@ -339,7 +344,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             }
         }
     };
-    auto issue = [&](const SlabSrc& sr, int ks_idx, int buf) {
+    auto issue = [&](const SlabSrc& sr, int ks_idx, int buf, int part = 2) {
         LDS_AS char* lds = (LDS_AS char*)(&s_ab[buf][0]);
         if constexpr (RAGGED_K && GATHER != 0) {
             // MN-major gathered operand: chunk (k row, column c) of token tok
@@ -358,7 +363,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             for (int i = 0; i < kLoads; ++i) g.g_off[i] = col < lim ? ro[i] + (uint32_t)(col * 2) : kMasked;
             issue_slab<GATHER>(g, ks_idx, lds, wave);  // the gathered operand's slab step is 0
         } else {
-            issue_slab<GATHER>(sr, ks_idx, lds, wave);
+            issue_slab<GATHER>(sr, ks_idx, lds, wave, part);
         }
     };
 
@@ -484,6 +489,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     int nk = (tl.k_end - tl.k_begin) / BK;
     int buf0 = 0;  // LDS buffer holding slab 0 of the current tile
     constexpr bool kTok = RAGGED_K && GATHER != 0;
+    constexpr bool kSplitCopies = !kTok && !MX && EPI != EPI_DGLU;  // A and B copies in different K steps
     // (a non-empty ragged-K tile has at least two slabs: expert regions are
     // 128-row multiples, so the token prefetch below never runs past a tile)
     if (nk > 0) {
@@ -541,20 +547,20 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 // the second MFMA row of the slab's first K step, so that the
                 // first MFMAs after the barrier do not wait behind the copies'
                 // issue; they still have most of the slab to land.
-                auto do_issue = [&]() {
+                auto do_issue = [&](int part) {
                 if (!last) {
-                    issue(src, kt + 1, cur ^ 1);
+                    issue(src, kt + 1, cur ^ 1, part);
                     if constexpr (kTok) {
                         if (kt + 2 < nk) fetch_toks(tl, kt + 2);
                         else if (nk_next > 0) fetch_toks(tl_next, 0);
                     }
                 } else if (nk_next > 0) {
-                    issue(src_next, 0, cur ^ 1);
+                    issue(src_next, 0, cur ^ 1, part);
                     if constexpr (MX) issue_scales(make_scales(tl_next), 0, (sg0 + ng) & 1);
                     if constexpr (kTok) fetch_toks(tl_next, 1);
                 }
                 };
-                if constexpr (MX) do_issue();
+                if constexpr (MX) do_issue(2);
                 if constexpr (MX) {
                     // the next group's scales go to the buffer the previous group
                     // left (its last reads ended before the previous slab barrier);
@@ -594,7 +600,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int j = 0; j < TNW; ++j)
                         acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][1], acc[1][j], 0, 0, 0);
-                    if constexpr (ks == 0) do_issue();  // the next slab's copies, after the second MFMA row
+                    // the next slab's A copies here and its B copies one K step later,
+                    // spreading the copy issue and the LDS writes it causes (both at
+                    // once with a token table, and for the dGLU epilogue kernel, which
+                    // measured slower split)
+                    if constexpr (ks == 0) do_issue(kSplitCopies ? 0 : 2);
+                    if constexpr (ks == 1 && kSplitCopies) {
+                        if (!last) issue(src, kt + 1, cur ^ 1, 1);
+                        else if (nk_next > 0) issue(src_next, 0, cur ^ 1, 1);
+                    }
 #pragma unroll
                     for (int i = 2; i < 4; ++i)
 #pragma unroll
