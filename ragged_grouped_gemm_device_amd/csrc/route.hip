@@ -4,7 +4,8 @@
 //   token (8, 16, 32 or 64 lanes, the smallest that holds E, 64 beyond 32).
 //   [Dropless MoE 학습과 NVIDIA Transformer Engine 소개, section on ragged
 //   tensors: a learned router activates each token's top-K experts.]
-// route_bwd_kernel: the router's softmax backward from dS.
+// route_bwd_kernel: the router's softmax backward from dS (one wavefront per
+//   token; route_bwd_group_kernel: one group of 8, 16 or 32 lanes when E <= 32).
 // layout kernels: per-expert counts, 128-aligned offsets and the two row maps,
 //   computed on the device with no host readback, deterministically (a stable
 //   counting sort: per-chunk histograms, an exclusive scan over chunks, then
@@ -302,9 +303,78 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const float* __restrict_
     }
 }
 
+// The same for E <= G = 8, 16 or 32: one group of G lanes per token, lane gl
+// holding logit gl, so small expert counts do not leave most of a wavefront
+// idle. The chosen slots' probabilities come from the lanes holding their
+// logits (a lane exchange inside the group), in slot order.
+template <int G>
+__global__ void __launch_bounds__(256) route_bwd_group_kernel(const float* __restrict__ logits, int T, int E,
+                                                              int k, int renorm,
+                                                              const int32_t* __restrict__ topk_idx,
+                                                              const float* __restrict__ ds,
+                                                              float* __restrict__ dlogits) {
+    const int lane = lane_id();
+    const int gl = lane % G, gbase = lane - gl;
+    const int t = (int)(((int64_t)blockIdx.x * 256 + threadIdx.x) / G);
+    const bool live = t < T;
+    const bool own = live && gl < E;
+    float x = -INFINITY;
+    if (own) {
+        x = logits[(int64_t)t * E + gl];
+        if (!isfinite(x)) x = -INFINITY;
+    }
+    float mx = x;
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float s = x > -INFINITY ? expf(x - mx) : 0.f;
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    if (!(mx > -INFINITY)) s = 1.f;
+    const float inv_s = 1.f / s;
+    // P = sum of the chosen probabilities, c = sum_j p_j dS_j; and this lane's
+    // slot (its dS and probability) if its expert was chosen
+    float pj_sum = 0.f, c = 0.f, dsel = 0.f, psel = 0.f;
+    bool chosen = false;
+    for (int j = 0; j < k; ++j) {
+        const int ej = live ? topk_idx[(int64_t)t * k + j] : 0;
+        const float dj = live ? ds[(int64_t)t * k + j] : 0.f;
+        const float xj = __shfl(x, gbase + (ej & (G - 1)), 64);
+        const float pj = xj > -INFINITY ? expf(xj - mx) * inv_s : 0.f;
+        pj_sum += pj;
+        c += pj * dj;
+        if (ej == gl) {
+            chosen = true;
+            dsel = dj;
+            psel = pj;
+        }
+    }
+    if (renorm) c = pj_sum > 0.f ? c / pj_sum : 0.f;  // sum_j w_j dS_j
+    if (!own) return;
+    float out;
+    if (renorm) {
+        const float wj = pj_sum > 0.f ? psel / pj_sum : 0.f;
+        out = chosen ? wj * (dsel - c) : 0.f;
+    } else {
+        const float pe = x > -INFINITY ? expf(x - mx) * inv_s : 0.f;
+        out = pe * ((chosen ? dsel : 0.f) - c);
+    }
+    dlogits[(int64_t)t * E + gl] = out;
+}
+
 int launch_route_bwd(const float* logits, int T, int E, int k, int renorm, const int32_t* topk_idx,
                      const float* ds, float* dlogits, hipStream_t s) {
-    route_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, ds, dlogits);
+    auto grouped = [&](auto kern, int g) {
+        const int64_t blocks = ((int64_t)T * g + 255) / 256;
+        kern<<<(unsigned)blocks, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, ds, dlogits);
+    };
+    if (E <= 8)
+        grouped(route_bwd_group_kernel<8>, 8);
+    else if (E <= 16)
+        grouped(route_bwd_group_kernel<16>, 16);
+    else if (E <= 32)
+        grouped(route_bwd_group_kernel<32>, 32);
+    else
+        route_bwd_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, ds, dlogits);
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
