@@ -543,9 +543,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 const int cur = (buf0 + kt) & 1;
                 const bool last = kt + 1 == nk;
-                // The next slab's copies. In the bf16 modes they are issued after
-                // the second MFMA row of the slab's first K step, so that the
-                // first MFMAs after the barrier do not wait behind the copies'
+                // The next slab's copies (part: 0 = A, 1 = B, 2 = both). In the bf16
+                // modes they are issued after the second MFMA row of the slab's
+                // first K step (the B copies one step later when split), so that
+                // the first MFMAs after the barrier do not wait behind the copies'
                 // issue; they still have most of the slab to land.
                 auto do_issue = [&](int part) {
                 if (!last) {
