@@ -174,8 +174,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     const int ntm = RAGGED_K ? (p.M + BM - 1) / BM : 0;
 
     // ---------------------------------------------------------- schedule
-    // Persistent workgroups walk a logical tile order. Ragged M: bands of 8 M
-    // tiles with N tiles inner, and each XCD (workgroups are dealt to the 8
+    // Persistent workgroups walk a logical tile order. Ragged M: bands of 4 M
+    // tiles (8 in the MX mode) with M tiles inner, and each XCD (workgroups are dealt to the 8
     // XCDs round robin) takes a contiguous run of 1/8 of every round. Ragged
     // K: experts by descending row count (longest tiles first), so the tail
     // of the schedule holds the short tiles.
@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     auto get_tile = [&](int t) -> Tile {
         Tile tl;
         if constexpr (!RAGGED_K) {
-            const RaggedTile r = ragged_m_decode(p.offsets, p.E, ntn, total / ntn, s_tiles, t);
+            const RaggedTile r = ragged_m_decode<MX ? 8 : 4>(p.offsets, p.E, ntn, total / ntn, s_tiles, t);
             tl.e = __builtin_amdgcn_readfirstlane(r.e);
             tl.row0 = __builtin_amdgcn_readfirstlane(r.row0);
             tl.row_end = __builtin_amdgcn_readfirstlane(r.row_end);

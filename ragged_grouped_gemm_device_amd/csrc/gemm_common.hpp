@@ -113,12 +113,16 @@ __device__ __forceinline__ int ragged_m_prefix(const int32_t* offsets, int E, in
     return s_tiles[E];
 }
 
-// Tile number tt (of mtiles * ntn) -> tile: bands of 8 M tiles with the N
-// tiles inner, so neighbouring tiles share B column slabs; the expert is the
-// last one whose first M tile is <= the tile's M index.
+// Tile number tt (of mtiles * ntn) -> tile: bands of G M tiles with the M
+// tiles inner, so that the 32 tiles one XCD runs at a time (a contiguous run)
+// form a G x (32 / G) window whose operand panels its L2 shares; the expert is
+// the last one whose first M tile is <= the tile's M index. The bf16 GEMMs
+// use G = 4 (measured 1% faster on FC1 than 8, whose 8 x 4 window has the
+// same panel count; 16 was 2% slower); the MXFP8 GEMMs keep G = 8 (1.5-3.5%
+// slower with 4).
+template <int G = 8>
 __device__ __forceinline__ RaggedTile ragged_m_decode(const int32_t* offsets, int E, int ntn, int mtiles,
                                                       const int* s_tiles, int tt) {
-    constexpr int G = 8;
     const int band = tt / (G * ntn);
     const int within = tt - band * G * ntn;
     const int bm = min(G, mtiles - band * G);
