@@ -280,8 +280,14 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
             const int slot = t / per;
             const int r = t - slot * per;
             tl.e = __builtin_amdgcn_readfirstlane(s_tiles[slot]);
-            tl.m0 = (r / ntn) * BM;
-            tl.n0 = (r % ntn) * BN;
+            // bands of 4 M tiles, M inner: an XCD's 32 consecutive tiles form a
+            // 4 x 8 window of the expert's output (12 operand panels), not a 1 x 32 row
+            constexpr int GK = 4;
+            const int band = r / (GK * ntn);
+            const int within = r - band * GK * ntn;
+            const int bm = min(GK, ntm - band * GK);
+            tl.m0 = (band * GK + within % bm) * BM;
+            tl.n0 = (within / bm) * BN;
             tl.row0 = tl.row_end = 0;
             tl.k_begin = __builtin_amdgcn_readfirstlane(p.offsets[tl.e]);
             tl.nk = (__builtin_amdgcn_readfirstlane(p.offsets[tl.e + 1]) - tl.k_begin) / MBK;
