@@ -64,6 +64,16 @@ def _t16(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
     """Time the oracle on the first R tokens (routed like the full batch)."""
     from threadpoolctl import threadpool_info
@@ -92,6 +102,8 @@ def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
         "value": flops / dt2 / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"first {R2} of {wl.T} tokens of the {wl.name} workload (top-{wl.k}), whole "
                   f"forward+backward in numpy fp64, {dt2:.1f} s wall",
@@ -101,7 +113,7 @@ def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="balanced")
     ap.add_argument("--act", choices=["swiglu", "geglu", "srelu"], default="swiglu",
@@ -159,39 +171,66 @@ def main():
         buf.quantize_weights(w1, w2)
         mx = buf.mx_fwd()   # FC1 on x_q / w1t_q, FC2 on a_q / w2t_q
 
-    ev = []  # (start, end) of the FC1 launch in each timed step
+    # (start, end) events of the launches timed inside every timed step: FC1 (the roofline
+    # kernel) and the memory-bound permute / combine kernels (the bandwidth object)
+    ev = {}
+
+    def timed(record, name, fn):
+        if not record:
+            fn()
+            return
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev.setdefault(name, []).append((e0, e1))
+
+    QRC = M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE
 
     def step(record=False):
         M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets,
                            buf.row_of, buf.src_of, buf.M_cap, buf.err, buf.route_ws)
         if mx_mode:
             # X_perm only as MXFP8: row-wise (FC1) and column-wise (FC1 wgrad), fused with the permute
-            M.moe_permute_quant_mxfp8(x, buf.src_of, wl.k, wl.E, M.MOE_QUANT_ROWWISE | M.MOE_QUANT_COLWISE,
-                                      buf.x_q, buf.x_s, buf.xt_q, buf.xt_s)
+            timed(record, "permute+quant x", lambda: M.moe_permute_quant_mxfp8(
+                x, buf.src_of, wl.k, wl.E, QRC, buf.x_q, buf.x_s, buf.xt_q, buf.xt_s))
             buf.xt_from_forward = True
         elif not args.gather:
-            M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            timed(record, "permute x", lambda: M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets,
+                                                             wl.k, wl.E, buf.x_perm))
         if args.gather:
-            M.moe_grouped_mlp_fwd(x, w1, w2, buf.offsets, buf.h, buf.a, buf.y,
-                                  M.MOE_STAGE_FC1 | M.MOE_GATHER_ROWS, mx=mx, act=act,
-                                  src_of=buf.src_of, k=wl.k)
+            timed(record, "fc1", lambda: M.moe_grouped_mlp_fwd(
+                x, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGE_FC1 | M.MOE_GATHER_ROWS,
+                mx=mx, act=act, src_of=buf.src_of, k=wl.k))
         else:
             # with MXFP8 the bf16 A is not written: FC2 reads its MXFP8 copy
-            M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a,
-                                  buf.y, M.MOE_STAGE_FC1, mx=mx, act=act)
-        if record:
-            e1.record(stream)
-            ev.append((e0, e1))
+            timed(record, "fc1", lambda: M.moe_grouped_mlp_fwd(
+                buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a, buf.y,
+                M.MOE_STAGE_FC1, mx=mx, act=act))
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a, buf.y,
                               M.MOE_STAGE_FC2, mx=mx)
-        M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out)
-        # with MXFP8 the FC2 dgrad writes only the MXFP8 copies of dH and A' (all the later
-        # MXFP8 GEMMs read)
-        M.backward(buf, dout, w1, w2, act=act, logits=logits, x=x if args.gather else None,
-                   mx=mx_mode, mx_bf16_copies=False)
+        timed(record, "combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out))
+        # backward: the same calls as moe.backward, written out so that the memory-bound
+        # launches can be timed one by one
+        if mx_mode:
+            timed(record, "permute+quant dO", lambda: M.moe_permute_quant_mxfp8(
+                dout, buf.src_of, wl.k, wl.E, QRC, buf.dy_q, buf.dy_s, buf.dyt_q, buf.dyt_s))
+            # the FC2 dgrad writes only the MXFP8 copies of dH and A' (all the later MXFP8 GEMMs read)
+            M.moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
+                                  buf.offsets, None, None, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                                  buf.bwd_ws, M.MOE_STAGES_BWD, act=act, mx=buf.mx_bwd(True))
+        elif args.gather:
+            M.moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
+                                  buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                                  buf.bwd_ws, M.MOE_STAGES_BWD | M.MOE_GATHER_ROWS, act=act)
+        else:
+            timed(record, "permute dO", lambda: M.moe_permute(dout, buf.row_of, buf.src_of, buf.offsets,
+                                                              wl.k, wl.E, buf.dy_u))
+            M.moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
+                                  buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
+                                  buf.bwd_ws, M.MOE_STAGES_BWD, act=act)
+        timed(record, "unpermute-sum dX", lambda: M.moe_combine(buf.dx_perm, buf.row_of, None, wl.k, buf.dx))
+        M.moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits)
 
     for _ in range(args.warmup):
         step()
@@ -208,8 +247,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
-    fc1_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    avg_ms = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) for name, pairs in ev.items()}
+    fc1_ms = avg_ms["fc1"]
     assert int(buf.err.item()) == 0
+    bandwidth = _bandwidth(wl, buf, avg_ms, mx_mode)
+    for name, r in bandwidth["kernels"].items():
+        print(f"[bench] {name:18s} {r['us']:8.1f} us  {r['GBps']:8.1f} GB/s ({100 * r['frac']:.1f}% HBM)",
+              file=sys.stderr, flush=True)
 
     M_rows = wl.T * wl.k
     # FC1 is 2 M d n1 with n1 = 2n (gated) or n (sReLU); FC2, and each of the four backward
@@ -268,9 +312,42 @@ def main():
             "traffic": measured_traffic(wl.name) if act == M.MOE_ACT_SWIGLU else None,
             "traffic_unit": "bytes per launch",
         },
+        "bandwidth": bandwidth,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def _bandwidth(wl, buf, avg_ms, mx_mode):
+    """Achieved HBM rate of the memory-bound launches of the step: algorithmic bytes (what
+    the method must move for the T*k real pairs; padding rows and re-reads are overhead
+    charged to the kernel) over the launch's average time from HIP events on its stream
+    inside the timed steps."""
+    T, k, d = wl.T, wl.k, wl.d
+    P = T * k
+    model = {
+        # read x once and row_of, write k copies of each row
+        "permute x": (2.0 * T * d + 4.0 * P + 2.0 * P * d, "gather x [T, d] -> X_perm; 2Td + 4Tk + 2Tkd"),
+        "permute dO": (2.0 * T * d + 4.0 * P + 2.0 * P * d, "gather dO [T, d] -> dY_u; 2Td + 4Tk + 2Tkd"),
+        # read the k rows, row_of and the weights of every token, write the token row
+        "combine": (2.0 * P * d + 8.0 * P + 2.0 * T * d, "weighted sum of Y rows -> out; 2Tkd + 8Tk + 2Td"),
+        "unpermute-sum dX": (2.0 * P * d + 4.0 * P + 2.0 * T * d, "sum of dX_perm rows -> dX; 2Tkd + 4Tk + 2Td"),
+        # read x once and src_of, write row- and column-wise codes (1 B) plus scales (1 B / 32)
+        "permute+quant x": (2.0 * T * d + 4.0 * P + 2.0 * P * d * 33 / 32,
+                            "gather x + MXFP8 row and column copies; 2Td + 4Tk + 2Tkd(1 + 1/32)"),
+        "permute+quant dO": (2.0 * T * d + 4.0 * P + 2.0 * P * d * 33 / 32,
+                             "gather dO + MXFP8 row and column copies; 2Td + 4Tk + 2Tkd(1 + 1/32)"),
+    }
+    kernels = {}
+    for name, ms in avg_ms.items():
+        if name not in model:
+            continue
+        by, formula = model[name]
+        gbs = by / (ms * 1e-3) / 1e9
+        kernels[name] = {"bytes": by, "us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_model": formula}
+    return {"unit": "GB/s", "peak": PEAK_HBM_GBS, "timing": "HIP events on the launch stream, "
+            "average over the timed steps", "kernels": kernels}
 
 
 def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0, glu="SwiGLU",

@@ -33,8 +33,12 @@ Readings where the pages are silent (each listed in the design notes):
   * A' = w * A (routing-weighted activation) and dW in fp64/fp32;
   * MXFP8 blocks of 32 elements (OCP MX v1.0 element and scale formats) with
     the shared exponent rounded up so that no element saturates: the smallest
-    e with amax <= 448 * 2^e (the Transformer Engine MXFP8 recipe rounds the
-    scale up); E4M3 codes rounded to nearest-even, zero block -> scale 0.
+    e with amax <= 448 * 2^e; E4M3 codes rounded to nearest-even, zero block
+    -> scale 0. The pages name MXFP8 but give no scale rule. The floor rule
+    (floor(log2 amax) - 8) would clip a block maximum whose significand is
+    above 1.75 to 448 * 2^e, an error of up to 12.5% of that element, beyond
+    the 6e-2 tolerance the MXFP8 path is held to; the rounded-up exponent
+    never clips, at the cost of one binade of resolution for such blocks.
 
 Parity pins live in tests/test_oracle_*.py.
 """

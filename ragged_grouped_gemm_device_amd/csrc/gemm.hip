@@ -161,7 +161,6 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // per stage: the A slab (BM x BK) then the B slab (BN x BK), 64 KiB
     __shared__ __attribute__((aligned(1024))) uint16_t s_ab[2][(BM + BN) * BK];
     __shared__ int s_tiles[MOE_MAX_E + 1];  // ragged M: tile prefix; ragged K: experts by work
-    __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
     // MX: block scales of 4 consecutive slabs (a group), 16 bytes for each of the
     // BM A rows then the BN B rows, double-buffered by group
     __shared__ __attribute__((aligned(1024))) uint8_t s_sc[MX ? 2 : 1][MX ? (BM + BN) * 16 : 16];
@@ -183,18 +182,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     if constexpr (!RAGGED_K) {
         total = ragged_m_prefix(p.offsets, p.E, s_tiles) * ntn;
     } else {
-        for (int i = tid; i < p.E; i += kThreads) s_rows[i] = p.offsets[i + 1] - p.offsets[i];
-        __syncthreads();
-        for (int i = tid; i < p.E; i += kThreads) {
-            const int ri = s_rows[i];
-            int rank = 0;
-            for (int j = 0; j < p.E; ++j) {
-                const int rj = s_rows[j];
-                rank += (rj > ri) || (rj == ri && j < i);
-            }
-            s_tiles[rank] = i;
-        }
-        __syncthreads();
+        // sort keys in the operand stage, which no copy has touched yet
+        experts_by_rows<kThreads>(p.offsets, p.E, (uint64_t*)&s_ab[0][0], s_tiles);
         total = p.E * ntm * ntn;
     }
     // Round r covers tiles [r nb, (r + 1) nb); within it, XCD x (workgroups

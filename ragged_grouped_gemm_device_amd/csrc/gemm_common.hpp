@@ -4,6 +4,7 @@
 #pragma once
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -151,18 +152,56 @@ __device__ __forceinline__ bool ragged_m_tile(const int32_t* offsets, int E, int
     return true;
 }
 
-// Compute units of the current device (cached per device).
+// Ragged-K scheduling: the experts ordered by descending row count (ties to
+// the lower index), so the longest wgrad tiles start first and the short ones
+// fill the tail. A bitonic sort of 64-bit keys (rows << 11 | 1024 | 1023 - e:
+// the 1024 bit keeps every real key above the zero padding of the power-of-
+// two array) in LDS scratch `key` of at least 1024 entries; order[0, E) gets
+// the expert indices. log2(P) (log2(P) + 1) / 2 barrier steps for P >= E, one
+// compare-exchange per thread and step at P = 1024. Must be called by the
+// whole workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ void experts_by_rows(const int32_t* offsets, int E, uint64_t* key, int* order) {
+    const int tid = threadIdx.x;
+    int P = 1;
+    while (P < E) P <<= 1;
+    for (int i = tid; i < P; i += NT)
+        key[i] = i < E ? ((uint64_t)(uint32_t)(offsets[i + 1] - offsets[i]) << 11) | 1024u | (uint32_t)(1023 - i)
+                       : 0ull;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P; i += NT) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint64_t a = key[i], b = key[l];
+                    const bool desc = (i & k) == 0;  // the last merge (k = P) is descending throughout
+                    if (desc ? a < b : a > b) {
+                        key[i] = b;
+                        key[l] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = tid; i < E; i += NT) order[i] = 1023 - (int)(key[i] & 1023u);
+    __syncthreads();
+}
+
+// Compute units of the current device, cached per device on first use (the
+// only state the library keeps; concurrent first calls store the same value).
 inline int device_cus() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] <= 0) {
-        int v = 0;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
             v = 256;
-        cache[dev] = v;
+        cache[dev].store(v, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return v;
 }
 
 // Persistent grid: one workgroup per compute unit (the LDS footprint allows

@@ -229,7 +229,6 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     // BM A rows then the BN B rows, double-buffered by group
     __shared__ __attribute__((aligned(1024))) uint8_t s_sc[2][(BM + BN) * 16];
     __shared__ int s_tiles[MOE_MAX_E + 1];
-    __shared__ int s_rows[RAGGED_K ? MOE_MAX_E : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / (kWaves / 2), wn = wave % (kWaves / 2);  // 2 x (kWaves / 2) wavefront grid
@@ -242,18 +241,8 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     if constexpr (!RAGGED_K) {
         total = ragged_m_prefix(p.offsets, p.E, s_tiles) * ntn;
     } else {
-        for (int i = tid; i < p.E; i += kThreads) s_rows[i] = p.offsets[i + 1] - p.offsets[i];
-        __syncthreads();
-        for (int i = tid; i < p.E; i += kThreads) {
-            const int ri = s_rows[i];
-            int rank = 0;
-            for (int j = 0; j < p.E; ++j) {
-                const int rj = s_rows[j];
-                rank += (rj > ri) || (rj == ri && j < i);
-            }
-            s_tiles[rank] = i;
-        }
-        __syncthreads();
+        // sort keys in the operand stage, which no copy has touched yet
+        experts_by_rows<kThreads>(p.offsets, p.E, (uint64_t*)&s_ab[0][0], s_tiles);
         total = p.E * ntm * ntn;
     }
     const int nb = gridDim.x;  // a multiple of 8

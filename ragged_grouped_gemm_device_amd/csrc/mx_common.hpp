@@ -4,7 +4,9 @@
 // activations become MXFP8 plus a transposed copy; Transformer Engine page,
 // three-components section: group-aware MXFP8 quantization.] The pages give
 // no encoding rule; the OCP Microscaling (MX) v1.0 formats are used with the
-// scale rounded up (as the Transformer Engine MXFP8 recipe does): a block of
+// scale rounded up, so that no element of a block is clipped (the floor rule
+// clips block maxima with a significand above 1.75 by up to 12.5%, more than
+// the MXFP8 path's 6e-2 error budget): a block of
 // 32 elements shares the smallest exponent e with amax <= 448 * 2^e, clamped
 // to [-127, 127], stored as E8M0 (e + 127); an all-zero block takes code 0.
 // Elements are v / 2^e in E4M3 (1-4-3, bias 7, no infinities), rounded to

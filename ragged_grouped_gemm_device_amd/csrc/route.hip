@@ -103,8 +103,10 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
             if (j < 8) {
                 p = chosen_w[j];
             } else {
-                const int e = topk_idx[(int64_t)t * k + j];
-                p = expf(row[e] - mx) / s;  // k > 8: recompute from the logit
+                // k > 8: recompute from the logit; a non-finite one weighs 0, as
+                // in the selection above
+                const float x = row[topk_idx[(int64_t)t * k + j]];
+                p = isfinite(x) ? expf(x - mx) / s : 0.f;
             }
             topk_w[(int64_t)t * k + j] = p * inv;
         }

@@ -20,7 +20,7 @@ import torch
 from oracle import moe_oracle as O
 from ragged_grouped_gemm_device_amd import workloads as W
 
-from ._util import bf16_tensor, bf16_values, f32_tensor, rel_err
+from ._util import bf16_tensor, bf16_values, check_fused_copies_vs_oracle, f32_tensor, rel_err
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -238,6 +238,12 @@ def test_fullsize_mxfp8_step(M):
         err = rel_err(got, ref)
         print(f"  {key}: {err:.3e}", flush=True)
         assert err <= tol, key
+    # every fused MXFP8 copy over the whole region of expert 0 (rows 0..4095):
+    # the oracle's quantization of the GPU's own bf16 A, dH and A', bit for bit
+    check_fused_copies_vs_oracle(buf.a[:4096], 4096, buf.a_q, buf.a_s, None, None, "A (expert 0)")
+    check_fused_copies_vs_oracle(buf.dh[:4096], 4096, buf.dh_q, buf.dh_s, buf.dht_q, buf.dht_s,
+                                 "dH (expert 0)")
+    check_fused_copies_vs_oracle(buf.a_w[:4096], 4096, None, None, buf.awt_q, buf.awt_s, "A' (expert 0)")
     # column-wise copies of two 32-row blocks of expert 0: X from the oracle's
     # permutation, dH and A' from the GPU's own bf16 values (bit-exact)
     xp = O.from_bf16(inp["x"][:4096])          # expert 0 holds tokens 0..4095 in order

@@ -26,6 +26,9 @@ CASES = [
     W.small("empty", T=300, k=2, E=16, d=256, n=128, seed=22, routing="zipf"),
     W.small("wide", T=1200, k=2, E=4, d=512, n=384, seed=23),
     W.small("balanced", T=1024, k=1, E=4, d=256, n=256, seed=24, routing="balanced"),
+    # many experts, most of them empty or with equal counts: the ragged-K schedule's
+    # sort of experts by rows (300 keys padded to 512), ties and zero-row experts
+    W.small("many-experts", T=512, k=4, E=300, d=128, n=64, seed=25, routing="normal"),
 ]
 
 

@@ -4,9 +4,11 @@ epilogue of FC1 and the MX-scaled grouped FC2.
 * Standalone quantization: codes and scales bit-exact against the oracle on
   seeded inputs (with outliers), on every finite bf16 pattern, and on edge
   cases (zero blocks, subnormals, saturation, partial tiles, batches).
-* Fused epilogue: its codes equal the standalone kernel's codes on the same
-  bf16 A (GPU-internal consistency; the standalone kernel is pinned to the
-  oracle above), and dequantize to within 6e-2 of the oracle's A.
+* Fused epilogue: its codes and scales equal, bit for bit, the oracle's
+  quantization of the GPU's own bf16 A over the whole expert region (the two
+  A's may differ in the last bf16 bit, so codes are compared on the GPU's A);
+  as an extra, they equal the standalone kernel's codes of the same A, and
+  they dequantize to within 6e-2 of the oracle's A.
 * MX FC2: within 6e-2 of the oracle's MX forward from the same seeded inputs;
   on identical codes (verified bit-exact) within 1e-2.
 """
@@ -17,7 +19,7 @@ import torch
 from oracle import moe_oracle as O
 from ragged_grouped_gemm_device_amd import workloads as W
 
-from ._util import bf16_tensor, bf16_values, f32_tensor, rel_err
+from ._util import bf16_tensor, bf16_values, check_fused_copies_vs_oracle, f32_tensor, rel_err
 
 pytestmark = pytest.mark.gpu
 U8 = torch.uint8
@@ -166,7 +168,9 @@ def test_fused_quant_epilogue(M, wl, act, gather):
     buf = _run_mx_forward(M, wl, inp, act=M.MOE_ACT_GEGLU if act == "geglu" else M.MOE_ACT_SWIGLU,
                           gather=gather)
     end = int(buf.offsets[-1].item())
-    # GPU-internal: the fused codes equal the standalone quantization of the same A
+    # against the oracle: its quantization of the GPU's own bf16 A, bit for bit
+    check_fused_copies_vs_oracle(buf.a, end, buf.a_q, buf.a_s, buf.at_q, buf.at_s)
+    # GPU-internal extra: the fused codes equal the standalone quantization of the same A
     a_bits = buf.a.view(torch.int16).cpu().numpy().view(np.uint16)
     g = _gpu_quant(M, a_bits[:end], 3)
     assert np.array_equal(buf.a_q.cpu().numpy()[:end], g[0][0])
@@ -284,7 +288,9 @@ def test_mx_fc1_forward_parity(M, wl, act):
     err = rel_err(bf16_values(buf.out), out)
     print(f"  out: {err:.3e}", flush=True)
     assert err <= 6e-2
-    # the fused A copy equals the standalone quantization of the same bf16 A
+    # the fused A copy equals the oracle's quantization of the GPU's bf16 A, bit for bit
+    check_fused_copies_vs_oracle(buf.a, end, buf.a_q, buf.a_s, None, None)
+    # extra: and the standalone quantization kernel's copy of the same A
     a_bits = buf.a.view(torch.int16).cpu().numpy().view(np.uint16)
     g = _gpu_quant(M, a_bits[:end], 1)
     assert np.array_equal(buf.a_q.cpu().numpy()[:end], g[0][0])

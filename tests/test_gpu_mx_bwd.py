@@ -2,10 +2,11 @@
 the MX-scaled FC1 dgrad and the two MX-scaled ragged wgrads.
 
 * DGRAD2 stays bf16: dH, A' and dS within 2e-2 of the oracle (as the bf16 path).
-* Its fused MXFP8 copies equal the standalone quantization kernel's codes of
-  the same bf16 dH and A' (bit-exact; that kernel is pinned to the oracle),
-  and the column-wise dY_u / X_perm copies and row-wise W1 copy equal the
-  oracle's quantization of the (bit-exact) permuted inputs.
+* Its fused MXFP8 copies equal, bit for bit, the oracle's quantization of the
+  GPU's own bf16 dH and A' over the whole expert region (and, as an extra,
+  the standalone quantization kernel's copies of them); the column-wise
+  dY_u / X_perm copies and row-wise W1 copy equal the oracle's quantization
+  of the (bit-exact) permuted inputs.
 * The three MX GEMMs on the GPU's own codes: dW1 and dW2 within 1e-3 of the
   fp64 block-scaled product of those codes, dX_perm within 1e-2 (one bf16
   rounding). The scaled MFMA is not exact-products-plus-fp32-sum: on random
@@ -22,7 +23,7 @@ import torch
 from oracle import moe_oracle as O
 from ragged_grouped_gemm_device_amd import workloads as W
 
-from ._util import bf16_bits, bf16_tensor, bf16_values, f32_tensor, rel_err
+from ._util import bf16_bits, bf16_tensor, bf16_values, check_fused_copies_vs_oracle, f32_tensor, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +32,7 @@ CASES = [
     W.small("mxb-ragged", T=700, k=3, E=6, d=192, n=320, seed=21, routing="zipf"),
     W.small("mxb-empty", T=300, k=2, E=16, d=256, n=128, seed=22, routing="zipf"),
     W.small("mxb-wide", T=1200, k=2, E=4, d=640, n=384, seed=23),
+    W.small("mxb-many", T=400, k=4, E=300, d=128, n=128, seed=26, routing="zipf"),
 ]
 
 
@@ -110,7 +112,10 @@ def test_mx_backward_parity(M, wl, act, dgrad2_mx):
     _check("dH", bf16_values(buf.dh)[:end], b["dH"][:end], 2e-2)
     _check("A'", bf16_values(buf.a_w)[:end], b["a_w"][:end], 2e-2)
 
-    # fused copies == standalone quantization of the same bf16 tensors
+    # fused copies == the oracle's quantization of the GPU's own bf16 dH and A', bit for bit
+    check_fused_copies_vs_oracle(buf.dh, end, buf.dh_q, buf.dh_s, buf.dht_q, buf.dht_s, "dH")
+    check_fused_copies_vs_oracle(buf.a_w, end, None, None, buf.awt_q, buf.awt_s, "A'")
+    # extra: == the standalone quantization kernel's copies of the same bf16 tensors
     g = _gpu_quant(M, buf.dh[:end], 3)
     assert np.array_equal(_np(buf.dh_q)[:end], g[0]), "dH row codes"
     assert np.array_equal(_np(buf.dh_s)[:end], g[1]), "dH row scales"

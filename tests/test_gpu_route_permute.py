@@ -54,6 +54,8 @@ ROUTE_CASES = [
     (77, 1024, 6, "normal"),
     (4096, 16, 1, "constant"),
     (5000, 24, 4, "normal"),
+    (300, 64, 12, "normal"),     # k > 8: the renormalised weights of slots 8.. are recomputed
+    (200, 40, 16, "ties"),
 ]
 
 
@@ -95,6 +97,35 @@ def test_route_flags_nonfinite_logits(M):
     assert ((g["topk_idx"] >= 0) & (g["topk_idx"] < 8)).all()
     assert g["offsets"][-1] <= cap
     assert (np.sort(g["row_of"]) == np.unique(g["row_of"])).all()
+
+
+@pytest.mark.parametrize("k", [2, 12])
+def test_route_nonfinite_logits_renorm(M, k):
+    """With renormalisation (and k > 8, where slots 8.. take another code path) a
+    non-finite logit is never preferred and weighs 0, so every weight stays finite
+    in [0, 1] and each affected token's weights still sum to 1; rows with only
+    finite logits match the oracle exactly as before."""
+    T, E = 96, 64
+    lg = _logits(T, E, "normal", 11)
+    bad_rows = [3, 17, 40, 50]
+    lg[3, 5] = np.nan
+    lg[17, :20] = np.inf          # more non-finite logits than k - 8 ...
+    lg[40, ::2] = -np.inf         # ... and half of the row
+    lg[50, 6:] = np.nan           # fewer finite logits than k: slots 6.. pick non-finite ones
+    cap, g = _route(M, lg, k, renorm=True)
+    assert g["err"][0] & M.MOE_ERRBIT_NONFINITE_LOGIT
+    w = g["topk_w"]
+    assert np.isfinite(w).all() and (w >= 0).all() and (w <= 1).all()
+    np.testing.assert_allclose(w[bad_rows].sum(axis=1), 1.0, rtol=1e-5)
+    idx = g["topk_idx"]
+    assert ((idx >= 0) & (idx < E)).all()
+    for t in bad_rows:            # a chosen non-finite logit weighs exactly 0
+        chosen = lg[t, idx[t]]
+        assert (w[t][~np.isfinite(chosen)] == 0).all()
+    good = np.setdiff1d(np.arange(T), bad_rows)
+    o_idx, o_w = O.route(lg[good], k, renorm=True)
+    assert np.array_equal(idx[good], o_idx)
+    np.testing.assert_allclose(w[good], o_w, rtol=2e-6, atol=1e-7)
 
 
 @pytest.mark.parametrize("T,E,k,d", [(256, 8, 2, 128), (999, 13, 3, 200), (64, 4, 4, 8),

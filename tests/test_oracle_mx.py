@@ -166,3 +166,35 @@ def test_mx_gemm_equals_dequantized_matmul():
     np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
     # and it approximates the bf16 product within the MX tolerance
     assert O.max_abs_normalised_error(got, a @ b.T) < 6e-2
+
+
+def test_mx_fc2_rounds_y_to_bf16():
+    """The grouped MX FC2 stores Y in bf16: small-integer codes with unit scales
+    make the exact dot products 257 and 259 (9 significant bits), which bf16
+    (8 bits) rounds to 256 (a tie, to the even significand) and 260. Without
+    the storage rounding Y would hold 257 and 259. Also checks that expert e's
+    rows meet W2_e (a second expert whose weights are 2x the first's)."""
+    E, n, d = 2, 32, 2
+    M_cap = 2 * 128
+    counts = np.array([1, 1])
+    offsets = np.array([0, 128, 256])
+    a = np.zeros((M_cap, n))
+    a[0] = 8.0
+    a[0, 0] = 9.0                     # 9 + 31 * 8 = 257 against a column of ones
+    a[128] = 8.0
+    a[128, :3] = 9.0                  # 3 * 9 + 29 * 8 = 259
+    a_q = O.e4m3_encode(a)
+    a_s = np.full((M_cap, n // 32), 127, np.uint8)
+    w = np.zeros((E, d, n))           # W2_e stored transposed [d, n]
+    w[0, 0] = 1.0
+    w[0, 1] = 0.5
+    w[1, 0] = 2.0
+    w[1, 1] = 1.0
+    w_q = O.e4m3_encode(w)
+    w_s = np.full((E, d, n // 32), 127, np.uint8)
+    Y = O.mx_fc2(a_q, a_s, w_q, w_s, counts, offsets)
+    assert Y[0, 0] == 256.0 and Y[0, 1] == 128.0      # 257 -> 256, 128.5 -> 128
+    assert Y[128, 0] == 520.0 and Y[128, 1] == 260.0  # 518 -> 520, 259 -> 260
+    Yx = O.mx_fc2(a_q, a_s, w_q, w_s, counts, offsets, rounding=False)
+    assert Yx[0, 0] == 257.0 and Yx[128, 1] == 259.0
+    assert not Y[1:128].any() and not Y[129:].any()   # padding rows stay zero
