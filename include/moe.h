@@ -12,9 +12,12 @@
  *     element counts; every matrix is row-major and densely packed.
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
  *     The caller owns every buffer and keeps it alive until the stream work
- *     that uses it has completed. The library allocates nothing, keeps no
- *     pointer after a call returns and holds no mutable global state, so
- *     calls are reentrant and thread-safe.
+ *     that uses it has completed. The library allocates nothing and keeps no
+ *     pointer after a call returns. Its only mutable global state is two
+ *     per-device caches filled on first use (the compute-unit count, and the
+ *     device address of the static scratch of moe_route_counts_noalloc), so
+ *     calls are reentrant and thread-safe, except that moe_route_counts_noalloc
+ *     calls overlapping on one GPU share that scratch.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     legacy default stream). No call synchronises, allocates or copies
  *     device-to-host, so every call may be recorded into a hipGraph. Shapes
@@ -141,6 +144,31 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm,
                      int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                      int32_t* row_of, int32_t* src_of, int64_t M_cap, int32_t* err_word,
                      void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Bytes of the static device scratch behind moe_route_counts_noalloc (per GPU). */
+#define MOE_ROUTE_STATIC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * moe_route_counts_noalloc -- moe_route_counts with no workspace argument, for
+ *   callers that cannot allocate device memory: code under hipGraph capture
+ *   that may not call hipMalloc, tight serving loops, harnesses that forbid
+ *   allocation. Same arguments (minus the workspace), the same kernels and
+ *   bit-identical outputs. The layout scratch is a device array of
+ *   MOE_ROUTE_STATIC_SCRATCH_BYTES that the library reserves statically; each
+ *   GPU holds its own copy until the process ends, and its address is looked
+ *   up once per device on the first call with that device current. The call
+ *   allocates nothing (no hipMalloc/hipFree, no allocating library routine).
+ *   Returns MOE_ERR_WORKSPACE, before launching anything, when
+ *   moe_route_workspace_bytes(T, k, E) exceeds that size (8 bytes per expert
+ *   per 1024 routed pairs: e.g. T*k = 2^20 pairs with E = 1024 experts fit).
+ *   Every call on one GPU shares the array and leaves its contents behind
+ *   (nothing in it needs clearing between calls), so calls that overlap on a
+ *   GPU (concurrent streams or host threads) race: the caller serialises them.
+ */
+int moe_route_counts_noalloc(const float* logits, int T, int E, int k, int renorm,
+                             int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* row_of, int32_t* src_of, int64_t M_cap, int32_t* err_word,
+                             moe_stream_t stream);
 
 /*
  * moe_route_bwd -- router backward: gradient of the loss w.r.t. the router

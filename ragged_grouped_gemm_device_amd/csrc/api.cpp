@@ -73,6 +73,19 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm, int32
     return rc ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
+int moe_route_counts_noalloc(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                             int32_t* src_of, int64_t M_cap, int32_t* err_word, moe_stream_t stream) {
+    const int64_t cap = capacity(T, k, E);
+    if (cap < 0) return MOE_ERR_INVALID_ARG;
+    if (!logits || !topk_idx || !topk_w || !counts || !offsets || !row_of || !src_of) return MOE_ERR_INVALID_ARG;
+    if (M_cap < cap || M_cap > ((int64_t)1 << 31) - 1) return MOE_ERR_WORKSPACE;
+    if (moe::route_workspace_bytes(T, k, E) > moe::kRouteStaticScratch) return MOE_ERR_WORKSPACE;
+    const int rc = moe::launch_route_noalloc(logits, T, E, k, renorm, topk_idx, topk_w, counts, offsets, row_of,
+                                             src_of, M_cap, err_word, S(stream));
+    return rc == 0 ? MOE_OK : rc == -3 ? MOE_ERR_WORKSPACE : MOE_ERR_LAUNCH;
+}
+
 int moe_route_bwd(const float* logits, const int32_t* topk_idx, const float* ds, int T, int E, int k,
                   int renorm, float* dlogits, moe_stream_t stream) {
     if (T <= 0 || E <= 0 || k <= 0 || k > E || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;

@@ -18,6 +18,15 @@ int launch_route(const float* logits, int T, int E, int k, int renorm, int32_t* 
                  int32_t* src_of, int64_t M_cap, int32_t* err_word, void* ws, hipStream_t s);
 size_t route_workspace_bytes(int T, int k, int E);
 
+// Allocation-free routing: the layout scratch is a static device array of
+// kRouteStaticScratch bytes per GPU. Returns -3 when route_workspace_bytes
+// exceeds it (nothing launched), -4 on a failed symbol lookup or launch.
+constexpr size_t kRouteStaticScratch = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+int launch_route_noalloc(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                         int32_t* src_of, int64_t M_cap, int32_t* err_word, hipStream_t s);
+
 int launch_route_bwd(const float* logits, int T, int E, int k, int renorm, const int32_t* topk_idx,
                      const float* ds, float* dlogits, hipStream_t s);
 int launch_permute(const uint16_t* x, const int32_t* row_of, const int32_t* src_of,

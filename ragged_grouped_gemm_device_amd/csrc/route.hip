@@ -14,6 +14,8 @@
 //   counts live in GPU memory; Transformer Engine page, grouped-GEMM section:
 //   expert regions aligned to 128 tokens; dropless-boundary section: one slot
 //   per (token, expert) pair, regions padded to the alignment unit.]
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -414,6 +416,41 @@ size_t route_workspace_bytes(int T, int k, int E) {
     const int64_t P = (int64_t)T * k;
     const int64_t nchunks = (P + kChunkPairs - 1) / kChunkPairs;
     return (size_t)(2 * nchunks * E) * sizeof(int32_t);
+}
+
+// Scratch of the allocation-free routing entry point: the per-chunk
+// histograms and scan bases of the layout, in device memory the library
+// reserves statically (kRouteStaticScratch bytes per GPU, held until the
+// process ends). Nothing in it has to start at zero: the histogram kernel
+// writes every chunk's counts and the scan every base before they are read.
+// In host code `scratch` names a host-side stand-in; the kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kRouteStaticScratch];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+static void* route_scratch_ptr() {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+int launch_route_noalloc(const float* logits, int T, int E, int k, int renorm, int32_t* topk_idx,
+                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                         int32_t* src_of, int64_t M_cap, int32_t* err_word, hipStream_t s) {
+    if (route_workspace_bytes(T, k, E) > kRouteStaticScratch) return -3;
+    void* ws = route_scratch_ptr();
+    if (!ws) return -4;
+    return launch_route(logits, T, E, k, renorm, topk_idx, topk_w, counts, offsets, row_of, src_of, M_cap,
+                        err_word, ws, s);
 }
 
 }  // namespace moe

@@ -39,6 +39,7 @@ MOE_GATHER_ROWS = 0x100
 MOE_ERRBIT_NONFINITE_LOGIT = 0x1
 MOE_QUANT_ROWWISE = 0x1
 MOE_QUANT_COLWISE = 0x2
+MOE_ROUTE_STATIC_SCRATCH_BYTES = 8 << 20
 
 # (name, restype, argtypes) of every exported symbol
 _P = C.c_void_p
@@ -51,6 +52,7 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_mlp_bwd_workspace_bytes": (_SZ, [_I, _I64]),
     "moe_route_counts": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "moe_route_counts_noalloc": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P, _P]),
     "moe_route_bwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_permute": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _I, _I, _I, _P, _P]),
@@ -143,6 +145,16 @@ def moe_route_counts(logits, k, topk_idx, topk_w, counts, offsets, row_of, src_o
                                  _ptr(src_of), M_cap, _ptr(err_word), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream())
     _check("moe_route_counts", rc)
+
+
+def moe_route_counts_noalloc(logits, k, topk_idx, topk_w, counts, offsets, row_of, src_of, M_cap,
+                             err_word, renorm=False):
+    """moe_route_counts on the library's static scratch (no workspace argument)."""
+    T, E = logits.shape
+    rc = _lib().moe_route_counts_noalloc(_ptr(logits), T, E, k, int(bool(renorm)), _ptr(topk_idx),
+                                         _ptr(topk_w), _ptr(counts), _ptr(offsets), _ptr(row_of),
+                                         _ptr(src_of), M_cap, _ptr(err_word), _stream())
+    _check("moe_route_counts_noalloc", rc)
 
 
 def moe_route_bwd(logits, topk_idx, ds, dlogits, renorm=False):

@@ -44,6 +44,15 @@ def test_constants_match_header():
         assert int(m.group(1)) == getattr(M, name)
 
 
+def test_static_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+MOE_ROUTE_STATIC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.MOE_ROUTE_STATIC_SCRATCH_BYTES
+    launch = open(os.path.join(ROOT, "ragged_grouped_gemm_device_amd", "csrc", "launch.hpp")).read()
+    m = re.search(r"kRouteStaticScratch\s*=\s*\(size_t\)(\d+)\s*<<\s*(\d+)", launch)
+    assert m and int(m.group(1)) << int(m.group(2)) == M.MOE_ROUTE_STATIC_SCRATCH_BYTES
+
+
 def test_status_strings_and_capacity():
     assert M.moe_status_str(0) == "MOE_OK"
     assert M.moe_status_str(-3) == "MOE_ERR_WORKSPACE"
@@ -80,6 +89,17 @@ def test_host_validation_returns_before_launch():
     # misaligned workspace
     rc = lib.moe_route_counts(f, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, _fake(0x1004), 1 << 20, None)
     assert rc == M.MOE_ERR_INVALID_ARG
+    # allocation-free routing: host checks as above, and a layout whose scratch would
+    # exceed the static array (2^24 pairs x 1024 experts: 128 MiB) is refused
+    rc = lib.moe_route_counts_noalloc(None, 8, 4, 2, 0, f, f, f, f, f, f, 1024, None, None)
+    assert rc == M.MOE_ERR_INVALID_ARG
+    rc = lib.moe_route_counts_noalloc(f, 8, 4, 2, 0, f, f, f, f, f, f, 100, None, None)
+    assert rc == M.MOE_ERR_WORKSPACE
+    big_T, big_E = 1 << 21, 1024
+    assert M.moe_route_workspace_bytes(big_T, 8, big_E) > M.MOE_ROUTE_STATIC_SCRATCH_BYTES
+    rc = lib.moe_route_counts_noalloc(f, big_T, big_E, 8, 0, f, f, f, f, f, f,
+                                      M.moe_capacity_rows(big_T, 8, big_E), None, None)
+    assert rc == M.MOE_ERR_WORKSPACE
     # permute: d not a multiple of 8
     rc = lib.moe_permute(f, f, f, f, 8, 2, 4, 12, 1024, f, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
