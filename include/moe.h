@@ -62,6 +62,7 @@ extern "C" {
 #define MOE_MX_BLOCK 32        /* elements per MXFP8 scale block           */
 #define MOE_GLU_INTERLEAVE 32  /* gate/up interleave granularity (columns) */
 #define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_WIDTH (1 << 20) /* largest d and FC1 width (2n, or n for sReLU) */
 
 /* status codes */
 #define MOE_OK 0
@@ -233,6 +234,8 @@ typedef struct moe_mx_fwd {
     const uint8_t* x_s;    /* [M_cap, d/32] its scales (in)                      */
     const uint8_t* w1t_q;  /* [E, 2n, d]    W1_e quantized along d, transposed (in) */
     const uint8_t* w1t_s;  /* [E, 2n, d/32] its scales (in)                      */
+    uint8_t* y_q;          /* [M_cap, d]    row-wise codes of Y (out), or NULL    */
+    uint8_t* y_s;          /* [M_cap, d/32] its scales (out)                     */
 } moe_mx_fwd;
 
 /*
@@ -246,18 +249,24 @@ typedef struct moe_mx_fwd {
  *        the fp32 accumulators, f = silu (act = MOE_ACT_SWIGLU) or exact
  *        gelu (act = MOE_ACT_GEGLU) [P1, problem section: SwiGLU and GeGLU
  *        epilogues]; H is stored (bf16) when h != NULL.
- *   FC2: Y = bf16(A[R_e] W2_e); with mx != NULL the FC1 epilogue also writes
- *        the MXFP8 row-wise (and, if at_q != NULL, transposed) copy of the
- *        bf16 A [P1, core-idea section: MXFP8 and transposed output fused in
- *        the GEMM], and FC2 runs on MX-scaled MFMA from a_q/a_s and
- *        w2t_q/w2t_s instead of w2 [P3, three-components section: MXFP8
- *        grouped GEMM]. With mx->x_q != NULL FC1 also runs on MX-scaled MFMA,
- *        from x_q/x_s and w1t_q/w1t_s instead of x_perm and w1 (then
- *        d % 128 == 0 and no MOE_GATHER_ROWS).
+ *   FC2: Y = bf16(A[R_e] W2_e). With mx != NULL:
+ *        - a_q != NULL: the FC1 epilogue also writes the MXFP8 row-wise (and,
+ *          if at_q != NULL, transposed) copy of the bf16 A [P1, core-idea
+ *          section: MXFP8 and transposed output fused in the GEMM];
+ *        - w2t_q != NULL: FC2 runs on MX-scaled MFMA from a_q/a_s and
+ *          w2t_q/w2t_s instead of a and w2 [P3, three-components section:
+ *          MXFP8 grouped GEMM]; otherwise FC2 stays bf16 from a and w2;
+ *        - y_q != NULL: the FC2 epilogue also writes the row-wise MXFP8 copy
+ *          of the bf16 Y (blocks of 32 along d; the "GroupGemm + Quantize"
+ *          fused kernel [P3, next-steps section], for an FP8 combine or
+ *          all-to-all), and y may then be NULL;
+ *        - x_q != NULL: FC1 also runs on MX-scaled MFMA, from x_q/x_s and
+ *          w1t_q/w1t_s instead of x_perm and w1 (then a_q is required,
+ *          d % 128 == 0 and no MOE_GATHER_ROWS).
  *   x_perm [M_cap, d], w1 [E, d, 2n], w2 [E, n, d] (bf16, in);
  *   offsets [E+1] (in); h [M_cap, 2n] (out, nullable), a [M_cap, n] (out;
- *   nullable when mx != NULL, whose FC2 reads only A's MXFP8 copy),
- *   y [M_cap, d] (out; needed with MOE_STAGE_FC2).
+ *   nullable when A's MXFP8 copy is written and FC2 reads only that copy),
+ *   y [M_cap, d] (out; needed with MOE_STAGE_FC2 unless y_q is given).
  *   stages: MOE_STAGE_FC1 and/or MOE_STAGE_FC2 (FC2 alone reads a), plus
  *   optionally MOE_GATHER_ROWS: x_perm is then x [T, d] and FC1 reads its
  *   rows through src_of [M_cap] (T, k: the routing shape; both are ignored
@@ -266,9 +275,14 @@ typedef struct moe_mx_fwd {
  * w1 [E, d, n], A = bf16(relu(H)^2), h [M_cap, n]; no MXFP8 form (mx must be
  * NULL).
  * Requires d % 64 == 0, n % 64 == 0, act MOE_ACT_SWIGLU, MOE_ACT_GEGLU or MOE_ACT_SRELU,
- * M_cap % 128 == 0, M_cap * max(d, 2n) * 2 < 2^31 and d * 2n * 2 < 2^31
- * (operands are addressed with 32-bit byte offsets); 16-byte aligned
- * pointers. Otherwise MOE_ERR_UNSUPPORTED.
+ * M_cap % 128 == 0, M_cap < 2^31, d and the FC1 width (2n; n for sReLU) at
+ * most MOE_MAX_WIDTH; no limit on the size of any tensor (every GEMM tile
+ * and K slab is addressed from its own 64-bit base). With MOE_GATHER_ROWS
+ * the un-permuted x is addressed as a whole with 32-bit byte offsets:
+ * T * d * 2 < 2^31. With mx != NULL: n % 128 == 0 (the MX FC2 reads whole
+ * 128-byte K slabs of A's codes), and with mx->x_q also d % 128 == 0, so the
+ * MXFP8 form needs d, n multiples of 128 (a 2880-wide model is refused).
+ * 16-byte aligned pointers. Otherwise MOE_ERR_UNSUPPORTED.
  */
 int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
                         const int32_t* offsets, const int32_t* src_of, int T, int k, int E, int d,
@@ -295,6 +309,8 @@ typedef struct moe_mx_bwd {
     const uint8_t* dy_s;   /* [M_cap, d/32]                                     */
     const uint8_t* w2_q;   /* [E, n, d]       W2_e row-wise along d (DGRAD2 in) */
     const uint8_t* w2_s;   /* [E, n, d/32]                                      */
+    uint8_t* dx_q;         /* [M_cap, d]      row-wise codes of dX_perm (DGRAD1 out), or NULL */
+    uint8_t* dx_s;         /* [M_cap, d/32]                                     */
 } moe_mx_bwd;
 
 /*
@@ -330,7 +346,10 @@ typedef struct moe_mx_bwd {
  *   section: MXFP8 grouped GEMM]: DGRAD2 stays bf16 and its epilogue also
  *   writes the MXFP8 copies of the bf16 dH (row-wise, and column-wise
  *   transposed) and of A' (column-wise transposed); the other three GEMMs
- *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q, WGRAD2 from awt_q x
+ *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q (with dx_q != NULL its
+ *   epilogue also writes the row-wise MXFP8 copy of the bf16 dX_perm, the
+ *   "GroupGemm + Quantize" kernel [P3, next-steps section], and dx_perm may
+ *   then be NULL), WGRAD2 from awt_q x
  *   dyt_q, WGRAD1 from xt_q x dht_q (K = the expert's row region). Only the
  *   rows of expert regions are written in the transposed copies; dh and
  *   a_w may then be NULL (their bf16 stores are skipped; no stage reads
@@ -338,7 +357,9 @@ typedef struct moe_mx_bwd {
  *   dy_q != NULL DGRAD2 also runs on MX-scaled MFMA (dy_q x w2_q, then d %
  *   128 == 0 and no MOE_GATHER_ROWS), its dGLU epilogue taking that product
  *   as dA' and dS on the rewritten side as always.
- * Requires the shape constraints of moe_grouped_mlp_fwd.
+ * Requires the shape constraints of moe_grouped_mlp_fwd; with mx != NULL also
+ * M_cap < 2^23 (the MX wgrads address 256 rows of the transposed [rows,
+ * M_cap] copies with 32-bit byte offsets).
  */
 int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16_t* w2,
                         const uint16_t* h, const uint16_t* dy_u, const float* topk_w,

@@ -3,6 +3,8 @@
 // memory; every shape that depends on the routing stays on the device.
 #include <hip/hip_runtime.h>
 
+#include <stdint.h>
+
 #include "../../include/moe.h"
 #include "launch.hpp"
 
@@ -22,11 +24,10 @@ int check_mlp_shape(int E, int d, int n, int64_t M_cap, int act) {
     if (E <= 0 || E > MOE_MAX_EXPERTS || d <= 0 || n <= 0 || M_cap <= 0) return MOE_ERR_INVALID_ARG;
     if (act != MOE_ACT_SWIGLU && act != MOE_ACT_GEGLU && act != MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;
     if (d % 64 || n % 64 || M_cap % MOE_ALIGN) return MOE_ERR_UNSUPPORTED;
-    // the GEMMs address operands with 32-bit buffer offsets (bytes)
+    // row maps are int32; a GEMM tile's 32-bit buffer offsets span at most
+    // 256 rows of one operand (each K slab and tile gets its own 64-bit base)
     const int64_t n1 = act == MOE_ACT_SRELU ? n : 2 * n;
-    const int64_t widest = d > n1 ? d : n1;
-    if (M_cap * widest * 2 >= ((int64_t)1 << 31) || (int64_t)d * n1 * 2 >= ((int64_t)1 << 31))
-        return MOE_ERR_UNSUPPORTED;
+    if (M_cap > INT32_MAX || d > MOE_MAX_WIDTH || n1 > MOE_MAX_WIDTH) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -135,50 +136,66 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
                         uint16_t* y, const moe_mx_fwd* mx, moe_stream_t stream) {
     int rc = check_mlp_shape(E, d, n, M_cap, act);
     if (rc) return rc;
-    if (!offsets || (!a && !mx)) return MOE_ERR_INVALID_ARG;  // with mx, FC2 reads A's MXFP8 copy
+    if (!offsets) return MOE_ERR_INVALID_ARG;
     if ((stages & ~(unsigned)(MOE_STAGES_FWD | MOE_GATHER_ROWS)) || !(stages & MOE_STAGES_FWD))
         return MOE_ERR_INVALID_ARG;
     moe::GatherSpec gx;
     if ((rc = gather_spec(stages, src_of, T, k, E, d, gx))) return rc;
+    // with mx: FC1's epilogue writes A's MXFP8 copies when a_q is given (it must be
+    // when FC1 runs on MXFP8 operands); FC2 runs on MXFP8 operands (A's codes x W2's)
+    // when w2t_q is given, else in bf16 from a and w2; y_q asks FC2's epilogue for
+    // the row-wise MXFP8 copy of Y (GroupGemm + Quantize), and then y may be NULL
+    const bool fc2_mx = mx && mx->w2t_q;
+    const bool y_mx = mx && mx->y_q;
     if (mx) {
         if (act == MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;  // MXFP8 copies exist for the GLU forms
-        if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
-        if (!mx->a_q || !mx->a_s || !aligned16(mx->a_q) || !aligned16(mx->a_s)) return MOE_ERR_INVALID_ARG;
-        if ((mx->at_q == nullptr) != (mx->at_s == nullptr)) return MOE_ERR_INVALID_ARG;
-        if (mx->at_q && (!aligned16(mx->at_q) || !aligned16(mx->at_s))) return MOE_ERR_INVALID_ARG;
-        if ((stages & MOE_STAGE_FC2) &&
-            (!mx->w2t_q || !mx->w2t_s || !aligned16(mx->w2t_q) || !aligned16(mx->w2t_s)))
+        if ((mx->a_q == nullptr) != (mx->a_s == nullptr)) return MOE_ERR_INVALID_ARG;
+        if ((mx->at_q == nullptr) != (mx->at_s == nullptr) || (mx->at_q && !mx->a_q)) return MOE_ERR_INVALID_ARG;
+        if ((mx->y_q == nullptr) != (mx->y_s == nullptr)) return MOE_ERR_INVALID_ARG;
+        if ((mx->a_q && (!aligned16(mx->a_q) || !aligned16(mx->a_s))) ||
+            (mx->at_q && (!aligned16(mx->at_q) || !aligned16(mx->at_s))) || (mx->y_q && !aligned16(mx->y_q)))
             return MOE_ERR_INVALID_ARG;
+        if (fc2_mx && (stages & MOE_STAGE_FC2)) {
+            if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
+            if (!mx->a_q || !mx->w2t_s || !aligned16(mx->w2t_q) || !aligned16(mx->w2t_s))
+                return MOE_ERR_INVALID_ARG;
+        }
     }
+    // A is read by a bf16 FC2 and is the FC1 output unless only its MXFP8 copy is kept
+    if (!a && (!mx || !mx->a_q || ((stages & MOE_STAGE_FC2) && !fc2_mx))) return MOE_ERR_INVALID_ARG;
     const bool fc1_mx = mx && mx->x_q;  // FC1 on MXFP8 operands
     if (fc1_mx && (stages & MOE_STAGE_FC1)) {
         if (d % 128 || (stages & MOE_GATHER_ROWS)) return MOE_ERR_UNSUPPORTED;
         if (!mx->x_s || !mx->w1t_q || !mx->w1t_s || !aligned16(mx->x_q) || !aligned16(mx->w1t_q))
             return MOE_ERR_INVALID_ARG;
     }
+    if (fc1_mx && (stages & MOE_STAGE_FC1) && !mx->a_q) return MOE_ERR_INVALID_ARG;
     if ((stages & MOE_STAGE_FC1) && !fc1_mx) {
         if (!x_perm || !w1 || !aligned16(x_perm) || !aligned16(w1)) return MOE_ERR_INVALID_ARG;
     }
     if ((stages & MOE_STAGE_FC1) && h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
     if (a && !aligned16(a)) return MOE_ERR_INVALID_ARG;
     if (stages & MOE_STAGE_FC2) {
-        if (!y || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-        if (!mx && (!w2 || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
+        if ((!y && !y_mx) || (y && !aligned16(y))) return MOE_ERR_INVALID_ARG;
+        if (!fc2_mx && (!w2 || !aligned16(w2))) return MOE_ERR_INVALID_ARG;
     }
     hipStream_t s = S(stream);
     if (stages & MOE_STAGE_FC1) {
         const int rc1 = fc1_mx ? moe::launch_fc1_glu_mxin(mx->x_q, mx->x_s, mx->w1t_q, mx->w1t_s, offsets, E,
                                                           d, n, M_cap, act, h, a, mx->a_q, mx->a_s, mx->at_q,
                                                           mx->at_s, s)
-                        : mx ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a,
-                                                      mx->a_q, mx->a_s, mx->at_q, mx->at_s, s)
-                             : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, s);
+                        : (mx && mx->a_q)
+                            ? moe::launch_fc1_glu_mx(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, mx->a_q,
+                                                     mx->a_s, mx->at_q, mx->at_s, s)
+                            : moe::launch_fc1_glu(x_perm, w1, offsets, E, d, n, M_cap, act, gx, h, a, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }
     if (stages & MOE_STAGE_FC2) {
-        const int rc2 = mx ? moe::launch_mx_fc2(mx->a_q, mx->a_s, mx->w2t_q, mx->w2t_s, offsets, E, d, n,
-                                                 M_cap, y, s)
-                           : moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, s);
+        uint8_t* y_q = y_mx ? mx->y_q : nullptr;
+        uint8_t* y_s = y_mx ? mx->y_s : nullptr;
+        const int rc2 = fc2_mx ? moe::launch_mx_fc2(mx->a_q, mx->a_s, mx->w2t_q, mx->w2t_s, offsets, E, d, n,
+                                                     M_cap, y, y_q, y_s, s)
+                               : moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, y_q, y_s, s);
         if (rc2) return MOE_ERR_LAUNCH;
     }
     return MOE_OK;
@@ -223,7 +240,12 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if (!mx && (!a_w || !dy_u || !aligned16(a_w) || !aligned16(dy_u))) return MOE_ERR_INVALID_ARG;
     }
     if (stages & MOE_STAGE_DGRAD1) {
-        if (!dx_perm || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
+        // with mx->dx_q the FC1 dgrad also writes dX_perm's row-wise MXFP8 copy
+        // (GroupGemm + Quantize) and dx_perm may be NULL
+        const bool dx_mx = mx && mx->dx_q;
+        if ((!dx_perm && !dx_mx) || (dx_perm && !aligned16(dx_perm))) return MOE_ERR_INVALID_ARG;
+        if (mx && ((mx->dx_q == nullptr) != (mx->dx_s == nullptr) || (dx_mx && !aligned16(mx->dx_q))))
+            return MOE_ERR_INVALID_ARG;
         if (!mx && (!dh || !w1 || !aligned16(dh) || !aligned16(w1))) return MOE_ERR_INVALID_ARG;
     }
     if (stages & MOE_STAGE_WGRAD1) {
@@ -231,6 +253,8 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if (!mx && (!x_perm || !dh || !aligned16(x_perm) || !aligned16(dh))) return MOE_ERR_INVALID_ARG;
     }
     if (mx && act == MOE_ACT_SRELU) return MOE_ERR_UNSUPPORTED;
+    // MX wgrads: 256 rows of a transposed [rows, M_cap] copy per tile, 32-bit offsets
+    if (mx && M_cap >= ((int64_t)1 << 23)) return MOE_ERR_UNSUPPORTED;
     const int n1 = act == MOE_ACT_SRELU ? n : 2 * n;  // FC1 width
     if (mx) {
         auto ok = [](const void* p, const void* q) { return p && q && aligned16(p); };
@@ -267,7 +291,7 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     }
     if (stages & MOE_STAGE_DGRAD1) {
         const int rc1 = mx ? moe::launch_mx_ragged_m(mx->dh_q, mx->dh_s, mx->w1_q, mx->w1_s, offsets, E, d,
-                                                      2 * n, M_cap, dx_perm, s)
+                                                      2 * n, M_cap, dx_perm, mx->dx_q, mx->dx_s, s)
                            : moe::launch_dgrad1(dh, w1, offsets, E, d, n1, M_cap, dx_perm, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }

@@ -48,6 +48,7 @@ enum Epi {
     EPI_BF16 = 0, EPI_GLU = 1, EPI_DGLU = 2, EPI_F32 = 3, EPI_GLU_MX = 4, EPI_DGLU_MX = 5,
     EPI_ACT = 6,   // non-gated activation (sReLU): H and A = f(H), same columns
     EPI_DACT = 7,  // its backward: dH = w dA' f'(H), A' = w f(H), dS partials
+    EPI_BF16_MX = 8,  // bf16 C (optional) and its row-wise MXFP8 copy (GroupGemm + Quantize)
 };
 
 struct GemmArgs {
@@ -102,13 +103,14 @@ __device__ __forceinline__ int token_of(int src, int k, uint64_t magic) {
 __device__ __forceinline__ int kmaj_off(int r, int chunk) { return kmaj_byte(r, chunk) >> 1; }
 __device__ __forceinline__ int mnmaj_off(int k, int chunk) { return mnmaj_byte(k, chunk) >> 1; }
 
-// Where one operand slab comes from: base and readable size (the buffer
-// resource is rebuilt from them at each issue, a few scalar ops), the byte
-// step per K slab and per copy index, and this lane's offset for copy 0.
+// Where one operand slab comes from: base and readable size from it (the
+// buffer resource of slab ks is rebuilt at each issue from base + ks * step,
+// a few scalar ops), the byte step per K slab and per copy index, and this
+// lane's offset for copy 0 (relative to the slab's own base).
 struct SlabSrc {
     const uint16_t* a_base;
     const uint16_t* b_base;
-    uint32_t a_bytes, b_bytes;
+    int64_t a_bytes, b_bytes;
     uint32_t a_step, b_step;
     uint32_t a_istep, b_istep;
     uint32_t a_off, b_off;
@@ -120,31 +122,30 @@ struct SlabSrc {
 struct ScaleSrc {
     const uint8_t* as_base;
     const uint8_t* bs_base;
-    uint32_t as_bytes, bs_bytes;
+    int64_t as_bytes, bs_bytes;
 };
 
 // Enqueue the direct global -> LDS copies of K slab `ks` (A slab then B slab)
 // into the LDS stage at `lds`. Copy i of wavefront w fills LDS block i * 8 + w
-// (1 KiB); lane l writes chunk l of it. A masked lane's offset stays past the
-// buffer end: the API bounds keep every operand region under 2^31 bytes, so
-// the sums cannot wrap.
+// (1 KiB); lane l writes chunk l of it. The resource of slab ks starts at the
+// slab (base + ks * step, in 64 bits), so lane offsets span one slab's rows:
+// below 2^31 for any operand size. A masked lane's offset (kMasked plus less
+// than a slab) stays past the resource's end without wrapping.
 template <int GATHER>
 // part: 0 = the A slab's copies only, 1 = the B slab's only, 2 = both.
 __device__ __forceinline__ void issue_slab(const SlabSrc& sr, int ks, LDS_AS char* lds, int wave, int part = 2) {
-    const uint32_t da = (uint32_t)ks * sr.a_step, db = (uint32_t)ks * sr.b_step;
-    const i32x4_t ra = rsrc_words(sr.a_base, sr.a_bytes);
-    const i32x4_t rb = rsrc_words(sr.b_base, sr.b_bytes);
+    const i32x4_t ra = rsrc_from(sr.a_base, sr.a_bytes, (int64_t)ks * sr.a_step);
+    const i32x4_t rb = rsrc_from(sr.b_base, sr.b_bytes, (int64_t)ks * sr.b_step);
     const uint32_t l0 = (uint32_t)(uintptr_t)lds + wave * 1024;
     if (part != 1) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        lds_copy16(ra, l0 + i * kWaves * 1024, GATHER == 1 ? sr.g_off[i] + da : sr.a_off + (da + i * sr.a_istep));
+        lds_copy16(ra, l0 + i * kWaves * 1024, GATHER == 1 ? sr.g_off[i] : sr.a_off + i * sr.a_istep);
     }
     if (part != 0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-        lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024,
-                   GATHER == 2 ? sr.g_off[i] + db : sr.b_off + (db + i * sr.b_istep));
+        lds_copy16(rb, l0 + BM * BK * 2 + i * kWaves * 1024, GATHER == 2 ? sr.g_off[i] : sr.b_off + i * sr.b_istep);
     }
 }
 
@@ -241,39 +242,40 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     auto make_src = [&](const Tile& tl) -> SlabSrc {
         SlabSrc sr;
         const uint16_t*& a_base = sr.a_base;
-        uint32_t& a_bytes = sr.a_bytes;
+        int64_t& a_bytes = sr.a_bytes;
         if constexpr (!RAGGED_K) {
+            // a ragged-M tile reads at most BM rows of its expert
             a_base = p.A + (int64_t)tl.row0 * p.lda;
-            a_bytes = (uint32_t)((int64_t)(tl.row_end - tl.row0) * p.lda * 2);
+            a_bytes = (int64_t)min(tl.row_end - tl.row0, BM) * p.lda * 2;
             sr.a_step = BK * 2;
         } else {
             a_base = p.A + (int64_t)tl.k_begin * p.lda;
-            a_bytes = (uint32_t)((int64_t)(tl.k_end - tl.k_begin) * p.lda * 2);
+            a_bytes = (int64_t)(tl.k_end - tl.k_begin) * p.lda * 2;
             sr.a_step = (uint32_t)(BK * p.lda * 2);
         }
         const uint16_t*& b_base = sr.b_base;
-        uint32_t& b_bytes = sr.b_bytes;
+        int64_t& b_bytes = sr.b_bytes;
         if constexpr (RAGGED_K) {
             b_base = p.B + (int64_t)tl.k_begin * p.ldb;
-            b_bytes = (uint32_t)((int64_t)(tl.k_end - tl.k_begin) * p.ldb * 2);
+            b_bytes = (int64_t)(tl.k_end - tl.k_begin) * p.ldb * 2;
             sr.b_step = (uint32_t)(BK * p.ldb * 2);
         } else if constexpr (B_KMAJ) {
             b_base = p.B + (int64_t)tl.e * p.b_estride + (int64_t)tl.n0 * p.ldb;
-            b_bytes = (uint32_t)((int64_t)(p.N - tl.n0) * p.ldb * 2);
+            b_bytes = (int64_t)min(p.N - tl.n0, BN) * p.ldb * 2;
             sr.b_step = BK * 2;
         } else {
             b_base = p.B + (int64_t)tl.e * p.b_estride;
-            b_bytes = (uint32_t)((int64_t)p.K * p.ldb * 2);
+            b_bytes = (int64_t)p.K * p.ldb * 2;
             sr.b_step = (uint32_t)(BK * p.ldb * 2);
         }
         if constexpr (GATHER == 1) {  // A rows from the un-permuted tensor
             a_base = p.A;
-            a_bytes = (uint32_t)(p.g_rows * p.lda * 2);
+            a_bytes = p.g_rows * p.lda * 2;
             sr.a_step = RAGGED_K ? 0u : (uint32_t)(BK * 2);  // ragged K: offsets are per slab
         }
         if constexpr (GATHER == 2) {
             b_base = p.B;
-            b_bytes = (uint32_t)(p.g_rows * p.ldb * 2);
+            b_bytes = p.g_rows * p.ldb * 2;
             sr.b_step = RAGGED_K ? 0u : (uint32_t)(BK * 2);
         }
         sr.g_col0 = GATHER == 2 ? tl.n0 : tl.m0;
@@ -403,16 +405,16 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     auto make_scales = [&](const Tile& tl) -> ScaleSrc {
         ScaleSrc sc;
         sc.as_base = p.as + (int64_t)tl.row0 * p.kb;
-        sc.as_bytes = (uint32_t)((int64_t)(tl.row_end - tl.row0) * p.kb);
+        sc.as_bytes = (int64_t)min(tl.row_end - tl.row0, BM) * p.kb;
         sc.bs_base = p.bs + ((int64_t)tl.e * p.N + tl.n0) * p.kb;
-        sc.bs_bytes = (uint32_t)((int64_t)(p.N - tl.n0) * p.kb);
+        sc.bs_bytes = (int64_t)min(p.N - tl.n0, BN) * p.kb;
         return sc;
     };
     auto issue_scales = [&](const ScaleSrc& sr, int g, int sbuf) {
         if constexpr (MX) {
             const bool a_side = wave < kWaves / 2;
             const int row = (wave % (kWaves / 2)) * 64 + lane;
-            const i32x4_t r = a_side ? rsrc_words(sr.as_base, sr.as_bytes) : rsrc_words(sr.bs_base, sr.bs_bytes);
+            const i32x4_t r = a_side ? rsrc_from(sr.as_base, sr.as_bytes, 0) : rsrc_from(sr.bs_base, sr.bs_bytes, 0);
             const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS char*)(&s_sc[sbuf][0]) + wave * 1024;
             lds_copy16(r, l, (uint32_t)(row * p.kb + g * 16));
         }
@@ -653,7 +655,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // the memory requests for the same bytes. The 16-byte chunks of a staged
     // row are XOR-swizzled by the row so both sides stay free of LDS bank
     // conflicts.
-    if constexpr (EPI == EPI_F32 || EPI == EPI_BF16) {
+    if constexpr (EPI == EPI_F32 || EPI == EPI_BF16 || EPI == EPI_BF16_MX) {
         __syncthreads();  // the last slab and the previous tile's staging are read out
         uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
         const int r = lane & 31;
@@ -680,22 +682,42 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 });
             } else {
                 // row r: 64 bf16 = 8 chunks, half h of chunk 4J + Q from this lane
+                uint32_t pk[TNW][8];  // EPI_BF16_MX: the lane's bf16 pairs of each 32-column block
                 static_for<TNW>([&](auto J) {
                     static_for<4>([&](auto Q) {
                         const int ch = 4 * J + Q;
                         uint2 v;
                         v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
                         v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                        if constexpr (EPI == EPI_BF16_MX) {
+                            pk[J][2 * Q] = v.x;
+                            pk[J][2 * Q + 1] = v.y;
+                        }
                         *(uint2*)(stg + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h) = v;
                     });
                 });
+                if constexpr (EPI == EPI_BF16_MX) {
+                    // the row-wise MXFP8 copy of the bf16-rounded output (blocks of 32
+                    // columns: lanes l and l ^ 32 share a row, so both take the branch)
+                    const int m = rband + 32 * I + r;
+                    if (m < row_end) {
+                        static_for<TNW>([&](auto J) {
+                            const int cb = col0 + 32 * J;
+                            if (cb < p.N)
+                                mx_rowq32(pk[J], lane, p.q_row + (int64_t)m * p.N + cb,
+                                          p.s_row + (int64_t)m * (p.N / 32) + cb / 32);
+                        });
+                    }
+                }
                 wave_lds_sync();
-                static_for<4>([&](auto It) {
-                    const int R = 8 * It + (lane >> 3), c = lane & 7;
-                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
-                    const int m = rband + 32 * I + R, col = col0 + 8 * c;
-                    if (m < row_end && col < p.N) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + col) = v;
-                });
+                if (EPI == EPI_BF16 || p.out0) {  // the bf16 output is optional beside its MXFP8 copy
+                    static_for<4>([&](auto It) {
+                        const int R = 8 * It + (lane >> 3), c = lane & 7;
+                        const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                        const int m = rband + 32 * I + R, col = col0 + 8 * c;
+                        if (m < row_end && col < p.N) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + col) = v;
+                    });
+                }
             }
             wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
@@ -1208,12 +1230,14 @@ int launch_fc1_glu_mxin(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w
 }
 
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
-               int64_t M_cap, uint16_t* y, hipStream_t s) {
+               int64_t M_cap, uint16_t* y, uint8_t* y_q, uint8_t* y_s, hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = a; g.lda = n;
     g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;
     g.offsets = offsets; g.E = E; g.N = d; g.K = n;
     g.out0 = y; g.ld0 = d;
+    g.q_row = y_q; g.s_row = y_s;
+    if (y_q) return run<false, true, false, EPI_BF16_MX>(g, ragged_m_grid(M_cap, E, d), s);
     return run<false, true, false, EPI_BF16>(g, ragged_m_grid(M_cap, E, d), s);
 }
 

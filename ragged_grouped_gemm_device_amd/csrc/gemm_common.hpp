@@ -58,6 +58,19 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) 
     return r;
 }
 
+// Readable bytes of a buffer resource from a 64-bit extent: at most 2^31 - 1
+// (every lane offset the kernels form stays below 2^31), none if empty.
+__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
+    return bytes <= 0 ? 0u : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFFu : (uint32_t)bytes);
+}
+
+// Resource over bytes [skip, total) of an operand that starts at base: every
+// K slab gets its own 64-bit base, so the 32-bit lane offsets only span one
+// slab (or one tile's rows) and no operand size limits the GEMMs.
+__device__ __forceinline__ i32x4_t rsrc_from(const void* base, int64_t total, int64_t skip) {
+    return rsrc_words((const char*)base + skip, clamp_records(total - skip));
+}
+
 __device__ __forceinline__ void lds_copy16(i32x4_t rsrc, uint32_t lds, uint32_t voff) {
     // resource and LDS address are wave-uniform; readfirstlane pins them to
     // scalar registers when the compiler cannot prove it (free otherwise)

@@ -211,8 +211,10 @@ struct MxArgs {
     const int32_t* offsets;
     int E, M, N, K;      // ragged K: M unused by ragged M; K unused by ragged K
     int64_t ld;          // ragged K: bytes per code row (M_cap)
-    uint16_t* out;       // ragged M: [M_cap, N] bf16
+    uint16_t* out;       // ragged M: [M_cap, N] bf16 (nullable when q_row is given)
     float* outf;         // ragged K: [E, M, N] fp32
+    uint8_t* q_row;      // ragged M, nullable: row-wise MXFP8 copy of out, codes [M_cap, N]
+    uint8_t* s_row;      //   and scales [M_cap, N/32]
 };
 
 constexpr int MBK = 128;  // K bytes per LDS slab
@@ -285,6 +287,8 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
     };
     // operand regions of a tile: codes and scales; rows past the region (ragged
     // M) or past M and N read as 0
+    // (a tile reads at most BM rows of A and BN rows of B; byte counts are
+    // formed in 64 bits and clamped to what a buffer resource holds)
     struct MxSrc {
         const uint8_t *a, *b, *as, *bs;
         uint32_t a_bytes, b_bytes, as_bytes, bs_bytes;
@@ -293,23 +297,23 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
         MxSrc s;
         if constexpr (!RAGGED_K) {
             s.a = p.A + (int64_t)t.row0 * p.K;
-            s.a_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * p.K);
+            s.a_bytes = clamp_records((int64_t)min(t.row_end - t.row0, BM) * p.K);
             s.b = p.B + ((int64_t)t.e * p.N + t.n0) * p.K;
-            s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * p.K);
+            s.b_bytes = clamp_records((int64_t)min(p.N - t.n0, BN) * p.K);
             s.as = p.As + (int64_t)t.row0 * KB;
-            s.as_bytes = (uint32_t)((int64_t)(t.row_end - t.row0) * KB);
+            s.as_bytes = clamp_records((int64_t)min(t.row_end - t.row0, BM) * KB);
             s.bs = p.Bs + ((int64_t)t.e * p.N + t.n0) * KB;
-            s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB);
+            s.bs_bytes = clamp_records((int64_t)min(p.N - t.n0, BN) * KB);
         } else {
             const int kb = t.k_begin / 32;
             s.a = p.A + (int64_t)t.m0 * rowb + t.k_begin;
-            s.a_bytes = (uint32_t)((int64_t)(p.M - t.m0) * rowb - t.k_begin);
+            s.a_bytes = clamp_records((int64_t)min(p.M - t.m0, BM) * rowb - t.k_begin);
             s.b = p.B + (int64_t)t.n0 * rowb + t.k_begin;
-            s.b_bytes = (uint32_t)((int64_t)(p.N - t.n0) * rowb - t.k_begin);
+            s.b_bytes = clamp_records((int64_t)min(p.N - t.n0, BN) * rowb - t.k_begin);
             s.as = p.As + (int64_t)t.m0 * KB + kb;
-            s.as_bytes = (uint32_t)((int64_t)(p.M - t.m0) * KB - kb);
+            s.as_bytes = clamp_records((int64_t)min(p.M - t.m0, BM) * KB - kb);
             s.bs = p.Bs + (int64_t)t.n0 * KB + kb;
-            s.bs_bytes = (uint32_t)((int64_t)(p.N - t.n0) * KB - kb);
+            s.bs_bytes = clamp_records((int64_t)min(p.N - t.n0, BN) * KB - kb);
         }
         return s;
     };
@@ -479,21 +483,37 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
         const int col0 = tl.n0 + wn * WN;
         static_for<4>([&](auto I) {
             if constexpr (!RAGGED_K) {
+                uint32_t pk[TNW][8];  // the lane's bf16 pairs of each 32-column block
                 static_for<TNW>([&](auto J) {
                     static_for<4>([&](auto Q) {
                         uint2 v;
                         v.x = pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]);
                         v.y = pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]);
+                        pk[J][2 * Q] = v.x;
+                        pk[J][2 * Q + 1] = v.y;
                         *(uint2*)(stg + r * 128 + (((4 * J + Q) ^ ((r >> 1) & 7)) << 4) + 8 * h) = v;
                     });
                 });
+                // GroupGemm + Quantize: the row-wise MXFP8 copy of the bf16 output
+                // (lanes l and l ^ 32 share a row, so both take the branch)
+                const int mq = tl.row0 + wm * 128 + 32 * I + r;
+                if (p.q_row && mq < tl.row_end) {
+                    static_for<TNW>([&](auto J) {
+                        const int cb = col0 + 32 * J;
+                        if (cb < p.N)
+                            mx_rowq32(pk[J], lane, p.q_row + (int64_t)mq * p.N + cb,
+                                      p.s_row + (int64_t)mq * (p.N / 32) + cb / 32);
+                    });
+                }
                 wave_lds_sync();
-                static_for<4>([&](auto It) {
-                    const int R = 8 * It + (lane >> 3), c = lane & 7;
-                    const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
-                    const int m = tl.row0 + wm * 128 + 32 * I + R, col = col0 + 8 * c;
-                    if (m < tl.row_end && col < p.N) *(uint4*)(p.out + (int64_t)m * p.N + col) = v;
-                });
+                if (p.out) {
+                    static_for<4>([&](auto It) {
+                        const int R = 8 * It + (lane >> 3), c = lane & 7;
+                        const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                        const int m = tl.row0 + wm * 128 + 32 * I + R, col = col0 + 8 * c;
+                        if (m < tl.row_end && col < p.N) *(uint4*)(p.out + (int64_t)m * p.N + col) = v;
+                    });
+                }
             } else {
                 static_for<TNW>([&](auto J) {
                     static_for<4>([&](auto Q) {
@@ -525,18 +545,19 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
 
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
                   const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
-                  hipStream_t s) {
-    return launch_mx_ragged_m(a_q, a_s, w2t_q, w2t_s, offsets, E, d, n, M_cap, y, s);
+                  uint8_t* y_q, uint8_t* y_s, hipStream_t s) {
+    return launch_mx_ragged_m(a_q, a_s, w2t_q, w2t_s, offsets, E, d, n, M_cap, y, y_q, y_s, s);
 }
 
 int launch_mx_ragged_m(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                        const int32_t* offsets, int E, int N, int K, int64_t M_cap, uint16_t* out,
-                       hipStream_t s) {
+                       uint8_t* q_row, uint8_t* s_row, hipStream_t s) {
     MxArgs a;
     __builtin_memset(&a, 0, sizeof(a));
     a.A = a_q; a.As = a_s; a.B = b_q; a.Bs = b_s;
     a.offsets = offsets; a.E = E; a.N = N; a.K = K; a.ld = K;
     a.out = out;
+    a.q_row = q_row; a.s_row = s_row;
     const int64_t tb = ragged_m_grid(M_cap, E, N);
     if (tb <= 0) return 0;
     mx_gemm_kernel<false><<<persistent_grid(tb), kThreads, 0, s>>>(a);

@@ -210,6 +210,28 @@ __device__ __forceinline__ void mx_stage_flush(const uint8_t* stage, int lane, u
     }
 }
 
+// Row-wise MXFP8 block of one row of a 32 x 32 block held the MFMA way: this
+// lane has 16 of the row's 32 bf16 values (pk[j / 2], 16-bit slot j: column
+// 8 (j / 4) + 4 h + j % 4, h = lane / 32), the lane l ^ 32 the other 16. The
+// block maximum is one lane exchange away; the codes go to q (the row's first
+// column of the block) as four 4-byte words per lane, the E8M0 scale to *sc
+// (the same byte from both lanes).
+__device__ __forceinline__ void mx_rowq32(const uint32_t pk[8], int lane, uint8_t* q, uint8_t* sc) {
+    uint32_t am = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) am = max_u16x2(am, pk[r] & 0x7fff7fffu);
+    uint32_t amax = max(am & 0xffffu, am >> 16);
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+    const int e = mx_block_exp(amax);
+    const float inv = mx_inv_scale(e);
+    const int h = (lane >> 5) & 1;
+#pragma unroll
+    for (int Q = 0; Q < 4; ++Q)
+        *(uint32_t*)(q + 8 * Q + 4 * h) = e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv,
+                                                 bf16_lo(pk[2 * Q + 1]) * inv, bf16_hi(pk[2 * Q + 1]) * inv);
+    *sc = (uint8_t)(e + 127);
+}
+
 // Order this wavefront's LDS writes before its later reads of other lanes' data.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

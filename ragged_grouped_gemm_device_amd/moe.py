@@ -71,9 +71,10 @@ class MoEError(RuntimeError):
         self.status = status
 
 
-MX_FWD_FIELDS = ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s", "x_q", "x_s", "w1t_q", "w1t_s")
+MX_FWD_FIELDS = ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s", "x_q", "x_s", "w1t_q", "w1t_s",
+                 "y_q", "y_s")
 MX_BWD_FIELDS = ("dh_q", "dh_s", "dht_q", "dht_s", "awt_q", "awt_s", "dyt_q", "dyt_s", "xt_q", "xt_s",
-                 "w1_q", "w1_s", "dy_q", "dy_s", "w2_q", "w2_s")
+                 "w1_q", "w1_s", "dy_q", "dy_s", "w2_q", "w2_s", "dx_q", "dx_s")
 
 
 class moe_mx_fwd(C.Structure):
@@ -298,6 +299,12 @@ class Buffers:
             self.dy_s = torch.empty(M, d // 32, dtype=u8, device=dev)
             self.w2_q = torch.empty(E, n, d, dtype=u8, device=dev)
             self.w2_s = torch.empty(E, n, d // 32, dtype=u8, device=dev)
+            # row-wise MXFP8 copies of the FC2 output and of the FC1 dgrad output
+            # (GroupGemm + Quantize), written only when asked
+            self.y_q = torch.empty(M, d, dtype=u8, device=dev)
+            self.y_s = torch.empty(M, d // 32, dtype=u8, device=dev)
+            self.dx_q = torch.empty(M, d, dtype=u8, device=dev)
+            self.dx_s = torch.empty(M, d // 32, dtype=u8, device=dev)
         self.xt_from_forward = False
 
     def quantize_weights(self, w1, w2):
@@ -309,19 +316,24 @@ class Buffers:
         moe_quant_mxfp8(w2, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, self.w2_q, self.w2_s, self.w2t_q,
                         self.w2t_s)
 
-    def mx_fwd(self, fc1=True, transposed_a=False):
+    def mx_fwd(self, fc1=True, transposed_a=False, quant_y=False):
         """The moe_mx_fwd fields: FC1 on MXFP8 operands when fc1; the transposed copy of A
         only when asked (the training step's FC2 wgrad reads A' = w A, quantized by the FC2
-        dgrad, not A)."""
-        keys = MX_FWD_FIELDS if fc1 else MX_FWD_FIELDS[:6]
+        dgrad, not A); the row-wise MXFP8 copy of Y (FC2 epilogue) when quant_y."""
+        keys = MX_FWD_FIELDS[:10] if fc1 else MX_FWD_FIELDS[:6]
         d = {key: getattr(self, key) for key in keys}
         if not transposed_a:
             d["at_q"] = d["at_s"] = None
+        if quant_y:
+            d["y_q"], d["y_s"] = self.y_q, self.y_s
         return d
 
-    def mx_bwd(self, dgrad2=True):
-        keys = MX_BWD_FIELDS if dgrad2 else MX_BWD_FIELDS[:12]
-        return {key: getattr(self, key) for key in keys}
+    def mx_bwd(self, dgrad2=True, quant_dx=False):
+        keys = MX_BWD_FIELDS[:16] if dgrad2 else MX_BWD_FIELDS[:12]
+        d = {key: getattr(self, key) for key in keys}
+        if quant_dx:
+            d["dx_q"], d["dx_s"] = self.dx_q, self.dx_s
+        return d
 
 
 def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES_FWD, store_h=True,

@@ -21,6 +21,7 @@ Workload shapes follow the pages' descriptions:
     receive no tokens (the empty groups of the Transformer Engine page,
     section on the three components).
   * "train": a GPT-OSS-like training step (32 experts, top-4, d=n=2880).
+  * "skewed-large": the skewed recipe at T=32768 (permuted tensors of 3.8 GB).
   * "mxfp8": the balanced shape with 1 % of activations scaled by 50.
 """
 from __future__ import annotations
@@ -55,6 +56,10 @@ WORKLOADS = {
                          routing="balanced", w_std=0.01),
     "skewed": Workload("skewed", T=16384, k=8, E=32, d=7168, n=2048, seed=1003, routing="zipf"),
     "train": Workload("train", T=8192, k=4, E=32, d=2880, n=2880, seed=1004, routing="normal"),
+    # the skewed shape at twice the tokens: every permuted [M_cap, d] tensor is 3.8 GB,
+    # past what 32-bit byte offsets address from one base
+    "skewed-large": Workload("skewed-large", T=32768, k=8, E=32, d=7168, n=2048, seed=1006,
+                             routing="zipf"),
     "mxfp8": Workload("mxfp8", T=32768, k=1, E=8, d=8192, n=2048, seed=1005, routing="balanced",
                       w_std=0.01, outlier_p=0.01, outlier_scale=50.0),
 }

@@ -111,8 +111,8 @@ def _sample_tokens(wl, idx, counts, rng, n=12):
 
 
 @pytest.mark.parametrize("name,gather", [("balanced", False), ("skewed", False), ("train", False),
-                                         ("skewed", True)],
-                         ids=["balanced", "skewed", "train", "skewed-gather"])
+                                         ("skewed", True), ("skewed-large", False)],
+                         ids=["balanced", "skewed", "train", "skewed-gather", "skewed-large"])
 def test_fullsize_forward_backward(M, name, gather):
     wl = W.WORKLOADS[name]
     print(f"full-size case {wl} gather={gather}", flush=True)
@@ -128,8 +128,10 @@ def test_fullsize_forward_backward(M, name, gather):
     assert np.array_equal(buf.row_of.cpu().numpy(), row_of)
     assert np.array_equal(buf.src_of.cpu().numpy(), src_of)
     assert int(buf.err.item()) == 0
-    if name == "skewed":
+    if name.startswith("skewed"):
         assert (counts == 0).sum() >= 3
+    if name == "skewed-large":   # permuted tensors past 2^31 bytes
+        assert buf.M_cap * wl.d * 2 >= 2 ** 31
     # per-token results on a sample
     rng = np.random.default_rng(wl.seed)
     ts = _sample_tokens(wl, idx, counts, rng)

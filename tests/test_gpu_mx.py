@@ -336,3 +336,48 @@ def test_permute_quant_bit_exact(M, wl):
         for i in sel:
             assert np.array_equal(part[i].cpu().numpy(), ref[i]), (mode, i)
 
+
+
+GQ_CASES = [MX_CASES[0], MX_CASES[1], FC1_MX_CASES[1]]
+
+
+@pytest.mark.parametrize("wl", GQ_CASES, ids=[c.name for c in GQ_CASES])
+def test_groupgemm_quantize_fc2(M, wl):
+    """GroupGemm + Quantize: the FC2 epilogue's row-wise MXFP8 copy of Y equals, bit for
+    bit, the oracle's quantization of the GPU's own bf16 Y, on the bf16 FC2 (plain FC1,
+    mx given only for y_q) and on the MXFP8 FC2; the bf16 Y beside it is unchanged, and
+    with y = NULL the copy alone is written (the same bytes)."""
+    print(f"groupgemm+quantize case {wl}", flush=True)
+    inp = W.make_inputs(wl)
+    x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
+    logits = f32_tensor(inp["logits"])
+    buf = _mx_buffers(M, wl)
+    M.moe_route_counts(logits, wl.k, buf.topk_idx, buf.topk_w, buf.counts, buf.offsets, buf.row_of,
+                       buf.src_of, buf.M_cap, buf.err, buf.route_ws)
+    M.moe_permute(x, buf.row_of, buf.src_of, buf.offsets, wl.k, wl.E, buf.x_perm)
+    M.moe_quant_mxfp8(w2, M.MOE_QUANT_COLWISE, None, None, buf.w2t_q, buf.w2t_s)
+    end = int(buf.offsets[-1].item())
+    for fc2_mx in (False, True):
+        # reference: the same FC2 without the quantized copy
+        mx0 = dict(a_q=buf.a_q, a_s=buf.a_s, w2t_q=buf.w2t_q, w2t_s=buf.w2t_s) if fc2_mx else None
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD,
+                              mx=mx0)
+        y_ref = buf.y.clone()
+        for t in (buf.y_q, buf.y_s):
+            t.fill_(0xAB)
+        buf.y.fill_(float("nan"))
+        mx1 = dict(mx0 or {}, y_q=buf.y_q, y_s=buf.y_s)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD,
+                              mx=mx1)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.y[:end], y_ref[:end]), "bf16 Y changed"
+        check_fused_copies_vs_oracle(buf.y, end, buf.y_q, buf.y_s, None, None, "Y")
+        q_ref, s_ref = buf.y_q[:end].clone(), buf.y_s[:end].clone()
+        # quantized copy only (no bf16 Y)
+        buf.y_q.fill_(0xAB)
+        M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, None, M.MOE_STAGE_FC2, mx=mx1)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.y_q[:end], q_ref) and torch.equal(buf.y_s[:end], s_ref)
+        # rows past the last region are never written
+        if end < buf.M_cap:
+            assert torch.all(buf.y_q[end:] == 0xAB)
