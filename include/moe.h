@@ -160,8 +160,8 @@ int moe_route_counts(const float* logits, int T, int E, int k, int renorm,
  *   up once per device on the first call with that device current. The call
  *   allocates nothing (no hipMalloc/hipFree, no allocating library routine).
  *   Returns MOE_ERR_WORKSPACE, before launching anything, when
- *   moe_route_workspace_bytes(T, k, E) exceeds that size (8 bytes per expert
- *   per 1024 routed pairs: e.g. T*k = 2^20 pairs with E = 1024 experts fit).
+ *   moe_route_workspace_bytes(T, k, E) exceeds that size (at most 8 bytes per
+ *   expert per 1024 routed pairs: e.g. T*k = 2^20 pairs with E = 1024 experts fit).
  *   Every call on one GPU shares the array and leaves its contents behind
  *   (nothing in it needs clearing between calls), so calls that overlap on a
  *   GPU (concurrent streams or host threads) race: the caller serialises them.

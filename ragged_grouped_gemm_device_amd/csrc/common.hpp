@@ -86,6 +86,13 @@ __device__ __forceinline__ void unpack_bf16x4(uint2 v, float* f) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Order this wavefront's LDS writes before its later reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Butterfly sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

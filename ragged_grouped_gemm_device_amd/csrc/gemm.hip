@@ -645,7 +645,6 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
     // column 8q + 4h + s with h = l >> 5.
     const int h = lane >> 5;
     const int rbase = (RAGGED_K ? m0 : row0) + wm * 128 + (lane & 31);
-    const int cbase = n0 + wn * WN + 4 * h;
 
     // EPI_F32 and EPI_BF16 store through this wavefront's 8 KiB of the LDS
     // stage the tile no longer reads (the next tile's first slab goes to the

@@ -232,11 +232,4 @@ __device__ __forceinline__ void mx_rowq32(const uint32_t pk[8], int lane, uint8_
     *sc = (uint8_t)(e + 127);
 }
 
-// Order this wavefront's LDS writes before its later reads of other lanes' data.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 }  // namespace moe

@@ -64,6 +64,14 @@ def test_status_strings_and_capacity():
     assert M.moe_capacity_rows(10, 3, 2) == -1          # k > E
     assert M.moe_capacity_rows(10, 1, 2000) == -1       # E > MOE_MAX_EXPERTS
     assert M.moe_route_workspace_bytes(0, 1, 1) == 0
+    # the layout's scratch: one histogram row of E counters per chunk on the
+    # fused path (1024 threads route 1024 / G tokens per pass), two per 1024-pair
+    # chunk on the general path
+    assert M.moe_route_workspace_bytes(32768, 1, 8) == 256 * 8 * 4       # 128 tokens per chunk
+    assert M.moe_route_workspace_bytes(16384, 8, 32) == 512 * 32 * 4     # 32 tokens per chunk
+    assert M.moe_route_workspace_bytes(32700, 8, 32) == 511 * 32 * 4     # 2 passes of 32 tokens
+    assert M.moe_route_workspace_bytes(20000, 4, 128) == 2 * 79 * 128 * 4
+    assert M.moe_route_workspace_bytes(9000, 4, 1024) == 2 * 36 * 1024 * 4
     assert M.moe_mlp_bwd_workspace_bytes(2048, 1024) == 1024 * 32 * 4
 
 

@@ -56,6 +56,16 @@ ROUTE_CASES = [
     (5000, 24, 4, "normal"),
     (300, 64, 12, "normal"),     # k > 8: the renormalised weights of slots 8.. are recomputed
     (200, 40, 16, "ties"),
+    # the fused two-kernel layout at one GPU's skewed share (512 chunks of 32
+    # tokens) and with 2 token passes per chunk (511 chunks of 64 tokens, a
+    # partial last one); the general four-kernel layout where the fused pair
+    # would need more passes or histogram entries (128 and 1024 experts)
+    (16384, 32, 8, "zipf"),
+    (32700, 32, 8, "zipf"),
+    (20000, 128, 4, "zipf"),
+    (9000, 1024, 4, "normal"),
+    (500, 256, 8, "ties"),       # 4 logits per lane
+    (150, 600, 5, "normal"),     # 16 logits per lane
 ]
 
 

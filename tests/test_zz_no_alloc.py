@@ -62,9 +62,11 @@ def _logits(T, E, seed, zipf):
 
 @pytest.mark.parametrize("renorm", [False, True])
 def test_noalloc_route_matches_workspace_route(M, renorm):
-    # first a large routing (the skewed shape: 131072 pairs over 32 experts), then a
-    # smaller one on the same scratch
-    for (T, E, k, seed, zipf) in ((16384, 32, 8, 1003, True), (1000, 12, 3, 7, False)):
+    # a routing on the general layout path (1024 experts), then the skewed shape
+    # (131072 pairs over 32 experts, fused path), then a smaller one, all on the
+    # same scratch
+    for (T, E, k, seed, zipf) in ((9000, 1024, 4, 11, False), (16384, 32, 8, 1003, True),
+                                  (1000, 12, 3, 7, False)):
         print(f"noalloc route case T={T} E={E} k={k} renorm={renorm}", flush=True)
         lg = _logits(T, E, seed, zipf)
         cap, ref = _run(M, lg, k, noalloc=False, renorm=renorm)
