@@ -216,20 +216,26 @@ def main():
             timed(record, "permute+quant dO", lambda: M.moe_permute_quant_mxfp8(
                 dout, buf.src_of, wl.k, wl.E, QRC, buf.dy_q, buf.dy_s, buf.dyt_q, buf.dyt_s))
             # the FC2 dgrad writes only the MXFP8 copies of dH and A' (all the later MXFP8 GEMMs read)
-            M.moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
-                                  buf.offsets, None, None, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                                  buf.bwd_ws, M.MOE_STAGES_BWD, act=act, mx=buf.mx_bwd(True))
+        # dgrad2, wgrad2 and dgrad1 first; the unpermute-sum reads dX_perm while the last-level
+        # cache still holds it, before the FC1 wgrad's fp32 dW1 stores go through that cache
+        early = M.MOE_STAGES_BWD & ~M.MOE_STAGE_WGRAD1
+        if mx_mode:
+            bwd = lambda st: M.moe_grouped_mlp_bwd(
+                buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+                None, None, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, st, act=act, mx=buf.mx_bwd(True))
         elif args.gather:
-            M.moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
-                                  buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                                  buf.bwd_ws, M.MOE_STAGES_BWD | M.MOE_GATHER_ROWS, act=act)
+            bwd = lambda st: M.moe_grouped_mlp_bwd(
+                x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of, buf.offsets, buf.dh, buf.a_w,
+                buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, st | M.MOE_GATHER_ROWS, act=act)
         else:
             timed(record, "permute dO", lambda: M.moe_permute(dout, buf.row_of, buf.src_of, buf.offsets,
                                                               wl.k, wl.E, buf.dy_u))
-            M.moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
-                                  buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                                  buf.bwd_ws, M.MOE_STAGES_BWD, act=act)
+            bwd = lambda st: M.moe_grouped_mlp_bwd(
+                buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
+                buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, st, act=act)
+        bwd(early)
         timed(record, "unpermute-sum dX", lambda: M.moe_combine(buf.dx_perm, buf.row_of, None, wl.k, buf.dx))
+        bwd(M.MOE_STAGE_WGRAD1)
         M.moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits)
 
     for _ in range(args.warmup):

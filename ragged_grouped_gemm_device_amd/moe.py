@@ -365,14 +365,16 @@ def forward(buf: Buffers, x, logits, w1, w2, renorm=False, fwd_stages=MOE_STAGES
 
 def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIGLU, logits=None,
              renorm=False, x=None, mx=False, dgrad2_mx=True, mx_bf16_copies=True):
-    """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> wgrad1 -> unpermute-sum, and with
+    """gather dO -> dgrad2+dGLU (+dS) -> wgrad2 -> dgrad1 -> unpermute-sum -> wgrad1, and with
     the forward's logits also the router backward dS -> dlogits. With x given (the un-permuted
     input), the GEMMs read x and dO through src_of instead of permuted copies. With mx (buffers
     made with mx=True and quantize_weights done), dY_u is quantized (row-wise for the FC2 dgrad
     when dgrad2_mx, column-wise for the FC2 wgrad), X_perm column-wise unless the MXFP8 forward
     already did, and the GEMMs run on MXFP8 (the FC2 dgrad only with dgrad2_mx). With mx and
     mx_bf16_copies=False the FC2 dgrad writes only the MXFP8 copies of dH and A' (buf.dh and
-    buf.a_w are left untouched), which is all the later MXFP8 stages read."""
+    buf.a_w are left untouched), which is all the later MXFP8 stages read. The FC1 wgrad runs
+    last, after the unpermute-sum has read dX_perm."""
+    early, late = stages & ~MOE_STAGE_WGRAD1, stages & MOE_STAGE_WGRAD1
     if mx:
         if x is not None:
             raise ValueError("the MXFP8 backward quantizes the permuted copies: no row gather")
@@ -385,18 +387,22 @@ def backward(buf: Buffers, dout, w1, w2, stages=MOE_STAGES_BWD, act=MOE_ACT_SWIG
         if not buf.xt_from_forward:
             moe_quant_mxfp8(buf.x_perm, MOE_QUANT_COLWISE, None, None, buf.xt_q, buf.xt_s)
         dh, a_w = (buf.dh, buf.a_w) if mx_bf16_copies else (None, None)
-        moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
-                            buf.offsets, dh, a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                            buf.bwd_ws, stages, act=act, mx=buf.mx_bwd(dgrad2_mx))
+        bwd = lambda st: moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of,
+                                             buf.row_of, buf.offsets, dh, a_w, buf.ds, buf.dx_perm, buf.dw1,
+                                             buf.dw2, buf.bwd_ws, st, act=act, mx=buf.mx_bwd(dgrad2_mx))
     elif x is not None:
-        moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
-                            buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                            buf.bwd_ws, stages | MOE_GATHER_ROWS, act=act)
+        bwd = lambda st: moe_grouped_mlp_bwd(x, w1, w2, buf.h, dout, buf.topk_w, buf.src_of, buf.row_of,
+                                             buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1,
+                                             buf.dw2, buf.bwd_ws, st | MOE_GATHER_ROWS, act=act)
     else:
         moe_permute(dout, buf.row_of, buf.src_of, buf.offsets, buf.k, buf.E, buf.dy_u)
-        moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of,
-                            buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm, buf.dw1, buf.dw2,
-                            buf.bwd_ws, stages, act=act)
+        bwd = lambda st: moe_grouped_mlp_bwd(buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of,
+                                             buf.row_of, buf.offsets, buf.dh, buf.a_w, buf.ds, buf.dx_perm,
+                                             buf.dw1, buf.dw2, buf.bwd_ws, st, act=act)
+    if early:
+        bwd(early)
     moe_combine(buf.dx_perm, buf.row_of, None, buf.k, buf.dx)
+    if late:
+        bwd(late)
     if logits is not None:
         moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits, renorm)
