@@ -236,6 +236,8 @@ typedef struct moe_mx_fwd {
     const uint8_t* w1t_s;  /* [E, 2n, d/32] its scales (in)                      */
     uint8_t* y_q;          /* [M_cap, d]    row-wise codes of Y (out), or NULL    */
     uint8_t* y_s;          /* [M_cap, d/32] its scales (out)                     */
+    uint8_t* yt_q;         /* [d, M_cap]    transposed (column-wise) codes of Y (out), or NULL */
+    uint8_t* yt_s;         /* [d, M_cap/32] its scales (out)                     */
 } moe_mx_fwd;
 
 /*
@@ -259,7 +261,9 @@ typedef struct moe_mx_fwd {
  *        - y_q != NULL: the FC2 epilogue also writes the row-wise MXFP8 copy
  *          of the bf16 Y (blocks of 32 along d; the "GroupGemm + Quantize"
  *          fused kernel [P3, next-steps section], for an FP8 combine or
- *          all-to-all), and y may then be NULL;
+ *          all-to-all), and, if yt_q != NULL, its column-wise copy stored
+ *          transposed (blocks of 32 rows of an expert region, as at_q); y may
+ *          then be NULL;
  *        - x_q != NULL: FC1 also runs on MX-scaled MFMA, from x_q/x_s and
  *          w1t_q/w1t_s instead of x_perm and w1 (then a_q is required,
  *          d % 128 == 0 and no MOE_GATHER_ROWS).
@@ -311,6 +315,8 @@ typedef struct moe_mx_bwd {
     const uint8_t* w2_s;   /* [E, n, d/32]                                      */
     uint8_t* dx_q;         /* [M_cap, d]      row-wise codes of dX_perm (DGRAD1 out), or NULL */
     uint8_t* dx_s;         /* [M_cap, d/32]                                     */
+    uint8_t* dxt_q;        /* [d, M_cap]      column-wise codes of dX_perm, transposed (DGRAD1 out), or NULL */
+    uint8_t* dxt_s;        /* [d, M_cap/32]                                     */
 } moe_mx_bwd;
 
 /*
@@ -348,8 +354,9 @@ typedef struct moe_mx_bwd {
  *   transposed) and of A' (column-wise transposed); the other three GEMMs
  *   run on MX-scaled MFMA: DGRAD1 from dh_q x w1_q (with dx_q != NULL its
  *   epilogue also writes the row-wise MXFP8 copy of the bf16 dX_perm, the
- *   "GroupGemm + Quantize" kernel [P3, next-steps section], and dx_perm may
- *   then be NULL), WGRAD2 from awt_q x
+ *   "GroupGemm + Quantize" kernel [P3, next-steps section], with dxt_q !=
+ *   NULL also its column-wise copy stored transposed, and dx_perm may then
+ *   be NULL), WGRAD2 from awt_q x
  *   dyt_q, WGRAD1 from xt_q x dht_q (K = the expert's row region). Only the
  *   rows of expert regions are written in the transposed copies; dh and
  *   a_w may then be NULL (their bf16 stores are skipped; no stage reads

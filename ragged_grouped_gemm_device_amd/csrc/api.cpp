@@ -152,8 +152,10 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if ((mx->a_q == nullptr) != (mx->a_s == nullptr)) return MOE_ERR_INVALID_ARG;
         if ((mx->at_q == nullptr) != (mx->at_s == nullptr) || (mx->at_q && !mx->a_q)) return MOE_ERR_INVALID_ARG;
         if ((mx->y_q == nullptr) != (mx->y_s == nullptr)) return MOE_ERR_INVALID_ARG;
+        if ((mx->yt_q == nullptr) != (mx->yt_s == nullptr) || (mx->yt_q && !mx->y_q)) return MOE_ERR_INVALID_ARG;
         if ((mx->a_q && (!aligned16(mx->a_q) || !aligned16(mx->a_s))) ||
-            (mx->at_q && (!aligned16(mx->at_q) || !aligned16(mx->at_s))) || (mx->y_q && !aligned16(mx->y_q)))
+            (mx->at_q && (!aligned16(mx->at_q) || !aligned16(mx->at_s))) || (mx->y_q && !aligned16(mx->y_q)) ||
+            (mx->yt_q && (!aligned16(mx->yt_q) || !aligned16(mx->yt_s))))
             return MOE_ERR_INVALID_ARG;
         if (fc2_mx && (stages & MOE_STAGE_FC2)) {
             if (n % 128) return MOE_ERR_UNSUPPORTED;  // whole 128-byte K slabs of the MX FC2
@@ -193,9 +195,11 @@ int moe_grouped_mlp_fwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     if (stages & MOE_STAGE_FC2) {
         uint8_t* y_q = y_mx ? mx->y_q : nullptr;
         uint8_t* y_s = y_mx ? mx->y_s : nullptr;
+        uint8_t* yt_q = y_mx ? mx->yt_q : nullptr;
+        uint8_t* yt_s = y_mx ? mx->yt_s : nullptr;
         const int rc2 = fc2_mx ? moe::launch_mx_fc2(mx->a_q, mx->a_s, mx->w2t_q, mx->w2t_s, offsets, E, d, n,
-                                                     M_cap, y, y_q, y_s, s)
-                               : moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, y_q, y_s, s);
+                                                     M_cap, y, y_q, y_s, yt_q, yt_s, s)
+                               : moe::launch_fc2(a, w2, offsets, E, d, n, M_cap, y, y_q, y_s, yt_q, yt_s, s);
         if (rc2) return MOE_ERR_LAUNCH;
     }
     return MOE_OK;
@@ -246,6 +250,9 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
         if ((!dx_perm && !dx_mx) || (dx_perm && !aligned16(dx_perm))) return MOE_ERR_INVALID_ARG;
         if (mx && ((mx->dx_q == nullptr) != (mx->dx_s == nullptr) || (dx_mx && !aligned16(mx->dx_q))))
             return MOE_ERR_INVALID_ARG;
+        if (mx && ((mx->dxt_q == nullptr) != (mx->dxt_s == nullptr) || (mx->dxt_q && !dx_mx) ||
+                   (mx->dxt_q && (!aligned16(mx->dxt_q) || !aligned16(mx->dxt_s)))))
+            return MOE_ERR_INVALID_ARG;
         if (!mx && (!dh || !w1 || !aligned16(dh) || !aligned16(w1))) return MOE_ERR_INVALID_ARG;
     }
     if (stages & MOE_STAGE_WGRAD1) {
@@ -291,7 +298,8 @@ int moe_grouped_mlp_bwd(const uint16_t* x_perm, const uint16_t* w1, const uint16
     }
     if (stages & MOE_STAGE_DGRAD1) {
         const int rc1 = mx ? moe::launch_mx_ragged_m(mx->dh_q, mx->dh_s, mx->w1_q, mx->w1_s, offsets, E, d,
-                                                      2 * n, M_cap, dx_perm, mx->dx_q, mx->dx_s, s)
+                                                      2 * n, M_cap, dx_perm, mx->dx_q, mx->dx_s, mx->dxt_q,
+                                                      mx->dxt_s, s)
                            : moe::launch_dgrad1(dh, w1, offsets, E, d, n1, M_cap, dx_perm, s);
         if (rc1) return MOE_ERR_LAUNCH;
     }

@@ -698,13 +698,23 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 if constexpr (EPI == EPI_BF16_MX) {
                     // the row-wise MXFP8 copy of the bf16-rounded output (blocks of 32
                     // columns: lanes l and l ^ 32 share a row, so both take the branch)
+                    // and, when asked, its column-wise copy stored transposed (blocks of
+                    // 32 rows, which lie wholly inside or past a 128-row region, so the
+                    // whole wavefront takes the branch)
                     const int m = rband + 32 * I + r;
+                    const int mb = rband + 32 * I;
                     if (m < row_end) {
                         static_for<TNW>([&](auto J) {
                             const int cb = col0 + 32 * J;
-                            if (cb < p.N)
+                            if (cb < p.N) {
                                 mx_rowq32(pk[J], lane, p.q_row + (int64_t)m * p.N + cb,
                                           p.s_row + (int64_t)m * (p.N / 32) + cb / 32);
+                                if (p.q_col) {
+                                    const int64_t ls = p.M_cap / 32;
+                                    mx_colq32(pk[J], lane, p.q_col + (int64_t)cb * p.M_cap + mb, p.M_cap,
+                                              p.s_col + (int64_t)cb * ls + mb / 32, ls);
+                                }
+                            }
                         });
                     }
                 }
@@ -1229,13 +1239,15 @@ int launch_fc1_glu_mxin(const uint8_t* x_q, const uint8_t* x_s, const uint8_t* w
 }
 
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
-               int64_t M_cap, uint16_t* y, uint8_t* y_q, uint8_t* y_s, hipStream_t s) {
+               int64_t M_cap, uint16_t* y, uint8_t* y_q, uint8_t* y_s, uint8_t* yt_q, uint8_t* yt_s,
+               hipStream_t s) {
     GemmArgs g = zero_args();
     g.A = a; g.lda = n;
     g.B = w2; g.ldb = d; g.b_estride = (int64_t)n * d;
     g.offsets = offsets; g.E = E; g.N = d; g.K = n;
     g.out0 = y; g.ld0 = d;
     g.q_row = y_q; g.s_row = y_s;
+    g.q_col = yt_q; g.s_col = yt_s; g.M_cap = M_cap;
     if (y_q) return run<false, true, false, EPI_BF16_MX>(g, ragged_m_grid(M_cap, E, d), s);
     return run<false, true, false, EPI_BF16>(g, ragged_m_grid(M_cap, E, d), s);
 }

@@ -54,20 +54,23 @@ int launch_fc1_glu_mx(const uint16_t* x_perm, const uint16_t* w1, const int32_t*
                       uint16_t* a, uint8_t* a_q, uint8_t* a_s, uint8_t* at_q, uint8_t* at_s,
                       hipStream_t s);
 // q_row / s_row (nullable): the row-wise MXFP8 copy of the bf16 output, written by
-// the GEMM epilogue (GroupGemm + Quantize); the bf16 output is then nullable
+// the GEMM epilogue (GroupGemm + Quantize); the bf16 output is then nullable.
+// q_col / s_col (nullable, only beside q_row): its column-wise copy, transposed
+// (codes [N, M_cap], scales [N, M_cap / 32]).
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
                   const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
-                  uint8_t* y_q, uint8_t* y_s, hipStream_t s);
+                  uint8_t* y_q, uint8_t* y_s, uint8_t* yt_q, uint8_t* yt_s, hipStream_t s);
 // out[R_e] = MX(A[R_e]) x MX(B_e)^T (bf16 [M_cap, N]); A [M_cap, K], B [E, N, K]
 int launch_mx_ragged_m(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                        const int32_t* offsets, int E, int N, int K, int64_t M_cap, uint16_t* out,
-                       uint8_t* q_row, uint8_t* s_row, hipStream_t s);
+                       uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s);
 // out_e = MX(At[:, R_e]) x MX(Bt[:, R_e])^T (fp32 [E, M, N]); At [M, M_cap], Bt [N, M_cap]
 int launch_mx_wgrad(const uint8_t* at_q, const uint8_t* at_s, int M, const uint8_t* bt_q,
                     const uint8_t* bt_s, int N, const int32_t* offsets, int E, int64_t M_cap,
                     float* out, hipStream_t s);
 int launch_fc2(const uint16_t* a, const uint16_t* w2, const int32_t* offsets, int E, int d, int n,
-               int64_t M_cap, uint16_t* y, uint8_t* y_q, uint8_t* y_s, hipStream_t s);
+               int64_t M_cap, uint16_t* y, uint8_t* y_q, uint8_t* y_s, uint8_t* yt_q, uint8_t* yt_s,
+               hipStream_t s);
 int launch_dgrad2_dglu(const uint16_t* dy_u, const uint16_t* w2, const uint16_t* h,
                        const float* topk_w, const int32_t* src_of, const int32_t* offsets, int E,
                        int d, int n, int64_t M_cap, int act, const GatherSpec& gdy, uint16_t* dh,

@@ -215,6 +215,9 @@ struct MxArgs {
     float* outf;         // ragged K: [E, M, N] fp32
     uint8_t* q_row;      // ragged M, nullable: row-wise MXFP8 copy of out, codes [M_cap, N]
     uint8_t* s_row;      //   and scales [M_cap, N/32]
+    uint8_t* q_col;      // ragged M, nullable (only beside q_row): column-wise copy, transposed,
+    uint8_t* s_col;      //   codes [N, M_cap] and scales [N, M_cap/32]
+    int64_t M_cap;
 };
 
 constexpr int MBK = 128;  // K bytes per LDS slab
@@ -495,14 +498,24 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                     });
                 });
                 // GroupGemm + Quantize: the row-wise MXFP8 copy of the bf16 output
-                // (lanes l and l ^ 32 share a row, so both take the branch)
+                // (lanes l and l ^ 32 share a row, so both take the branch) and,
+                // when asked, its column-wise copy stored transposed (a 32-row block
+                // lies wholly inside or past a 128-row region: the whole wavefront
+                // takes the branch)
                 const int mq = tl.row0 + wm * 128 + 32 * I + r;
+                const int mb = tl.row0 + wm * 128 + 32 * I;
                 if (p.q_row && mq < tl.row_end) {
                     static_for<TNW>([&](auto J) {
                         const int cb = col0 + 32 * J;
-                        if (cb < p.N)
+                        if (cb < p.N) {
                             mx_rowq32(pk[J], lane, p.q_row + (int64_t)mq * p.N + cb,
                                       p.s_row + (int64_t)mq * (p.N / 32) + cb / 32);
+                            if (p.q_col) {
+                                const int64_t ls = p.M_cap / 32;
+                                mx_colq32(pk[J], lane, p.q_col + (int64_t)cb * p.M_cap + mb, p.M_cap,
+                                          p.s_col + (int64_t)cb * ls + mb / 32, ls);
+                            }
+                        }
                     });
                 }
                 wave_lds_sync();
@@ -545,19 +558,20 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
 
 int launch_mx_fc2(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w2t_q, const uint8_t* w2t_s,
                   const int32_t* offsets, int E, int d, int n, int64_t M_cap, uint16_t* y,
-                  uint8_t* y_q, uint8_t* y_s, hipStream_t s) {
-    return launch_mx_ragged_m(a_q, a_s, w2t_q, w2t_s, offsets, E, d, n, M_cap, y, y_q, y_s, s);
+                  uint8_t* y_q, uint8_t* y_s, uint8_t* yt_q, uint8_t* yt_s, hipStream_t s) {
+    return launch_mx_ragged_m(a_q, a_s, w2t_q, w2t_s, offsets, E, d, n, M_cap, y, y_q, y_s, yt_q, yt_s, s);
 }
 
 int launch_mx_ragged_m(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
                        const int32_t* offsets, int E, int N, int K, int64_t M_cap, uint16_t* out,
-                       uint8_t* q_row, uint8_t* s_row, hipStream_t s) {
+                       uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t s) {
     MxArgs a;
     __builtin_memset(&a, 0, sizeof(a));
     a.A = a_q; a.As = a_s; a.B = b_q; a.Bs = b_s;
     a.offsets = offsets; a.E = E; a.N = N; a.K = K; a.ld = K;
     a.out = out;
     a.q_row = q_row; a.s_row = s_row;
+    a.q_col = q_row ? q_col : nullptr; a.s_col = s_col; a.M_cap = M_cap;
     const int64_t tb = ragged_m_grid(M_cap, E, N);
     if (tb <= 0) return 0;
     mx_gemm_kernel<false><<<persistent_grid(tb), kThreads, 0, s>>>(a);

@@ -72,9 +72,10 @@ class MoEError(RuntimeError):
 
 
 MX_FWD_FIELDS = ("a_q", "a_s", "at_q", "at_s", "w2t_q", "w2t_s", "x_q", "x_s", "w1t_q", "w1t_s",
-                 "y_q", "y_s")
+                 "y_q", "y_s", "yt_q", "yt_s")
 MX_BWD_FIELDS = ("dh_q", "dh_s", "dht_q", "dht_s", "awt_q", "awt_s", "dyt_q", "dyt_s", "xt_q", "xt_s",
-                 "w1_q", "w1_s", "dy_q", "dy_s", "w2_q", "w2_s", "dx_q", "dx_s")
+                 "w1_q", "w1_s", "dy_q", "dy_s", "w2_q", "w2_s", "dx_q", "dx_s",
+                 "dxt_q", "dxt_s")
 
 
 class moe_mx_fwd(C.Structure):
@@ -305,6 +306,11 @@ class Buffers:
             self.y_s = torch.empty(M, d // 32, dtype=u8, device=dev)
             self.dx_q = torch.empty(M, d, dtype=u8, device=dev)
             self.dx_s = torch.empty(M, d // 32, dtype=u8, device=dev)
+            # and their column-wise copies, transposed
+            self.yt_q = torch.empty(d, M, dtype=u8, device=dev)
+            self.yt_s = torch.empty(d, M // 32, dtype=u8, device=dev)
+            self.dxt_q = torch.empty(d, M, dtype=u8, device=dev)
+            self.dxt_s = torch.empty(d, M // 32, dtype=u8, device=dev)
         self.xt_from_forward = False
 
     def quantize_weights(self, w1, w2):
@@ -316,23 +322,28 @@ class Buffers:
         moe_quant_mxfp8(w2, MOE_QUANT_ROWWISE | MOE_QUANT_COLWISE, self.w2_q, self.w2_s, self.w2t_q,
                         self.w2t_s)
 
-    def mx_fwd(self, fc1=True, transposed_a=False, quant_y=False):
+    def mx_fwd(self, fc1=True, transposed_a=False, quant_y=False, transposed_y=False):
         """The moe_mx_fwd fields: FC1 on MXFP8 operands when fc1; the transposed copy of A
         only when asked (the training step's FC2 wgrad reads A' = w A, quantized by the FC2
-        dgrad, not A); the row-wise MXFP8 copy of Y (FC2 epilogue) when quant_y."""
+        dgrad, not A); the row-wise MXFP8 copy of Y (FC2 epilogue) when quant_y, with its
+        transposed column-wise copy when transposed_y."""
         keys = MX_FWD_FIELDS[:10] if fc1 else MX_FWD_FIELDS[:6]
         d = {key: getattr(self, key) for key in keys}
         if not transposed_a:
             d["at_q"] = d["at_s"] = None
         if quant_y:
             d["y_q"], d["y_s"] = self.y_q, self.y_s
+            if transposed_y:
+                d["yt_q"], d["yt_s"] = self.yt_q, self.yt_s
         return d
 
-    def mx_bwd(self, dgrad2=True, quant_dx=False):
+    def mx_bwd(self, dgrad2=True, quant_dx=False, transposed_dx=False):
         keys = MX_BWD_FIELDS[:16] if dgrad2 else MX_BWD_FIELDS[:12]
         d = {key: getattr(self, key) for key in keys}
         if quant_dx:
             d["dx_q"], d["dx_s"] = self.dx_q, self.dx_s
+            if transposed_dx:
+                d["dxt_q"], d["dxt_s"] = self.dxt_q, self.dxt_s
         return d
 
 

@@ -165,6 +165,21 @@ def test_host_validation_returns_before_launch():
             rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, stage,
                                          f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)
             assert rc == M.MOE_ERR_INVALID_ARG, (stage, key)
+    # the transposed copy of dX_perm needs its scales and the row-wise copy beside it
+    for drop in ("dxt_s", "dx_q"):
+        mx = M.moe_mx_bwd(*[None if k2 in (drop, "dx_s" if drop == "dx_q" else "") else full[k2]
+                            for k2 in M.MX_BWD_FIELDS])
+        rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x10,
+                                     f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)
+        assert rc == M.MOE_ERR_INVALID_ARG, drop
+    # likewise the transposed copy of Y in the forward
+    fwd = {key: f for key in M.MX_FWD_FIELDS}
+    for drop in ("yt_s", "y_q"):
+        mxf = M.moe_mx_fwd(*[None if k2 in (drop, "y_s" if drop == "y_q" else "") else fwd[k2]
+                             for k2 in M.MX_FWD_FIELDS])
+        rc = lib.moe_grouped_mlp_fwd(f, f, f, f, None, 0, 0, 4, 128, 128, 1024, 0, 2, None, f, f,
+                                     C.byref(mxf), None)
+        assert rc == M.MOE_ERR_INVALID_ARG, drop
     mx = M.moe_mx_bwd(*[_fake(0x1001) if k2 == "w1_q" else full[k2] for k2 in M.MX_BWD_FIELDS])
     rc = lib.moe_grouped_mlp_bwd(f, f, f, f, f, f, f, f, f, 8, 2, 4, 128, 64, 1024, 0, 0x10,
                                  f, f, f, f, f, f, f, 1 << 20, C.byref(mx), None)

@@ -343,10 +343,11 @@ GQ_CASES = [MX_CASES[0], MX_CASES[1], FC1_MX_CASES[1]]
 
 @pytest.mark.parametrize("wl", GQ_CASES, ids=[c.name for c in GQ_CASES])
 def test_groupgemm_quantize_fc2(M, wl):
-    """GroupGemm + Quantize: the FC2 epilogue's row-wise MXFP8 copy of Y equals, bit for
-    bit, the oracle's quantization of the GPU's own bf16 Y, on the bf16 FC2 (plain FC1,
-    mx given only for y_q) and on the MXFP8 FC2; the bf16 Y beside it is unchanged, and
-    with y = NULL the copy alone is written (the same bytes)."""
+    """GroupGemm + Quantize: the FC2 epilogue's row-wise MXFP8 copy of Y and its
+    transposed column-wise copy equal, bit for bit, the oracle's quantization of the
+    GPU's own bf16 Y, on the bf16 FC2 (plain FC1, mx given only for the copies) and on
+    the MXFP8 FC2; the bf16 Y beside them is unchanged, and with y = NULL the copies
+    alone are written (the same bytes)."""
     print(f"groupgemm+quantize case {wl}", flush=True)
     inp = W.make_inputs(wl)
     x, w1, w2 = bf16_tensor(inp["x"]), bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
@@ -363,21 +364,25 @@ def test_groupgemm_quantize_fc2(M, wl):
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD,
                               mx=mx0)
         y_ref = buf.y.clone()
-        for t in (buf.y_q, buf.y_s):
+        for t in (buf.y_q, buf.y_s, buf.yt_q, buf.yt_s):
             t.fill_(0xAB)
         buf.y.fill_(float("nan"))
-        mx1 = dict(mx0 or {}, y_q=buf.y_q, y_s=buf.y_s)
+        mx1 = dict(mx0 or {}, y_q=buf.y_q, y_s=buf.y_s, yt_q=buf.yt_q, yt_s=buf.yt_s)
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, buf.a, buf.y, M.MOE_STAGES_FWD,
                               mx=mx1)
         torch.cuda.synchronize()
         assert torch.equal(buf.y[:end], y_ref[:end]), "bf16 Y changed"
-        check_fused_copies_vs_oracle(buf.y, end, buf.y_q, buf.y_s, None, None, "Y")
+        check_fused_copies_vs_oracle(buf.y, end, buf.y_q, buf.y_s, buf.yt_q, buf.yt_s, "Y")
         q_ref, s_ref = buf.y_q[:end].clone(), buf.y_s[:end].clone()
-        # quantized copy only (no bf16 Y)
+        qt_ref, st_ref = buf.yt_q[:, :end].clone(), buf.yt_s[:, :end // 32].clone()
+        # quantized copies only (no bf16 Y)
         buf.y_q.fill_(0xAB)
+        buf.yt_q.fill_(0xAB)
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, None, M.MOE_STAGE_FC2, mx=mx1)
         torch.cuda.synchronize()
         assert torch.equal(buf.y_q[:end], q_ref) and torch.equal(buf.y_s[:end], s_ref)
+        assert torch.equal(buf.yt_q[:, :end], qt_ref) and torch.equal(buf.yt_s[:, :end // 32], st_ref)
         # rows past the last region are never written
         if end < buf.M_cap:
             assert torch.all(buf.y_q[end:] == 0xAB)
+            assert torch.all(buf.yt_q[:, end:] == 0xAB)

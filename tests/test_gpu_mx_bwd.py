@@ -164,27 +164,31 @@ def test_mx_backward_parity(M, wl, act, dgrad2_mx):
 @pytest.mark.parametrize("wl", [CASES[0], CASES[2]], ids=[CASES[0].name, CASES[2].name])
 def test_groupgemm_quantize_dgrad1(M, wl):
     """GroupGemm + Quantize in the backward: the MX FC1 dgrad's epilogue writes the row-wise
-    MXFP8 copy of dX_perm, bit for bit the oracle's quantization of the GPU's own bf16
-    dX_perm, without changing dX_perm (and alone when dx_perm is NULL)."""
+    MXFP8 copy of dX_perm and its transposed column-wise copy, bit for bit the oracle's
+    quantization of the GPU's own bf16 dX_perm, without changing dX_perm (and alone when
+    dx_perm is NULL)."""
     inp = W.make_inputs(wl)
     buf = _run_gpu(M, wl, inp, M.MOE_ACT_SWIGLU)
     end = int(buf.offsets[-1].item())
     dx_ref = buf.dx_perm.clone()
-    for t in (buf.dx_q, buf.dx_s):
+    for t in (buf.dx_q, buf.dx_s, buf.dxt_q, buf.dxt_s):
         t.fill_(0xAB)
     w1, w2 = bf16_tensor(inp["w1"]), bf16_tensor(inp["w2"])
     args = (buf.x_perm, w1, w2, buf.h, buf.dy_u, buf.topk_w, buf.src_of, buf.row_of, buf.offsets,
             buf.dh, buf.a_w, buf.ds)
-    mx = buf.mx_bwd(dgrad2=False, quant_dx=True)
+    mx = buf.mx_bwd(dgrad2=False, quant_dx=True, transposed_dx=True)
     M.moe_grouped_mlp_bwd(*args, buf.dx_perm, buf.dw1, buf.dw2, buf.bwd_ws, M.MOE_STAGE_DGRAD1, mx=mx)
     torch.cuda.synchronize()
     assert torch.equal(buf.dx_perm[:end], dx_ref[:end])
-    check_fused_copies_vs_oracle(buf.dx_perm, end, buf.dx_q, buf.dx_s, None, None, "dX_perm")
-    q_ref = buf.dx_q[:end].clone()
+    check_fused_copies_vs_oracle(buf.dx_perm, end, buf.dx_q, buf.dx_s, buf.dxt_q, buf.dxt_s, "dX_perm")
+    q_ref, qt_ref = buf.dx_q[:end].clone(), buf.dxt_q[:, :end].clone()
     buf.dx_q.fill_(0xAB)
+    buf.dxt_q.fill_(0xAB)
     M.moe_grouped_mlp_bwd(*args, None, buf.dw1, buf.dw2, buf.bwd_ws, M.MOE_STAGE_DGRAD1, mx=mx)
     torch.cuda.synchronize()
-    assert torch.equal(buf.dx_q[:end], q_ref)
+    assert torch.equal(buf.dx_q[:end], q_ref) and torch.equal(buf.dxt_q[:, :end], qt_ref)
+    if end < buf.M_cap:
+        assert torch.all(buf.dxt_q[:, end:] == 0xAB)
 
 
 def test_mx_wgrad_all_tokens_to_one_expert(M):
