@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--gather", action="store_true",
                     help="GEMMs read x and dO rows through src_of (no permuted copies)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-replays", type=int, default=20,
+                    help="after the eager steps, capture one step in a hipGraph and time this many "
+                         "replays (0: skip)")
     ap.add_argument("--detail", action="store_true", help="also time every stage alone (stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (reference for HBM byte counters)")
@@ -272,6 +275,37 @@ def main():
     print(f"[bench] {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f} ms), {value:.1f} TFLOP/s; "
           f"FC1+{glu} {fc1_ms:.3f} ms = {fc1_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
+    # the same step captured once in a hipGraph and replayed: per-replay HIP events, median
+    graph = None
+    if args.graph_replays > 0:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()  # warm-up outside capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.graph_replays):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        med = times[len(times) // 2]
+        graph = {"replays": args.graph_replays, "ms_per_step_median": round(med, 4),
+                 "ms_min": round(times[0], 4), "ms_max": round(times[-1], 4),
+                 "value_median": round(flops / (med * 1e-3) / 1e12, 2)}
+        assert int(buf.err.item()) == 0
+        print(f"[bench] hipGraph replay: median {med:.3f} ms/step over {args.graph_replays} replays "
+              f"({graph['value_median']:.1f} TFLOP/s)", file=sys.stderr, flush=True)
+        del g
+
     if args.detail:
         buf.logits_for_detail = logits
         _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx, act=act, glu=glu, gather=args.gather,
@@ -319,6 +353,7 @@ def main():
             "traffic_unit": "bytes per launch",
         },
         "bandwidth": bandwidth,
+        "graph": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
