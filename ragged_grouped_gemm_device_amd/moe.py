@@ -180,6 +180,20 @@ def moe_combine(y, row_of, w, k, out):
     _check("moe_combine", rc)
 
 
+def _fits(t, rows, cols, name):
+    """The C ABI takes bare pointers: a tensor given for an operand of `cols` columns must be a
+    dense [>= rows, cols] matrix (or [E, rows, cols] when rows is a tuple), else the kernels
+    would address past it."""
+    if t is None:
+        return
+    want = tuple(rows) + (cols,) if isinstance(rows, tuple) else None
+    ok = t.is_contiguous() and (tuple(t.shape) == want if want else
+                                t.dim() == 2 and t.shape[1] == cols and t.shape[0] >= rows)
+    if not ok:
+        raise ValueError(f"{name}: shape {tuple(t.shape)} does not fit "
+                         f"{want if want else f'[>= {rows}, {cols}]'} (dense)")
+
+
 def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD, mx=None,
                         act=MOE_ACT_SWIGLU, src_of=None, k=0):
     """With MOE_GATHER_ROWS in stages, x_perm is the un-permuted x [T, d] and src_of, k are
@@ -188,6 +202,12 @@ def moe_grouped_mlp_fwd(x_perm, w1, w2, offsets, h, a, y, stages=MOE_STAGES_FWD,
     n = n1 if act == MOE_ACT_SRELU else n1 // 2
     M_cap = (a if a is not None else mx["a_q"]).shape[0]  # a may be None with mx
     T = x_perm.shape[0] if (stages & MOE_GATHER_ROWS) else 0
+    if x_perm is not None:
+        _fits(x_perm, T if (stages & MOE_GATHER_ROWS) else M_cap, d, "x_perm")
+    _fits(w2, (E, n), d, "w2")
+    _fits(h, M_cap, n1, "h")
+    _fits(a, M_cap, n, "a")
+    _fits(y, M_cap, d, "y")
     mxp = None
     if mx is not None:
         mxs = moe_mx_fwd(*[_ptr(mx.get(key)) for key in MX_FWD_FIELDS])
@@ -213,6 +233,17 @@ def moe_grouped_mlp_bwd(x_perm, w1, w2, h, dy_u, topk_w, src_of, row_of, offsets
         mxp = C.byref(moe_mx_bwd(*[_ptr(mx.get(key)) for key in MX_BWD_FIELDS]))
     T, k = topk_w.shape
     M_cap = src_of.shape[0]
+    n1 = n if act == MOE_ACT_SRELU else 2 * n
+    rows_in = T if (stages & MOE_GATHER_ROWS) else M_cap
+    _fits(x_perm, rows_in, d, "x_perm")
+    _fits(dy_u, rows_in, d, "dy_u")
+    _fits(w2, (E, n), d, "w2")
+    _fits(h, M_cap, n1, "h")
+    _fits(dh, M_cap, n1, "dh")
+    _fits(a_w, M_cap, n, "a_w")
+    _fits(dx_perm, M_cap, d, "dx_perm")
+    _fits(dw1, (E, d), n1, "dw1")
+    _fits(dw2, (E, n), d, "dw2")
     rc = _lib().moe_grouped_mlp_bwd(_ptr(x_perm), _ptr(w1), _ptr(w2), _ptr(h), _ptr(dy_u),
                                     _ptr(topk_w), _ptr(src_of), _ptr(row_of), _ptr(offsets), T, k,
                                     E, d, n, M_cap, act, stages, _ptr(dh), _ptr(a_w), _ptr(ds),
