@@ -200,3 +200,24 @@ def test_host_validation_returns_before_launch():
     assert rc == M.MOE_ERR_UNSUPPORTED
     rc = lib.moe_quant_mxfp8(f, 1, 40, 64, 2, None, None, f, f, None)
     assert rc == M.MOE_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_operands_of_the_wrong_shape():
+    """The C ABI takes bare pointers; the binding checks every operand it sizes (raises
+    before any call), so a W1 of another layout cannot make the kernels write past H."""
+    import torch
+    E, d, n, M_cap = 2, 256, 64, 512
+    bf = torch.bfloat16
+    x = torch.zeros(M_cap, d, dtype=bf)
+    w1, w2 = torch.zeros(E, d, 2 * n, dtype=bf), torch.zeros(E, n, d, dtype=bf)
+    offs = torch.zeros(E + 1, dtype=torch.int32)
+    h, a, y = torch.zeros(M_cap, 2 * n, dtype=bf), torch.zeros(M_cap, n, dtype=bf), torch.zeros(M_cap, d, dtype=bf)
+    w1t = w1.transpose(1, 2).contiguous()     # [E, 2n, d]: read as d = 2n, n1 = d
+    with pytest.raises(ValueError):
+        M.moe_grouped_mlp_fwd(x, w1t, w2, offs, h, a, y, M.MOE_STAGE_FC1)
+    with pytest.raises(ValueError):
+        M.moe_grouped_mlp_fwd(x, w1, w2, offs, h[:, :n], a, y, M.MOE_STAGE_FC1)
+    with pytest.raises(ValueError):
+        M.moe_grouped_mlp_fwd(x[:, :64], w1, w2, offs, h, a, y, M.MOE_STAGE_FC1)
+    with pytest.raises(ValueError):
+        M.moe_grouped_mlp_fwd(x, w1, w2.transpose(1, 2), offs, h, a, y, M.MOE_STAGE_FC2)
