@@ -443,30 +443,34 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         const uint8_t* sA = (const uint8_t*)s_ab[buf];
         const uint8_t* sB = sA + BM * BK * 2;
         const int hh = lane >> 5;
+        auto xfrag = [&](const uint8_t* s, int base, int ks) -> i32x8_t {
+            const int r = base + (lane & 31);
+            const i32x4_t lo = *(const i32x4_t*)(s + kmaj_byte(r, 4 * ks + hh));
+            const i32x4_t hi = *(const i32x4_t*)(s + kmaj_byte(r, 4 * ks + 2 + hh));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        // the first MFMA row's operands (B, then A row 0) first; each A fragment of
+        // the next K step as soon as its row's MFMAs are issued, the next step's B
+        // fragments after the last row (every accumulator's MFMA order unchanged)
+        i32x8_t xa[4], xb[TNW];
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[i] = xfrag(sA, wm * 128 + 32 * i, 0);
         static_for<2>([&](auto KS) {
             constexpr int ks = KS;
-            i32x8_t xa[4], xb[TNW];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = wm * 128 + 32 * i + (lane & 31);
-                const i32x4_t lo = *(const i32x4_t*)(sA + kmaj_byte(r, 4 * ks + hh));
-                const i32x4_t hi = *(const i32x4_t*)(sA + kmaj_byte(r, 4 * ks + 2 + hh));
-                xa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
-#pragma unroll
-            for (int j = 0; j < TNW; ++j) {
-                const int r = wn * WN + 32 * j + (lane & 31);
-                const i32x4_t lo = *(const i32x4_t*)(sB + kmaj_byte(r, 4 * ks + hh));
-                const i32x4_t hi = *(const i32x4_t*)(sB + kmaj_byte(r, 4 * ks + 2 + hh));
-                xb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            }
             __builtin_amdgcn_s_setprio(1);
             static_for<4>([&](auto I) {
                 static_for<TNW>([&](auto J) {
                     acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         xb[J], xa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0, (int)(sa[I] >> (16 * ks)));
                 });
+                if constexpr (ks == 0) xa[I] = xfrag(sA, wm * 128 + 32 * I, 1);
             });
+            if constexpr (ks == 0) {
+#pragma unroll
+                for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 1);
+            }
             __builtin_amdgcn_s_setprio(0);
         });
         // keep the MFMAs above the slab barrier (left alone, the compiler sinks
