@@ -22,6 +22,8 @@ namespace moe {
 // instruction, which rounds to nearest-even like the codec above (the scale
 // keeps every value within +-448, so it never saturates).
 constexpr int QT = 128;  // tile edge
+typedef uint32_t nt_u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t nt_u32x4_t __attribute__((ext_vector_type(4)));
 
 // largest magnitude bit pattern (sign cleared) among 8 bf16 values
 __device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
@@ -35,7 +37,11 @@ __device__ __forceinline__ uint32_t abs_max_bf16x8(uint4 v) {
 // GATHER: row r of the matrix is row src_of[r] / k of src [T, C] (the
 // expert-major permutation, with zeros for padding rows, src_of[r] < 0), so
 // the permuted bf16 copy is never written.
-template <bool ROW, bool COL, bool GATHER>
+// NT: the codes leave as streaming (non-temporal) stores, which do not evict
+// the source rows from the last-level cache: a gathered row is read k times,
+// and a source that fits the cache (as one its producer just wrote does)
+// stays there.
+template <bool ROW, bool COL, bool GATHER, bool NT>
 __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __restrict__ src, int64_t R,
                                                           int C, uint8_t* __restrict__ q_row,
                                                           uint8_t* __restrict__ s_row,
@@ -90,7 +96,10 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
             q.x = e4m3x4(bf16_lo(x.x) * inv, bf16_hi(x.x) * inv, bf16_lo(x.y) * inv, bf16_hi(x.y) * inv);
             q.y = e4m3x4(bf16_lo(x.z) * inv, bf16_hi(x.z) * inv, bf16_lo(x.w) * inv, bf16_hi(x.w) * inv);
             if (cok && r + i < R) {
-                *(uint2*)(qr + (r + i) * C + c) = q;
+                if constexpr (NT)
+                    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x2_t, q), (nt_u32x2_t*)(qr + (r + i) * C + c));
+                else
+                    *(uint2*)(qr + (r + i) * C + c) = q;
                 if ((cc & 3) == 0) {
                     if (rs_words)
                         s_rs[(8 * rg + i) * 4 + (cc >> 2)] = (uint8_t)(e + 127);
@@ -160,7 +169,13 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
             const int idx = it * 256 + threadIdx.x;
             const int col = idx >> 3, pq = idx & 7;  // rows 16 pq .. 16 pq + 15 of the column
             const uint4 val = *(const uint4*)(tq + col * QT + (((2 * pq) ^ (2 * ((col >> 3) & 7))) * 8));
-            if (c0 + col < C && r0 + 16 * pq < R) *(uint4*)(qc + (int64_t)(c0 + col) * R + r0 + 16 * pq) = val;
+            if (c0 + col < C && r0 + 16 * pq < R) {
+                uint4* dst = (uint4*)(qc + (int64_t)(c0 + col) * R + r0 + 16 * pq);
+                if constexpr (NT)
+                    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4_t, val), (nt_u32x4_t*)dst);
+                else
+                    *dst = val;
+            }
         }
     }
 }
@@ -170,12 +185,19 @@ static void quant_dispatch(const uint16_t* src, int batch, int64_t R, int C, int
                            uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, const int32_t* src_of, int k,
                            hipStream_t s) {
     const dim3 grid((C + QT - 1) / QT, (unsigned)((R + QT - 1) / QT), batch);
+    // streaming code stores when the rows are gathered (each source row is read k
+    // times) or the bf16 source fits the 256 MB last-level cache; a larger source
+    // measured faster with normal stores
+    const bool nt = GATHER || (int64_t)batch * R * C * 2 <= (256ll << 20);
+    auto go = [&](auto kern) {
+        kern<<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
+    };
     if ((mode & 3) == 3)
-        quant_mxfp8_kernel<true, true, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
+        nt ? go(quant_mxfp8_kernel<true, true, GATHER, true>) : go(quant_mxfp8_kernel<true, true, GATHER, false>);
     else if (mode & 1)
-        quant_mxfp8_kernel<true, false, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
+        nt ? go(quant_mxfp8_kernel<true, false, GATHER, true>) : go(quant_mxfp8_kernel<true, false, GATHER, false>);
     else
-        quant_mxfp8_kernel<false, true, GATHER><<<grid, 256, 0, s>>>(src, R, C, q_row, s_row, q_col, s_col, src_of, k);
+        nt ? go(quant_mxfp8_kernel<false, true, GATHER, true>) : go(quant_mxfp8_kernel<false, true, GATHER, false>);
 }
 
 int launch_quant_mxfp8(const uint16_t* src, int batch, int64_t R, int C, int mode, uint8_t* q_row,
