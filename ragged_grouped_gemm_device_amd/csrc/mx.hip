@@ -109,6 +109,15 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const uint16_t* __rest
             }
         }
     }
+    if constexpr (ROW && COL && GATHER) {
+        // Left alone, the compiler keeps the 64 unpacked floats of the row pass
+        // live into the column pass (123 VGPRs, 4 wavefronts per SIMD); opaque
+        // words make the column pass unpack them again (70 VGPRs, 7 wavefronts).
+        // Measured faster for the gathered form (-4 to -5%), slower for the
+        // plain quantizer (+2 to +4%), which keeps the first schedule.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y), "+v"(v[i].z), "+v"(v[i].w));
+    }
     if constexpr (COL) {
         // R is a multiple of 32 here, so a wavefront's 32-row block is whole or
         // absent. The transposed codes go through LDS ([128 columns][128 rows]
