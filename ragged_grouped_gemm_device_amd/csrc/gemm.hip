@@ -956,7 +956,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             const int ct = n0 + wn * WN + 32 * J;  // first activation column of the tile
             if (ct < p.N) {
                 const int gcol = 2 * ct;
-                // pass 1: dH (bf16 stores, row-wise codes, column-wise codes staged)
+                // One pass over H: dH (bf16 stores, row-wise codes, column-wise codes
+                // staged) and A', whose bf16 pairs stay in registers until the dH
+                // column codes have left the stage (a second H read for A' cost 8%).
+                // Prefetching the next block's H as well made the kernel spill.
+                uint32_t awp[4][8];  // A' bf16 pairs of the 4 blocks
                 static_for<4>([&](auto I) {
                     const int m = rbase + 32 * I;
                     const int mb = band + 32 * I;  // first row of this 32-row block
@@ -967,27 +971,34 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         uint32_t dgp[8], dup[8];  // bf16 pairs, slots 2p, 2p + 1
                         static_for<4>([&](auto Q) {
                             const int cc = 8 * Q + 4 * h;
-                            float g[4], uu[4], dg[4], du[4];
+                            float g[4], uu[4], dg[4], du[4], aw[4];
                             unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
                             unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 float fg, dfg;
                                 glu_gate_grad<ACT>(g[s], fg, dfg);
+                                const float a = fg * uu[s];
                                 const float dap = acc[I][J][4 * Q + s];
-                                dsum[I] = fmaf(dap, fg * uu[s], dsum[I]);
+                                dsum[I] = fmaf(dap, a, dsum[I]);
                                 const float da = w * dap;
                                 dg[s] = da * uu[s] * dfg;
                                 du[s] = da * fg;
+                                aw[s] = w * a;
                             }
                             dgp[2 * Q] = pack_bf16x2(dg[0], dg[1]);
                             dgp[2 * Q + 1] = pack_bf16x2(dg[2], dg[3]);
                             dup[2 * Q] = pack_bf16x2(du[0], du[1]);
                             dup[2 * Q + 1] = pack_bf16x2(du[2], du[3]);
+                            awp[I][2 * Q] = pack_bf16x2(aw[0], aw[1]);
+                            awp[I][2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
                             if (p.out0) {  // the bf16 dH is optional: later MX stages read its codes
                                 *(uint2*)(p.out0 + drow + gcol + cc) = make_uint2(dgp[2 * Q], dgp[2 * Q + 1]);
                                 *(uint2*)(p.out0 + drow + gcol + 32 + cc) = make_uint2(dup[2 * Q], dup[2 * Q + 1]);
                             }
+                            if (p.out1)  // the bf16 A' is optional as well
+                                *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) =
+                                    make_uint2(awp[I][2 * Q], awp[I][2 * Q + 1]);
                         });
                         rowq(dgp, m, gcol);
                         rowq(dup, m, gcol + 32);
@@ -1000,28 +1011,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 mx_stage_flush(stg + 4096, lane, p.q_col + (int64_t)(gcol + 32) * p.M_cap + band, p.M_cap,
                                band_rows);
                 wave_lds_sync();
-                // pass 2: A' = w a (bf16 stores, column-wise codes staged), a recomputed from H
+                // A' column-wise codes from the kept pairs
                 static_for<4>([&](auto I) {
-                    const int m = rbase + 32 * I;
                     const int mb = band + 32 * I;
-                    if (mb < row_end) {
-                        const float w = wI[I];
-                        const int64_t hrow = (int64_t)m * p.ld_aux;
-                        uint32_t awp[8];
-                        static_for<4>([&](auto Q) {
-                            const int cc = 8 * Q + 4 * h;
-                            float g[4], uu[4], aw[4];
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
-#pragma unroll
-                            for (int s = 0; s < 4; ++s) aw[s] = w * (glu_gate<ACT>(g[s]) * uu[s]);
-                            awp[2 * Q] = pack_bf16x2(aw[0], aw[1]);
-                            awp[2 * Q + 1] = pack_bf16x2(aw[2], aw[3]);
-                            if (p.out1)  // the bf16 A' is optional as well
-                                *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) = make_uint2(awp[2 * Q], awp[2 * Q + 1]);
-                        });
-                        mx_colq32_stage(awp, lane, stg, I, p.s2_col + (int64_t)ct * ls + mb / 32, ls);
-                    }
+                    if (mb < row_end) mx_colq32_stage(awp[I], lane, stg, I, p.s2_col + (int64_t)ct * ls + mb / 32, ls);
                 });
                 wave_lds_sync();
                 mx_stage_flush(stg, lane, p.q2_col + (int64_t)ct * p.M_cap + band, p.M_cap, band_rows);
