@@ -968,12 +968,20 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         const float w = wI[I];
                         const int64_t hrow = (int64_t)m * p.ld_aux;
                         const int64_t drow = (int64_t)m * p.ld0;
+                        // the block's H (this lane's 16 gate and 16 up values) requested
+                        // at once: loading inside the loop below waited on each pair
+                        uint2 hg[4], hu[4];
+#pragma unroll
+                        for (int Q = 0; Q < 4; ++Q) {
+                            hg[Q] = *(const uint2*)(p.aux + hrow + gcol + 8 * Q + 4 * h);
+                            hu[Q] = *(const uint2*)(p.aux + hrow + gcol + 32 + 8 * Q + 4 * h);
+                        }
                         uint32_t dgp[8], dup[8];  // bf16 pairs, slots 2p, 2p + 1
                         static_for<4>([&](auto Q) {
                             const int cc = 8 * Q + 4 * h;
                             float g[4], uu[4], dg[4], du[4], aw[4];
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + cc), g);
-                            unpack_bf16x4(*(const uint2*)(p.aux + hrow + gcol + 32 + cc), uu);
+                            unpack_bf16x4(hg[Q], g);
+                            unpack_bf16x4(hu[Q], uu);
 #pragma unroll
                             for (int s = 0; s < 4; ++s) {
                                 float fg, dfg;
