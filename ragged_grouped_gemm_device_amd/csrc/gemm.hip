@@ -457,9 +457,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) xa[i] = xfrag(sA, wm * 128 + 32 * i, 0);
+        // no MFMA-phase issue priority here (measured 1.5% faster on MX FC1, unlike the
+        // bf16 modes, where it gains 2.3%)
         static_for<2>([&](auto KS) {
             constexpr int ks = KS;
-            __builtin_amdgcn_s_setprio(1);
             static_for<4>([&](auto I) {
                 static_for<TNW>([&](auto J) {
                     acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -471,7 +472,6 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 1);
             }
-            __builtin_amdgcn_s_setprio(0);
         });
         // keep the MFMAs above the slab barrier (left alone, the compiler sinks
         // them below it and serialises the copy wait with the multiply)
