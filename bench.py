@@ -421,10 +421,19 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
          2.0 * Mr * d + 2.0 * wl.T * d + 8.0 * Mr),
     ]
     if mx is not None:
-        qr = torch.empty(end, n, dtype=torch.uint8, device="cuda")
-        sr = torch.empty(end, n // 32, dtype=torch.uint8, device="cuda")
-        qc = torch.empty(n, end, dtype=torch.uint8, device="cuda")
-        sc = torch.empty(n, end // 32, dtype=torch.uint8, device="cuda")
+        # the standalone quantizer of A ([rows, n] bf16, 128 MB at the mxfp8 shape) cycles
+        # through 4 copies of its input and outputs, so that no call finds its source in the
+        # 256 MB last-level cache
+        qsets = [(buf.a[:end].clone(), torch.empty(end, n, dtype=torch.uint8, device="cuda"),
+                  torch.empty(end, n // 32, dtype=torch.uint8, device="cuda"),
+                  torch.empty(n, end, dtype=torch.uint8, device="cuda"),
+                  torch.empty(n, end // 32, dtype=torch.uint8, device="cuda")) for _ in range(4)]
+        qturn = [0]
+
+        def quant_a_rotated():
+            src, qr, sr, qc, sc = qsets[qturn[0] % 4]
+            qturn[0] += 1
+            M.moe_quant_mxfp8(src, 3, qr, sr, qc, sc)
         rows += [
             (f"FC1+{glu}+MXq", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h,
                                                              buf.a, buf.y, M.MOE_STAGE_FC1,
@@ -444,8 +453,7 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
             ("FC2 MXFP8", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a,
                                                         buf.y, M.MOE_STAGE_FC2, mx=mx),
              2.0 * Mr * d * n, None, PEAK_MXFP8_TFLOPS),
-            ("quant A row+col", lambda: M.moe_quant_mxfp8(buf.a[:end], 3, qr, sr, qc, sc), None,
-             2.0 * end * n + 2.0 * (end * n + end * n // 32)),
+            ("quant A row+col", quant_a_rotated, None, 2.0 * end * n + 2.0 * (end * n + end * n // 32)),
         ]
     logits = buf.logits_for_detail
     rows.append(("route bwd", lambda: M.moe_route_bwd(logits, buf.topk_idx, buf.ds, buf.dlogits), None,
