@@ -78,6 +78,24 @@ def _check(name, got, ref, rows=None, tol=TOL):
     assert err <= tol, f"{name}: {err}"
 
 
+def _random_cases(count, seed):
+    """Shapes drawn from a seeded generator: any token count (one token included),
+    k up to min(E, 8), 1-48 experts, d and n any multiple of 64 up to 640, each with
+    its own routing recipe; they land on partial tiles in M, N and K."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        E = int(rng.integers(1, 49))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = 1 if i == 0 else int(rng.integers(2, 1500))
+        d, n = 64 * int(rng.integers(1, 11)), 64 * int(rng.integers(1, 11))
+        routing = ("normal", "zipf", "balanced")[int(rng.integers(0, 3))] if T % E == 0 else (
+            "normal", "zipf")[int(rng.integers(0, 2))]
+        out.append(W.small(f"random{i}", T=T, k=k, E=E, d=d, n=n, seed=100 + i, routing=routing))
+    return out
+
+
+RANDOM_CASES = _random_cases(8, 2024)
 GEGLU_CASES = [CASES[1], CASES[2], CASES[4]]
 # gathered rows (MOE_GATHER_ROWS): no permuted copies of x and dO
 GATHER_CASES = [CASES[0], CASES[1], CASES[2], CASES[3]]
@@ -86,9 +104,11 @@ GATHER_CASES = [CASES[0], CASES[1], CASES[2], CASES[3]]
 @pytest.mark.parametrize(
     "wl,act,gather",
     [(c, "swiglu", False) for c in CASES] + [(c, "geglu", False) for c in GEGLU_CASES]
-    + [(c, "swiglu", True) for c in GATHER_CASES] + [(CASES[1], "geglu", True)],
+    + [(c, "swiglu", True) for c in GATHER_CASES] + [(CASES[1], "geglu", True)]
+    + [(c, "swiglu", False) for c in RANDOM_CASES],
     ids=[c.name for c in CASES] + [c.name + "-geglu" for c in GEGLU_CASES]
-    + [c.name + "-gather" for c in GATHER_CASES] + [CASES[1].name + "-geglu-gather"])
+    + [c.name + "-gather" for c in GATHER_CASES] + [CASES[1].name + "-geglu-gather"]
+    + [c.name for c in RANDOM_CASES])
 def test_forward_backward_parity(M, wl, act, gather):
     print(f"mlp case {wl} act={act} gather={gather}", flush=True)
     inp = W.make_inputs(wl)
