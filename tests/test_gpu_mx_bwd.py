@@ -84,8 +84,24 @@ def _check(name, got, ref, tol):
 
 # dgrad2_mx: the FC2 dgrad also on MXFP8 (dY_u row-wise x W2_e along d); d must be a
 # multiple of 128 for it
+def _random_cases(count, seed):
+    """Seeded shapes for the all-MXFP8 backward: any token count (one token included),
+    k up to min(E, 8), 1-40 experts, d and n multiples of 128 up to 640."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        E = int(rng.integers(1, 41))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = 1 if i == 0 else int(rng.integers(2, 1200))
+        d, n = 128 * int(rng.integers(1, 6)), 128 * int(rng.integers(1, 6))
+        out.append(W.small(f"mxb-random{i}", T=T, k=k, E=E, d=d, n=n, seed=300 + i,
+                           routing=("normal", "zipf")[i % 2]))
+    return out
+
+
 MX_DG2 = [(c, "swiglu", False) for c in CASES] + [(CASES[1], "geglu", False)] + [
-    (CASES[0], "swiglu", True), (CASES[2], "swiglu", True), (CASES[3], "geglu", True)]
+    (CASES[0], "swiglu", True), (CASES[2], "swiglu", True), (CASES[3], "geglu", True)] + [
+    (c, "swiglu", True) for c in _random_cases(4, 77)]
 
 
 @pytest.mark.parametrize("wl,act,dgrad2_mx", MX_DG2,
