@@ -91,9 +91,12 @@ def _cpu_baseline(wl, inp, target_s=15.0, act="swiglu"):
                        act=act)
         return time.perf_counter() - t0
 
-    R = 128
-    dt = run(R)
-    R2 = int(min(wl.T, max(R, R * target_s / max(dt, 1e-3))))
+    # the run time is a fixed part (per-expert loops, the fp64 weight-gradient buffers) plus a
+    # part linear in the tokens: two probes fix both, so the sample lands near target_s
+    r1, r2 = 128, min(wl.T, 1024)
+    t1, t2 = run(r1), run(r2)
+    slope = max((t2 - t1) / max(r2 - r1, 1), 1e-7)
+    R2 = int(min(wl.T, max(r1, (target_s - max(t1 - slope * r1, 0.0)) / slope)))
     R2 = max(128, R2 // 128 * 128)
     dt2 = run(R2)
     flops = (12.0 if act == "srelu" else 18.0) * R2 * wl.k * wl.d * wl.n
