@@ -17,12 +17,12 @@
 //
 // Workgroup tile 256 x 256 x 64, 8 wavefronts (two per SIMD) in a 2 x 4 grid,
 // each owning a 128 x 64 sub-tile as 4 x 2 MFMA 32x32 tiles (fp32
-// accumulators); a wavefront raises its issue priority while it runs MFMAs so
-// its sibling's memory instructions fill the gaps. Operands move global -> LDS
-// with direct buffer loads (two LDS buffers: the next K slab streams in while
-// the current one is multiplied); reads past an expert's rows or past N come
-// back as zeros from the buffer bounds. An operand whose K index is
-// contiguous in memory is kept K-major in LDS and read with ds_read_b128; an
+// accumulators); in the bf16 modes a wavefront raises its issue priority while
+// it runs MFMAs so its sibling's memory instructions fill the gaps. Operands
+// move global -> LDS with direct buffer loads (two LDS buffers: the next K slab
+// streams in while the current one is multiplied); reads past an expert's rows
+// or past N come back as zeros from the buffer bounds. An operand whose K index
+// is contiguous in memory is kept K-major in LDS and read with ds_read_b128; an
 // operand whose M/N index is contiguous is kept MN-major and read with the
 // gfx950 transpose load ds_read_b64_tr_b16, so no operand is transposed in
 // memory. The MFMA is issued with the B fragment as its first operand, which
