@@ -449,9 +449,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             const i32x4_t hi = *(const i32x4_t*)(s + kmaj_byte(r, 4 * ks + 2 + hh));
             return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
-        // the first MFMA row's operands (B, then A row 0) first; each A fragment of
-        // the next K step as soon as its row's MFMAs are issued, the next step's B
-        // fragments after the last row (every accumulator's MFMA order unchanged)
+        // the first MFMA's operands (B, then A row 0) first; the MFMAs go column by
+        // column (all A rows with B fragment 0, then with B fragment 1), so each
+        // fragment of the next K step is requested right after its last MFMA of this
+        // step: at least three MFMAs before its first use (every accumulator's MFMA
+        // order unchanged)
         i32x8_t xa[4], xb[TNW];
 #pragma unroll
         for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 0);
@@ -461,17 +463,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         // bf16 modes, where it gains 2.3%)
         static_for<2>([&](auto KS) {
             constexpr int ks = KS;
-            static_for<4>([&](auto I) {
-                static_for<TNW>([&](auto J) {
+            static_for<TNW>([&](auto J) {
+                static_for<4>([&](auto I) {
                     acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         xb[J], xa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0, (int)(sa[I] >> (16 * ks)));
+                    if constexpr (ks == 0 && J + 1 == TNW) xa[I] = xfrag(sA, wm * 128 + 32 * I, 1);
                 });
-                if constexpr (ks == 0) xa[I] = xfrag(sA, wm * 128 + 32 * I, 1);
+                if constexpr (ks == 0) xb[J] = xfrag(sB, wn * WN + 32 * J, 1);
             });
-            if constexpr (ks == 0) {
-#pragma unroll
-                for (int j = 0; j < TNW; ++j) xb[j] = xfrag(sB, wn * WN + 32 * j, 1);
-            }
         });
         // keep the MFMAs above the slab barrier (left alone, the compiler sinks
         // them below it and serialises the copy wait with the multiply)

@@ -462,13 +462,13 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                 if (kt + 1 < nk) read_scales((sg0 + (kt + 1) / 4) & 1, (kt + 1) & 3, na, nb_);
                 const uint8_t* sA = s_ab[cur];
                 const uint8_t* sB = s_ab[cur] + BM * MBK;
-                // Fragments: the first MFMA row's operands (B, then A row 0) are
-                // requested first, so that row starts while the other A rows still
-                // load; each A fragment of the next K step is requested as soon as
-                // the last MFMA reading this step's is issued, and the next step's B
-                // fragments after the step's last row, so the loads of step 1 run
-                // under the MFMAs of step 0. The MFMA sequence of every accumulator
-                // is unchanged.
+                // Fragments: the first MFMA's operands (B, then A row 0) are requested
+                // first, so it starts while the other A rows still load. The MFMAs go
+                // column by column (all A rows with B fragment 0, then with B fragment
+                // 1), and each fragment of the next K step is requested as soon as
+                // the last MFMA reading this step's is issued, so the loads of step 1
+                // run under the MFMAs of step 0, at least three MFMAs ahead of their
+                // use. The MFMA sequence of every accumulator is unchanged.
                 i32x8_t fa[4], fb[TNW];
 #pragma unroll
                 for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, 0);
@@ -478,20 +478,17 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                     constexpr int ks = KS;
                     constexpr bool more = ks + 1 < MBK / 64;
                     __builtin_amdgcn_s_setprio(1);
-                    static_for<4>([&](auto I) {
-                        static_for<TNW>([&](auto J) {
+                    static_for<TNW>([&](auto J) {
+                        static_for<4>([&](auto I) {
                             // the instruction reads byte 0 of each scale register, so the
                             // block of this K step is shifted there (OPSEL stays 0)
                             acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                                 fb[J], fa[I], acc[I][J], 0, 0, 0, (int)(sb[J] >> (16 * ks)), 0,
                                 (int)(sa[I] >> (16 * ks)));
+                            if constexpr (more && J + 1 == TNW) fa[I] = frag(sA, wm * 128 + 32 * I, ks + 1);
                         });
-                        if constexpr (more) fa[I] = frag(sA, wm * 128 + 32 * I, ks + 1);
+                        if constexpr (more) fb[J] = frag(sB, wn * WN + 32 * J, ks + 1);
                     });
-                    if constexpr (more) {
-#pragma unroll
-                        for (int j = 0; j < TNW; ++j) fb[j] = frag(sB, wn * WN + 32 * j, ks + 1);
-                    }
                     __builtin_amdgcn_s_setprio(0);
                 });
                 // Pin the MFMAs here: left alone, the compiler sinks them below the
