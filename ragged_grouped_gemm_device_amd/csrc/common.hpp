@@ -93,6 +93,16 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Streaming (non-temporal) stores for outputs no kernel of the same step reads
+// soon (weight gradients, the H saved for the backward pass): they do not
+// take last-level cache lines from the operands the next kernels read.
+typedef uint32_t u32x4_nt_t __attribute__((ext_vector_type(4)));
+template <class T>
+__device__ __forceinline__ void st_nt16(void* p, T v) {
+    static_assert(sizeof(T) == 16, "16-byte store");
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt_t, v), (u32x4_nt_t*)p);
+}
+
 // Butterfly sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

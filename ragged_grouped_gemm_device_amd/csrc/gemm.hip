@@ -680,7 +680,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     const int R = 4 * It + (lane >> 4), c = lane & 15;
                     const float4 v = *(const float4*)(stg + R * 256 + ((c ^ (R & 15)) << 4));
                     const int m = rband + 32 * I + R, col = col0 + 4 * c;
-                    if (m < p.M && col < p.N) *(float4*)(out + (int64_t)m * p.ldf + col) = v;
+                    if (m < p.M && col < p.N) st_nt16(out + (int64_t)m * p.ldf + col, v);
                 });
             } else {
                 // row r: 64 bf16 = 8 chunks, half h of chunk 4J + Q from this lane
@@ -905,7 +905,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     const int R = 8 * It + (lane >> 3), c = lane & 7;
                     const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
                     const int m = rband + 32 * I + R;
-                    if (m < row_end && pair_ok) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + hc + 8 * c) = v;
+                    if (m < row_end && pair_ok) st_nt16(p.out0 + (int64_t)m * p.ld0 + hc + 8 * c, v);
                 });
             }
             wave_lds_sync();  // read out before the next 32 rows overwrite it

@@ -583,7 +583,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                     const int R = 4 * It + (lane >> 4), c = lane & 15;
                     const float4 v = *(const float4*)(stg + R * 256 + ((c ^ (R & 15)) << 4));
                     const int m = tl.m0 + wm * 128 + 32 * I + R, col = col0 + 4 * c;
-                    if (m < p.M && col < p.N) *(float4*)(o + (int64_t)m * p.N + col) = v;
+                    if (m < p.M && col < p.N) st_nt16(o + (int64_t)m * p.N + col, v);
                 });
             }
             wave_lds_sync();  // read out before the next 32 rows overwrite it
