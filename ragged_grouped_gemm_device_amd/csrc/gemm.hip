@@ -727,7 +727,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         const int R = 8 * It + (lane >> 3), c = lane & 7;
                         const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
                         const int m = rband + 32 * I + R, col = col0 + 8 * c;
-                        if (m < row_end && col < p.N) *(uint4*)(p.out0 + (int64_t)m * p.ld0 + col) = v;
+                        if (m < row_end && col < p.N) st_nt16(p.out0 + (int64_t)m * p.ld0 + col, v);
                     });
                 }
             }
@@ -1114,14 +1114,14 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                     const int R = 8 * it + (lane >> 3), c = lane & 7;
                     const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
                     const int mr = rband + 32 * I + R;
-                    if (mr < row_end && blk_ok) *(uint4*)(p.out0 + (int64_t)mr * p.ld0 + 2 * ct + 8 * c) = v;
+                    if (mr < row_end && blk_ok) st_nt16(p.out0 + (int64_t)mr * p.ld0 + 2 * ct + 8 * c, v);
                 }
 #pragma unroll
                 for (int it = 0; it < 2; ++it) {  // A': 4 lanes x 16 B a row
                     const int R = 16 * it + (lane >> 2), c = lane & 3;
                     const uint4 v = *(const uint4*)(stg + 4096 + R * 64 + ((c ^ ((R >> 1) & 3)) << 4));
                     const int mr = rband + 32 * I + R;
-                    if (mr < row_end && blk_ok) *(uint4*)(p.out1 + (int64_t)mr * p.ld1 + ct + 8 * c) = v;
+                    if (mr < row_end && blk_ok) st_nt16(p.out1 + (int64_t)mr * p.ld1 + ct + 8 * c, v);
                 }
                 wave_lds_sync();  // read out before the next block overwrites it
             });
