@@ -565,7 +565,7 @@ __global__ void __launch_bounds__(kThreads, 1) mx_gemm_kernel(MxArgs p) {
                         const int R = 8 * It + (lane >> 3), c = lane & 7;
                         const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
                         const int m = tl.row0 + wm * 128 + 32 * I + R, col = col0 + 8 * c;
-                        if (m < tl.row_end && col < p.N) *(uint4*)(p.out + (int64_t)m * p.N + col) = v;
+                        if (m < tl.row_end && col < p.N) st_nt16(p.out + (int64_t)m * p.N + col, v);
                     });
                 }
             } else {
