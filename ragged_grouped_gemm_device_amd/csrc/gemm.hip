@@ -738,7 +738,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         // blocks (32 columns of a row: 16 in this lane, 16 in lane l ^ 32) and
         // column-wise blocks (32 rows of a column: one per lane of a half-wave).
         // 32-row blocks never straddle experts (regions are 128-row aligned).
+        // H leaves through this wavefront's 8 KiB of the free LDS stage, as in
+        // the bf16 GLU epilogue: whole 128-byte rows instead of 8-byte pieces.
         const int n = p.N / 2;
+        __syncthreads();  // the last slab is read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
         static_for<4>([&](auto I) {
             const int m = rbase + 32 * I;
             const int mb = row0 + wm * 128 + 32 * I;  // first row of this 32-row block
@@ -762,16 +766,25 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                                 *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ac + 4 * h + 8 * Q) =
                                     make_uint2(abp[2 * Q], abp[2 * Q + 1]);
                             if (p.out0) {
+                                const int r = lane & 31;
                                 uint2 g2, u2;
                                 g2.x = pack_bf16x2(G[4 * Q], G[4 * Q + 1]);
                                 g2.y = pack_bf16x2(G[4 * Q + 2], G[4 * Q + 3]);
                                 u2.x = pack_bf16x2(Up[4 * Q], Up[4 * Q + 1]);
                                 u2.y = pack_bf16x2(Up[4 * Q + 2], Up[4 * Q + 3]);
-                                const int64_t rowp = (int64_t)m * p.ld0;
-                                *(uint2*)(p.out0 + rowp + hc + 4 * h + 8 * Q) = g2;
-                                *(uint2*)(p.out0 + rowp + hc + 32 + 4 * h + 8 * Q) = u2;
+                                *(uint2*)(stg + r * 128 + ((Q ^ ((r >> 1) & 7)) << 4) + 8 * h) = g2;
+                                *(uint2*)(stg + r * 128 + (((4 + Q) ^ ((r >> 1) & 7)) << 4) + 8 * h) = u2;
                             }
                         });
+                        if (p.out0) {
+                            wave_lds_sync();
+                            static_for<4>([&](auto It) {  // H: 8 lanes x 16 B a row
+                                const int R = 8 * It + (lane >> 3), c = lane & 7;
+                                const uint4 v = *(const uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4));
+                                st_nt16(p.out0 + (int64_t)(mb + R) * p.ld0 + hc + 8 * c, v);
+                            });
+                            wave_lds_sync();  // read out before the next 32 rows overwrite it
+                        }
                         // row-wise block (16 values here, 16 in lane l ^ 32)
                         uint32_t amax = max(am & 0xffffu, am >> 16);
                         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
