@@ -214,7 +214,7 @@ def main():
                 buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a, buf.y,
                 M.MOE_STAGE_FC1, mx=mx, act=act))
         M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, buf.h, None if mx_mode else buf.a, buf.y,
-                              M.MOE_STAGE_FC2, mx=mx)
+                              M.MOE_STAGE_FC2, mx=mx, act=act)
         timed(record, "combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out))
         # backward: the same calls as moe.backward, written out so that the memory-bound
         # launches can be timed one by one
@@ -419,7 +419,7 @@ def _detail(M, torch, wl, buf, x, w1, w2, dout, stream, mx=None, reps=10, act=0,
                                                      buf.y, M.MOE_STAGE_FC1, act=act),
          g1 * Mr * d * n, None),
         ("FC2", lambda: M.moe_grouped_mlp_fwd(buf.x_perm, w1, w2, buf.offsets, None, buf.a, buf.y,
-                                              M.MOE_STAGE_FC2), 2.0 * Mr * d * n, None),
+                                              M.MOE_STAGE_FC2, act=act), 2.0 * Mr * d * n, None),
         ("combine", lambda: M.moe_combine(buf.y, buf.row_of, buf.topk_w, wl.k, buf.out), None,
          2.0 * Mr * d + 2.0 * wl.T * d + 8.0 * Mr),
     ]

@@ -807,32 +807,45 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             }
         });
     } else if constexpr (EPI == EPI_ACT) {
-        // non-gated: A[m, c] = f(H[m, c]) from the fp32 accumulator, H stored when asked
+        // non-gated: A[m, c] = f(H[m, c]) from the fp32 accumulator, H stored when
+        // asked. Staged through LDS like the GLU epilogue, 32 rows at a time: the
+        // wavefront's 64 columns of A (128 B a row) at 0, of H at 4096, leaving
+        // as whole rows.
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
+        const int r = lane & 31;
+        const int rband = row0 + wm * 128;
+        const int cw0 = n0 + wn * WN;  // first column of the wavefront
         static_for<4>([&](auto I) {
-            const int m = rbase + 32 * I;
-            if (m < row_end) {
-                static_for<TNW>([&](auto J) {
-                    const int c0 = n0 + wn * WN + 32 * J;
-                    if (c0 < p.N) {
-                        static_for<4>([&](auto Q) {
-                            const int c = c0 + 8 * Q + 4 * h;
-                            float av[4];
+            static_for<TNW>([&](auto J) {
+                static_for<4>([&](auto Q) {
+                    float av[4];
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) {
-                                float f, df;
-                                plain_act_grad<ACT>(acc[I][J][4 * Q + s], f, df);
-                                av[s] = f;
-                            }
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + c) =
-                                make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
-                            if (p.out0)
-                                *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) =
-                                    make_uint2(pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]),
-                                               pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]));
-                        });
+                    for (int s = 0; s < 4; ++s) {
+                        float f, df;
+                        plain_act_grad<ACT>(acc[I][J][4 * Q + s], f, df);
+                        av[s] = f;
                     }
+                    const int ch = 4 * J + Q;
+                    *(uint2*)(stg + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h) =
+                        make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
+                    if (p.out0)
+                        *(uint2*)(stg + 4096 + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h) =
+                            make_uint2(pack_bf16x2(acc[I][J][4 * Q], acc[I][J][4 * Q + 1]),
+                                       pack_bf16x2(acc[I][J][4 * Q + 2], acc[I][J][4 * Q + 3]));
                 });
-            }
+            });
+            wave_lds_sync();
+            static_for<4>([&](auto It) {  // 8 lanes x 16 B a row
+                const int R = 8 * It + (lane >> 3), c = lane & 7;
+                const int m = rband + 32 * I + R, col = cw0 + 8 * c;
+                const int sw = (c ^ ((R >> 1) & 7)) << 4;
+                if (m < row_end && col < p.N) {
+                    *(uint4*)(p.out1 + (int64_t)m * p.ld1 + col) = *(const uint4*)(stg + R * 128 + sw);
+                    if (p.out0) st_nt16(p.out0 + (int64_t)m * p.ld0 + col, *(const uint4*)(stg + 4096 + R * 128 + sw));
+                }
+            });
+            wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
     } else if constexpr (EPI == EPI_DACT) {
         // acc = dA' (unweighted) over columns c; H [M, n] holds the pre-activation
