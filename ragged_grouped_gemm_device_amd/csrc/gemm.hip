@@ -848,7 +848,27 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             wave_lds_sync();  // read out before the next 32 rows overwrite it
         });
     } else if constexpr (EPI == EPI_DACT) {
-        // acc = dA' (unweighted) over columns c; H [M, n] holds the pre-activation
+        // acc = dA' (unweighted) over columns c; H [M, n] holds the pre-activation.
+        // Staged through LDS like the dGLU epilogue, 32 rows at a time: the
+        // wavefront's 64 columns of H come in as whole rows (the next block's
+        // loaded while this one is worked on), dH is written back in place and A'
+        // at 4096, and both leave as whole rows.
+        __syncthreads();  // the last slab and the previous tile's staging are read out
+        uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;
+        const int r = lane & 31;
+        const int rband = row0 + wm * 128;
+        const int cw0 = n0 + wn * WN;  // first column of the wavefront
+        uint4 hv[4];
+        auto load_h = [&](int I) {  // 8 lanes x 16 B a row, 8 rows per load
+            const int col = cw0 + 8 * (lane & 7);
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int m = rband + 32 * I + 8 * it + (lane >> 3);
+                hv[it] = make_uint4(0, 0, 0, 0);
+                if (m < row_end && col < p.N) hv[it] = *(const uint4*)(p.aux + (int64_t)m * p.ld_aux + col);
+            }
+        };
+        load_h(0);
         static_for<4>([&](auto I) {
             const int m = rbase + 32 * I;
             const bool row_ok = m < row_end;
@@ -857,32 +877,48 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                 const int src = p.src_of[m];
                 w = src >= 0 ? p.topk_w[src] : 0.f;
             }
-            float dsum = 0.f;
-            if (row_ok) {
-                static_for<TNW>([&](auto J) {
-                    const int c0 = n0 + wn * WN + 32 * J;
-                    if (c0 < p.N) {
-                        static_for<4>([&](auto Q) {
-                            const int c = c0 + 8 * Q + 4 * h;
-                            float hv[4], dh[4], aw[4];
-                            unpack_bf16x4(*(const uint2*)(p.aux + (int64_t)m * p.ld_aux + c), hv);
 #pragma unroll
-                            for (int s = 0; s < 4; ++s) {
-                                float f, df;
-                                plain_act_grad<ACT>(hv[s], f, df);
-                                const float dap = acc[I][J][4 * Q + s];
-                                dsum = fmaf(dap, f, dsum);
-                                dh[s] = w * dap * df;
-                                aw[s] = w * f;
-                            }
-                            *(uint2*)(p.out0 + (int64_t)m * p.ld0 + c) =
-                                make_uint2(pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3]));
-                            *(uint2*)(p.out1 + (int64_t)m * p.ld1 + c) =
-                                make_uint2(pack_bf16x2(aw[0], aw[1]), pack_bf16x2(aw[2], aw[3]));
-                        });
-                    }
-                });
+            for (int it = 0; it < 4; ++it) {
+                const int R = 8 * it + (lane >> 3), c = lane & 7;
+                *(uint4*)(stg + R * 128 + ((c ^ ((R >> 1) & 7)) << 4)) = hv[it];
             }
+            if constexpr (I + 1 < 4) load_h(I + 1);
+            wave_lds_sync();
+            // rows past the region or columns past N hold zeros here and in acc:
+            // they add nothing to dsum and are not stored
+            float dsum = 0.f;
+            static_for<TNW>([&](auto J) {
+                static_for<4>([&](auto Q) {
+                    const int ch = 4 * J + Q;
+                    uint2* ph = (uint2*)(stg + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h);
+                    float hf[4], dh[4], aw[4];
+                    unpack_bf16x4(*ph, hf);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        float f, df;
+                        plain_act_grad<ACT>(hf[s], f, df);
+                        const float dap = acc[I][J][4 * Q + s];
+                        dsum = fmaf(dap, f, dsum);
+                        dh[s] = w * dap * df;
+                        aw[s] = w * f;
+                    }
+                    *ph = make_uint2(pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3]));
+                    *(uint2*)(stg + 4096 + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4) + 8 * h) =
+                        make_uint2(pack_bf16x2(aw[0], aw[1]), pack_bf16x2(aw[2], aw[3]));
+                });
+            });
+            wave_lds_sync();
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {  // dH and A': 8 lanes x 16 B a row
+                const int R = 8 * it + (lane >> 3), c = lane & 7;
+                const int mr = rband + 32 * I + R, col = cw0 + 8 * c;
+                const int sw = (c ^ ((R >> 1) & 7)) << 4;
+                if (mr < row_end && col < p.N) {
+                    st_nt16(p.out0 + (int64_t)mr * p.ld0 + col, *(const uint4*)(stg + R * 128 + sw));
+                    st_nt16(p.out1 + (int64_t)mr * p.ld1 + col, *(const uint4*)(stg + 4096 + R * 128 + sw));
+                }
+            }
+            wave_lds_sync();  // read out before the next block overwrites it
             dsum += __shfl_xor(dsum, 32, 64);  // the partner lane holds the other half
             if (row_ok && h == 0) p.outf[(int64_t)m * p.n_part + (n0 / BN) * (BN / WN) + wn] = dsum;
         });
