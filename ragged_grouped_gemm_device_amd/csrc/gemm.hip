@@ -1030,12 +1030,29 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         const int64_t hrow = (int64_t)m * p.ld_aux;
                         const int64_t drow = (int64_t)m * p.ld0;
                         // the block's H (this lane's 16 gate and 16 up values) requested
-                        // at once: loading inside the loop below waited on each pair
+                        // at once: loading inside the loop below waited on each pair.
+                        // Lane half h loads whole 16-byte chunks h and 2 + h of the gate
+                        // and up columns (32 contiguous bytes a row per load, half the
+                        // loads of 8-byte pieces) and trades the half it does not use
+                        // with lane l ^ 32, which loaded the chunks next to them.
                         uint2 hg[4], hu[4];
+                        {
+                            uint4 ld[4];
 #pragma unroll
-                        for (int Q = 0; Q < 4; ++Q) {
-                            hg[Q] = *(const uint2*)(p.aux + hrow + gcol + 8 * Q + 4 * h);
-                            hu[Q] = *(const uint2*)(p.aux + hrow + gcol + 32 + 8 * Q + 4 * h);
+                            for (int c = 0; c < 4; ++c)  // gate 8h, gate 16 + 8h, up 8h, up 16 + 8h
+                                ld[c] = *(const uint4*)(p.aux + hrow + gcol + 32 * (c >> 1) + 16 * (c & 1) + 8 * h);
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const uint2 lo = make_uint2(ld[c].x, ld[c].y), hi = make_uint2(ld[c].z, ld[c].w);
+                                const uint2 keep = h ? hi : lo, give = h ? lo : hi;
+                                const auto s0 = __builtin_amdgcn_permlane32_swap(give.x, give.x, false, false);
+                                const auto s1 = __builtin_amdgcn_permlane32_swap(give.y, give.y, false, false);
+                                const uint2 got = h ? make_uint2(s0[0], s1[0]) : make_uint2(s0[1], s1[1]);
+                                uint2* dst = (c >> 1) ? hu : hg;
+                                const int q0 = 2 * (c & 1);  // chunks q0 (half 0) and q0 + 1 (half 1)
+                                dst[q0] = h ? got : keep;
+                                dst[q0 + 1] = h ? keep : got;
+                            }
                         }
                         uint32_t dgp[8], dup[8];  // bf16 pairs, slots 2p, 2p + 1
                         static_for<4>([&](auto Q) {
