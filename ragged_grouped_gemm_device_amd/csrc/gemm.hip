@@ -790,11 +790,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                         amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
                         const int er = mx_block_exp(amax);
                         const float invr = mx_inv_scale(er);
+                        uint32_t cw[4];
                         static_for<4>([&](auto Q) {
-                            *(uint32_t*)(p.q_row + (int64_t)m * n + ac + 4 * h + 8 * Q) =
-                                e4m3x4(bf16_lo(abp[2 * Q]) * invr, bf16_hi(abp[2 * Q]) * invr,
-                                       bf16_lo(abp[2 * Q + 1]) * invr, bf16_hi(abp[2 * Q + 1]) * invr);
+                            cw[Q] = e4m3x4(bf16_lo(abp[2 * Q]) * invr, bf16_hi(abp[2 * Q]) * invr,
+                                           bf16_lo(abp[2 * Q + 1]) * invr, bf16_hi(abp[2 * Q + 1]) * invr);
                         });
+                        mx_store_row32(cw, lane, p.q_row + (int64_t)m * n + ac);
                         p.s_row[(int64_t)m * (n / 32) + ac / 32] = (uint8_t)(er + 127);  // same byte from both halves
                         // column-wise blocks, stored transposed
                         if (p.q_col) {

@@ -210,6 +210,20 @@ __device__ __forceinline__ void mx_stage_flush(const uint8_t* stage, int lane, u
     }
 }
 
+// The 32 codes of a row-wise block, held as four words per lane (word Q: codes
+// 8 Q + 4 h .. 8 Q + 4 h + 3 of the row, h the lane half), leave as one 16-byte
+// store per lane: half 0 writes codes 0-15 and half 1 codes 16-31, after each
+// trades two words with lane l ^ 32 (v_permlane32_swap, which needs every lane
+// of the wavefront active). q: the row's first code of the block.
+__device__ __forceinline__ void mx_store_row32(const uint32_t w[4], int lane, uint8_t* q) {
+    const int h = (lane >> 5) & 1;
+    const uint32_t g0 = h ? w[0] : w[2], g1 = h ? w[1] : w[3];
+    const auto s0 = __builtin_amdgcn_permlane32_swap(g0, g0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(g1, g1, false, false);
+    const uint32_t r0 = h ? s0[0] : s0[1], r1 = h ? s1[0] : s1[1];
+    *(uint4*)(q + 16 * h) = h ? make_uint4(r0, w[2], r1, w[3]) : make_uint4(w[0], r0, w[1], r1);
+}
+
 // Row-wise MXFP8 block of one row of a 32 x 32 block held the MFMA way: this
 // lane has 16 of the row's 32 bf16 values (pk[j / 2], 16-bit slot j: column
 // 8 (j / 4) + 4 h + j % 4, h = lane / 32), the lane l ^ 32 the other 16. The
@@ -224,11 +238,12 @@ __device__ __forceinline__ void mx_rowq32(const uint32_t pk[8], int lane, uint8_
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
     const int e = mx_block_exp(amax);
     const float inv = mx_inv_scale(e);
-    const int h = (lane >> 5) & 1;
+    uint32_t w[4];
 #pragma unroll
     for (int Q = 0; Q < 4; ++Q)
-        *(uint32_t*)(q + 8 * Q + 4 * h) = e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv,
-                                                 bf16_lo(pk[2 * Q + 1]) * inv, bf16_hi(pk[2 * Q + 1]) * inv);
+        w[Q] = e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv, bf16_lo(pk[2 * Q + 1]) * inv,
+                      bf16_hi(pk[2 * Q + 1]) * inv);
+    mx_store_row32(w, lane, q);
     *sc = (uint8_t)(e + 127);
 }
 
