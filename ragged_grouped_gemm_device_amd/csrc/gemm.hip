@@ -989,7 +989,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
         uint8_t* stg = (uint8_t*)(&s_ab[next_buf0 ^ 1][0]) + wave * 8192;  // gate: 0, up: 4096
         const int band = row0 + wm * 128;                                  // first row of the band
         const int band_rows = min(max(row_end - band, 0), 128);
-        auto rowq = [&](const uint32_t* pk, int m, int col0) {  // 16 bf16 here, 16 in lane l ^ 32
+        // the row-wise codes of one 32-column block (16 bf16 here, 16 in lane l ^ 32)
+        // as four words, word Q holding columns 8 Q + 4 h .. + 3; the scale is stored
+        auto rowq = [&](const uint32_t* pk, int m, int col0, uint32_t* cw) {
             uint32_t am = 0;
 #pragma unroll
             for (int r = 0; r < 8; ++r) am = max_u16x2(am, pk[r] & 0x7fff7fffu);
@@ -998,11 +1000,32 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
             const int er = mx_block_exp(amax);
             const float inv = mx_inv_scale(er);
             static_for<4>([&](auto Q) {
-                *(uint32_t*)(p.q_row + (int64_t)m * n2 + col0 + 8 * Q + 4 * h) =
-                    e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv, bf16_lo(pk[2 * Q + 1]) * inv,
-                           bf16_hi(pk[2 * Q + 1]) * inv);
+                cw[Q] = e4m3x4(bf16_lo(pk[2 * Q]) * inv, bf16_hi(pk[2 * Q]) * inv, bf16_lo(pk[2 * Q + 1]) * inv,
+                               bf16_hi(pk[2 * Q + 1]) * inv);
             });
             p.s_row[(int64_t)m * (n2 / 32) + col0 / 32] = (uint8_t)(er + 127);  // same byte from both halves
+        };
+        // the gate and up blocks of a row: lane half 0 writes the gate block's 32
+        // codes, half 1 the up block's, each after trading the other block's four
+        // words with lane l ^ 32 (every lane active here)
+        auto rowq2 = [&](const uint32_t* pg, const uint32_t* pu, int m, int col0) {
+            uint32_t cg[4], cu[4], got[4];
+            rowq(pg, m, col0, cg);
+            rowq(pu, m, col0 + 32, cu);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t give = h ? cg[q] : cu[q];
+                const auto sw = __builtin_amdgcn_permlane32_swap(give, give, false, false);
+                got[q] = h ? sw[0] : sw[1];
+            }
+            uint8_t* dst = p.q_row + (int64_t)m * n2 + col0 + 32 * h;
+            if (h) {
+                *(uint4*)dst = make_uint4(got[0], cu[0], got[1], cu[1]);
+                *(uint4*)(dst + 16) = make_uint4(got[2], cu[2], got[3], cu[3]);
+            } else {
+                *(uint4*)dst = make_uint4(cg[0], got[0], cg[1], got[1]);
+                *(uint4*)(dst + 16) = make_uint4(cg[2], got[2], cg[3], got[3]);
+            }
         };
         float wI[4], dsum[4];
         static_for<4>([&](auto I) {
@@ -1087,8 +1110,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GemmArgs p) {
                                 *(uint2*)(p.out1 + (int64_t)m * p.ld1 + ct + cc) =
                                     make_uint2(awp[I][2 * Q], awp[I][2 * Q + 1]);
                         });
-                        rowq(dgp, m, gcol);
-                        rowq(dup, m, gcol + 32);
+                        rowq2(dgp, dup, m, gcol);
                         mx_colq32_stage(dgp, lane, stg, I, p.s_col + (int64_t)gcol * ls + mb / 32, ls);
                         mx_colq32_stage(dup, lane, stg + 4096, I, p.s_col + (int64_t)(gcol + 32) * ls + mb / 32, ls);
                     }
