@@ -228,8 +228,8 @@ __device__ __forceinline__ void mx_store_row32(const uint32_t w[4], int lane, ui
 // lane has 16 of the row's 32 bf16 values (pk[j / 2], 16-bit slot j: column
 // 8 (j / 4) + 4 h + j % 4, h = lane / 32), the lane l ^ 32 the other 16. The
 // block maximum is one lane exchange away; the codes go to q (the row's first
-// column of the block) as four 4-byte words per lane, the E8M0 scale to *sc
-// (the same byte from both lanes).
+// column of the block) as one 16-byte piece per lane (mx_store_row32), the
+// E8M0 scale to *sc (the same byte from both lanes).
 __device__ __forceinline__ void mx_rowq32(const uint32_t pk[8], int lane, uint8_t* q, uint8_t* sc) {
     uint32_t am = 0;
 #pragma unroll
